@@ -1,0 +1,412 @@
+// QJL decode attention for gfx950: one kernel per decode step.
+//
+// Method: "QJL: 1-Bit Quantized JL Transform for KV Cache Quantization with
+// Zero Overhead", Abstract (asymmetric estimator: the query takes the plain
+// JL transform, the key its sign bits; unbiased) and "The Geometry of
+// Forgetting: How Three Papers Cracked KV Cache Quantization", section "QJL:
+// one bit, zero parameters, unbiased inner products" (the sqrt(pi/2) constant
+// over the sketch size; attention scores are inner products).  For query head
+// h and cached token t:
+//   est_t = sqrt(pi/2)/m * ||k_t|| * sum_i (S^T q)_i (2 b_ti - 1),
+//   out   = sum_t softmax_t(scale * est) v_t.
+//
+// Kernel design.  The step is bound by HBM: per (token, kv head) it reads m/8
+// bytes of sign words, 4 bytes of norm and 2d bytes of bf16 values.
+// * Grid = (context split, kv head, batch).  A workgroup (4 waves) serves the
+//   G query heads of one kv head over one token range.
+// * Prologue: S^T q for the G heads (fp32) and, from it, a table in LDS of the
+//   16 possible signed sums of every group of 4 consecutive sketch
+//   coordinates (per head).  The bit dot product of a token then costs m/4
+//   table reads and adds per head instead of m masked adds.
+// * Main loop: a wave takes 64 tokens at a time.  Lane t of the wave scores
+//   token t (its m/32 sign words and norm arrive with 16-byte loads); the
+//   wave does the online-softmax update; then lanes regroup to 16 per token
+//   row and accumulate p * v over 16-byte value chunks.  The next tile's loads
+//   are issued before the current tile is used.
+// * Epilogue: waves merge in LDS; the workgroup writes its partial
+//   (max, sum, acc) per head; the last workgroup of a (batch, kv head) to
+//   arrive (atomic counter) merges all splits by log-sum-exp and writes out,
+//   then returns the counter to zero.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace qjl {
+namespace {
+
+constexpr int D = kHeadDim;
+constexpr int NW = 4;            // waves per workgroup
+constexpr int NT = 64 * NW;
+constexpr int TILE = 64;         // tokens per wave per step
+constexpr int VCH = TILE * D * 2 / 16 / 64;  // 16-byte value chunks per lane per tile (16)
+constexpr int MAX_SPLITS = 1024;
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// G floats read or written as one LDS access (b32 / b64 / b128; two b128 for G = 8).
+template <int G>
+struct alignas(G >= 4 ? 16 : 4 * G) VecG {
+  float v[G];
+};
+
+template <int M, int G>
+__global__ __launch_bounds__(NT) void decode_kernel(
+    const float* __restrict__ q, const uint32_t* __restrict__ signs,
+    const float* __restrict__ norms, const uint16_t* __restrict__ values,
+    const uint16_t* __restrict__ s_dm, int H_kv, int N, int cap, int n_split, int tps,
+    float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
+    float* __restrict__ part_acc, float* __restrict__ part_ml) {
+  constexpr int WPR = M / 32;        // sign words per token
+  constexpr int SV = WPR / 4;        // 16-byte sign loads per token
+  constexpr int NPOS = M / 4;        // nibble positions
+  constexpr int LUT_FLOATS = NPOS * 16 * G;
+
+  __shared__ __attribute__((aligned(16))) float lut[LUT_FLOATS];
+  __shared__ __attribute__((aligned(16))) float qs[G][D];
+  __shared__ __attribute__((aligned(16))) float sq[G][M];
+  __shared__ __attribute__((aligned(16))) float pbuf[NW][TILE][G];
+  __shared__ float red_acc[NW][G][D];
+  __shared__ float red_ml[NW][G][2];
+  __shared__ int is_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t bh = static_cast<int64_t>(b) * H_kv + kvh;
+  const int t_begin = split * tps;
+  const int t_end = min(N, t_begin + tps);
+
+  const uint32_t* sg_base = signs + bh * cap * WPR;
+  const float* nm_base = norms + bh * cap;
+  const uint16_t* v_base = values + bh * cap * D;
+
+  // ---- first tile's loads go out before the prologue ----
+  uint4 vc[VCH];
+  uint4 sc[SV];
+  float nc;
+  auto load_tile = [&](int t0, uint4* vv, uint4* ss, float& nn) {
+    const int ts = t0 + lane;
+    if (ts < t_end) {
+      const uint4* p = reinterpret_cast<const uint4*>(sg_base + static_cast<int64_t>(ts) * WPR);
+#pragma unroll
+      for (int k = 0; k < SV; ++k) ss[k] = p[k];
+      nn = nm_base[ts];
+    } else {
+#pragma unroll
+      for (int k = 0; k < SV; ++k) ss[k] = make_uint4(0, 0, 0, 0);
+      nn = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int tv = t0 + 4 * c + (lane >> 4);
+      vv[c] = tv < t_end
+                  ? reinterpret_cast<const uint4*>(v_base + static_cast<int64_t>(tv) * D)[lane & 15]
+                  : make_uint4(0, 0, 0, 0);
+    }
+  };
+  int t0 = t_begin + wave * TILE;
+  if (t0 < t_end) load_tile(t0, vc, sc, nc);
+
+  // ---- prologue: q -> LDS, S^T q, nibble table ----
+  const float* qb = q + (static_cast<int64_t>(b) * H_kv + kvh) * G * D;
+  for (int i = tid; i < G * D; i += NT) qs[i / D][i % D] = qb[i];
+  __syncthreads();
+  for (int i = tid; i < M; i += NT) {
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll 8
+    for (int jj = 0; jj < D; ++jj) {
+      const float s = __uint_as_float(static_cast<uint32_t>(s_dm[jj * M + i]) << 16);
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g] = __builtin_fmaf(s, qs[g][jj], acc[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) sq[g][i] = acc[g];
+  }
+  __syncthreads();
+  for (int e = tid; e < NPOS * 16; e += NT) {
+    const int p = e >> 4, v = e & 15;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = sq[g][4 * p + k];
+        s += ((v >> k) & 1) ? x : -x;
+      }
+      lut[e * G + g] = s;
+    }
+  }
+  __syncthreads();
+
+  // ---- main loop ----
+  float m_run[G], l_run[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  }
+
+  while (t0 < t_end) {
+    const int t_next = t0 + NW * TILE;
+    uint4 vn[VCH];
+    uint4 sn[SV];
+    float nn = 0.f;
+    if (t_next < t_end) load_tile(t_next, vn, sn, nn);
+
+    // scores: lane <-> token t0 + lane
+    float sc_g[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sc_g[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < SV; ++k) {
+      const uint32_t wv[4] = {sc[k].x, sc[k].y, sc[k].z, sc[k].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w = wv[u];
+#pragma unroll
+        for (int nib = 0; nib < 8; ++nib) {
+          const int pos = (4 * k + u) * 8 + nib;
+          const uint32_t idx = (w >> (4 * nib)) & 15u;
+          const VecG<G> t = *reinterpret_cast<const VecG<G>*>(&lut[(pos * 16 + idx) * G]);
+#pragma unroll
+          for (int g = 0; g < G; ++g) sc_g[g] += t.v[g];
+        }
+      }
+    }
+    const bool valid = (t0 + lane) < t_end;
+    VecG<G> pw;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float logit = valid ? sc_g[g] * (coef * nc) : -INFINITY;
+      const float tmax = wave_max(logit);
+      const float m_new = fmaxf(m_run[g], tmax);
+      const float alpha = exp2f(m_run[g] - m_new);
+      const float p = valid ? exp2f(logit - m_new) : 0.f;
+      l_run[g] = l_run[g] * alpha + p;
+      m_run[g] = m_new;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
+      pw.v[g] = p;
+    }
+    *reinterpret_cast<VecG<G>*>(&pbuf[wave][lane][0]) = pw;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // p * v: lane <-> (token 4c + lane/16, channels 8*(lane%16) .. +7)
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const VecG<G> pt = *reinterpret_cast<const VecG<G>*>(&pbuf[wave][4 * c + (lane >> 4)][0]);
+      const float v8[8] = {bf16lo(vc[c].x), bf16hi(vc[c].x), bf16lo(vc[c].y), bf16hi(vc[c].y),
+                           bf16lo(vc[c].z), bf16hi(vc[c].z), bf16lo(vc[c].w), bf16hi(vc[c].w)};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = __builtin_fmaf(pt.v[g], v8[e], acc[g][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    t0 = t_next;
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) vc[c] = vn[c];
+#pragma unroll
+    for (int k = 0; k < SV; ++k) sc[k] = sn[k];
+    nc = nn;
+  }
+
+  // ---- merge within the wave, then across waves ----
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l_run[g] = wave_sum(l_run[g]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[g][e];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[g][e] = x;
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_acc[wave][g][8 * lane + e] = acc[g][e];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      red_ml[wave][g][0] = m_run[g];
+      red_ml[wave][g][1] = l_run[g];
+    }
+  }
+  __syncthreads();
+
+  const int64_t slot0 = bh * n_split + split;   // partial index base
+  for (int i = tid; i < G * D; i += NT) {
+    const int g = i / D, dd = i % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_ml[w][g][0]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = red_ml[w][g][0];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - mx);
+      L += red_ml[w][g][1] * f;
+      A += red_acc[w][g][dd] * f;
+    }
+    if (n_split == 1) {
+      out[(bh * G + g) * D + dd] = A / L;
+    } else {
+      part_acc[(slot0 * G + g) * D + dd] = A;
+      if (dd == 0) {
+        part_ml[(slot0 * G + g) * 2 + 0] = mx;
+        part_ml[(slot0 * G + g) * 2 + 1] = L;
+      }
+    }
+  }
+  if (n_split == 1) return;
+
+  // ---- last workgroup of this (batch, kv head) merges the splits ----
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = atomicAdd(&counters[bh], 1u);
+    is_last = (prev == static_cast<uint32_t>(n_split - 1));
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+
+  // weights w_s,g = exp2(m_s - M) / L  (reuse the table memory)
+  float* wts = lut;   // n_split * G floats (n_split <= MAX_SPLITS)
+  __shared__ float gmax[G], gsum[G];
+  for (int g = wave; g < G; g += NW) {
+    float mx = -INFINITY;
+    for (int s = lane; s < n_split; s += 64) mx = fmaxf(mx, part_ml[((bh * n_split + s) * G + g) * 2]);
+    mx = wave_max(mx);
+    float L = 0.f;
+    for (int s = lane; s < n_split; s += 64) {
+      const float* ml = part_ml + ((bh * n_split + s) * G + g) * 2;
+      L += ml[1] * exp2f(ml[0] - mx);
+    }
+    L = wave_sum(L);
+    if (lane == 0) {
+      gmax[g] = mx;
+      gsum[g] = L;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_split * G; i += NT) {
+    const int s = i / G, g = i % G;
+    const float* ml = part_ml + ((bh * n_split + s) * G + g) * 2;
+    wts[i] = exp2f(ml[0] - gmax[g]) / gsum[g];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += NT) {
+    const int g = i / D, dd = i % D;
+    float o = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      o = __builtin_fmaf(wts[s * G + g], part_acc[((bh * n_split + s) * G + g) * D + dd], o);
+    }
+    out[(bh * G + g) * D + dd] = o;
+  }
+  if (tid == 0) counters[bh] = 0u;
+}
+
+template <int M, int G>
+int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float* q,
+                     const uint32_t* signs, const float* norms, const void* values, int B,
+                     int H_kv, int N, int cap, float coef, float* out, void* workspace,
+                     hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+  float* part_acc = reinterpret_cast<float*>(ws + plan.counter_bytes);
+  float* part_ml = part_acc + static_cast<size_t>(B) * H_kv * G * plan.n_split * D;
+  dim3 grid(plan.n_split, H_kv, B);
+  hipLaunchKernelGGL((decode_kernel<M, G>), grid, dim3(NT), 0, stream, q, signs, norms,
+                     static_cast<const uint16_t*>(values), s.s_dm, H_kv, N, cap, plan.n_split,
+                     plan.tokens_per_split, coef, out, counters, part_acc, part_ml);
+  return hipGetLastError();
+}
+
+template <int M>
+int launch_decode_m(int G, const DeviceSketch& s, const DecodePlan& plan, const float* q,
+                    const uint32_t* signs, const float* norms, const void* values, int B,
+                    int H_kv, int N, int cap, float coef, float* out, void* workspace,
+                    hipStream_t st) {
+  switch (G) {
+    case 1: return launch_decode_mg<M, 1>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+    case 2: return launch_decode_mg<M, 2>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+    case 4: return launch_decode_mg<M, 4>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+    case 8: return launch_decode_mg<M, 8>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan* plan) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || N <= 0 || d != D || (m != 256 && m != 512)) return false;
+  if (H_q % H_kv) return false;
+  const int64_t streams = static_cast<int64_t>(B) * H_kv;
+  // Aim for about two workgroups per compute unit (256 CUs) while keeping at
+  // least one full step (4 waves x 64 tokens) per split.
+  constexpr int64_t kTargetWorkgroups = 512;
+  constexpr int kMinTokens = NW * TILE;
+  int64_t want = (kTargetWorkgroups + streams - 1) / streams;
+  const int64_t most = (N + kMinTokens - 1) / kMinTokens;
+  if (want > most) want = most;
+  if (want > MAX_SPLITS) want = MAX_SPLITS;
+  if (want < 1) want = 1;
+  int64_t tps = (N + want - 1) / want;
+  tps = (tps + TILE - 1) / TILE * TILE;
+  const int64_t n_split = (N + tps - 1) / tps;
+  plan->n_split = static_cast<int>(n_split);
+  plan->tokens_per_split = static_cast<int>(tps);
+  plan->counter_bytes = (static_cast<size_t>(streams) * 4 + 255) / 256 * 256;
+  const size_t parts = static_cast<size_t>(B) * H_q * n_split;
+  plan->partial_bytes = parts * (D + 2) * sizeof(float);
+  plan->total_bytes = plan->counter_bytes + plan->partial_bytes;
+  return true;
+}
+
+int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,
+                  const uint32_t* signs, const float* norms, const void* values, int B, int H_q,
+                  int H_kv, int N, int cap, float scale, float* out, void* workspace,
+                  void* stream) {
+  const int G = H_q / H_kv;
+  // logits are kept in base 2: coef = sqrt(pi/2)/m * scale * log2(e)
+  const double c = 1.2533141373155002512 / s.m * static_cast<double>(scale) * 1.4426950408889634074;
+  const float coef = static_cast<float>(c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.m == 256)
+    return launch_decode_m<256>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+  return launch_decode_m<512>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+}
+
+}  // namespace qjl

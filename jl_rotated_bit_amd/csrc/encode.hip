@@ -1,0 +1,333 @@
+// QJL key encode for gfx950: sign bits of S^T k and ||k|| for every key.
+//
+// Method: "QJL: 1-Bit Quantized JL Transform for KV Cache Quantization with
+// Zero Overhead", Abstract (JL transform, then one sign bit per coordinate,
+// no quantization constants) and "The Geometry of Forgetting: How Three
+// Papers Cracked KV Cache Quantization", section "QJL: one bit, zero
+// parameters, unbiased inner products" (Q(x) = sign(Sx)).  The norm is kept
+// because that section's formulas are written for unit vectors, which the
+// random-rotation section reaches by scaling.
+//
+// Kernel design (one launch per call):
+// * The projection P^T = S^T K^T runs on the matrix cores
+//   (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  A workgroup has m/64
+//   waves; wave w owns sketch coordinates [64w, 64w+64) and keeps its slice
+//   of S^T (64 x 128 bf16, 64 VGPRs) resident for the whole kernel.
+// * Keys stream through LDS in tiles of 32 (one MFMA column block), loaded
+//   with coalesced 16-byte reads and double-buffered; the next tile's loads
+//   are in flight while the current tile is multiplied.
+// * The A-operand rows are permuted so that lane (key j, half h) ends up
+//   holding coordinates 64w + 32h + 0..31 of key j in its 32 accumulators:
+//   one word of packed bits per lane, assembled with v_alignbit (one
+//   instruction per bit-lane), no cross-lane traffic.
+// * ||k||^2 comes from the same B fragments (bf16 dot2, fp32 accumulate).
+// * Certification: an accumulator with |acc| <= tau, where tau bounds the
+//   accumulation error of a d-term fp32 dot product of exact bf16 products
+//   (with margin), is re-evaluated exactly: the wave sums the 128 fp64
+//   products (exact) in a tree with a rigorous error bound, and falls back to
+//   an exact integer long accumulator when even that is inconclusive.  The
+//   resulting bit is the sign of the exact real sum, with sign(0) = +1.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace qjl {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int D = kHeadDim;          // 128 key channels
+constexpr int KT = 32;               // keys per tile = MFMA N block
+constexpr int CW = 64;               // sketch coordinates per wave
+constexpr int ROW_B = D * 2;         // 256 bytes per key
+constexpr int LDS_ROW = ROW_B + 16;  // padded LDS row: spreads lanes over banks
+constexpr int TILE_LDS = KT * LDS_ROW;
+constexpr int CHUNKS = KT * ROW_B / 16;  // 16-byte chunks per key tile (512)
+constexpr int ACC_WORDS = 18;        // long accumulator: 576 bits
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
+// Exact bf16 -> fp64 built from the bit fields (no fp32 step, so bf16
+// subnormals are never flushed).
+__device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
+  const uint32_t e = (bits16 >> 7) & 0xFF;
+  const uint32_t f = bits16 & 0x7F;
+  const double v = e ? __longlong_as_double((static_cast<long long>(e + 896) << 52) |
+                                            (static_cast<long long>(f) << 45))
+                     : static_cast<double>(f) * 0x1.0p-133;
+  return (bits16 & 0x8000) ? -v : v;
+}
+
+// Adds v (< 2^48) << (32 * w) into a little-endian multiword integer in LDS.
+__device__ void long_add(uint32_t* acc, int w, uint64_t v) {
+  uint64_t carry = v;
+  for (int i = w; i < ACC_WORDS && carry != 0; ++i) {
+    const uint64_t t = static_cast<uint64_t>(acc[i]) + (carry & 0xFFFFFFFFull);
+    acc[i] = static_cast<uint32_t>(t);
+    carry = (carry >> 32) + (t >> 32);
+  }
+}
+
+// Exact sign of sum_c key[c] * s[c] over the 128 channels, from bf16 bits.
+// Serial (one lane); only reached when a tree sum in fp64 cannot decide.
+// Every bf16 value is sig * 2^(E - 134) with sig < 2^8 and 1 <= E <= 254, so
+// each product is an integer sig_k*sig_s < 2^16 times 2^(Ek + Es - 268):
+// it is added, shifted by Ek + Es - 2 bits, into one of two 576-bit
+// magnitudes (positive / negative terms), which are compared at the end.
+__device__ bool exact_sign_long(const uint16_t* key_lds, const uint16_t* s_row, uint32_t* scratch) {
+  uint32_t* pos = scratch;
+  uint32_t* neg = scratch + ACC_WORDS;
+  for (int i = 0; i < 2 * ACC_WORDS; ++i) scratch[i] = 0;
+  for (int c = 0; c < D; ++c) {
+    const uint32_t uk = key_lds[c];
+    const uint32_t us = s_row[c];
+    uint32_t ek = (uk >> 7) & 0xFF, es = (us >> 7) & 0xFF;
+    const uint32_t sk = ek ? ((uk & 0x7F) | 0x80) : (uk & 0x7F);
+    const uint32_t ss = es ? ((us & 0x7F) | 0x80) : (us & 0x7F);
+    if (sk == 0 || ss == 0) continue;
+    ek = ek ? (ek > 254 ? 254 : ek) : 1;  // Inf/NaN inputs: undefined but in bounds
+    es = es ? (es > 254 ? 254 : es) : 1;
+    const uint32_t shift = ek + es - 2;   // 0 .. 506
+    const uint64_t v = static_cast<uint64_t>(sk * ss) << (shift & 31);
+    long_add(((uk ^ us) & 0x8000) ? neg : pos, static_cast<int>(shift >> 5), v);
+  }
+  for (int i = ACC_WORDS - 1; i >= 0; --i) {
+    if (pos[i] != neg[i]) return pos[i] > neg[i];
+  }
+  return true;  // exact zero: sign(0) = +1
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Norm of a key whose fp32 sum of squares under- or overflowed: scale by a
+// power of two first (exact), then undo it.
+__device__ float scaled_norm(const uint16_t* key_lds) {
+  uint32_t emax = 0;
+  for (int c = 0; c < D; ++c) {
+    const uint32_t e = (key_lds[c] >> 7) & 0xFF;
+    emax = e > emax ? e : emax;
+  }
+  if (emax == 0) {
+    // all zeros or bf16 subnormals: scale up by 2^64 (exact)
+    float s = 0.f;
+    for (int c = 0; c < D; ++c) {
+      const float v = __uint_as_float(static_cast<uint32_t>(key_lds[c]) << 16) * 0x1.0p64f;
+      s = __builtin_fmaf(v, v, s);
+    }
+    return __builtin_sqrtf(s) * 0x1.0p-64f;
+  }
+  const int e = static_cast<int>(emax) - 127;
+  float s = 0.f;
+  for (int c = 0; c < D; ++c) {
+    const float v = __builtin_ldexpf(__uint_as_float(static_cast<uint32_t>(key_lds[c]) << 16), -e);
+    s = __builtin_fmaf(v, v, s);
+  }
+  return __builtin_ldexpf(__builtin_sqrtf(s), e);
+}
+
+template <int M>
+__global__ __launch_bounds__(64 * (M / CW)) void encode_kernel(
+    const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md,
+    const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
+    float* __restrict__ norms, int64_t R, int n, int cap, int pos, int ntiles, float c1,
+    float c2) {
+  constexpr int W = M / CW;
+  constexpr int NT = 64 * W;
+  constexpr int LOADS = CHUNKS / NT;  // 16-byte loads per thread per tile
+  constexpr int WPR = M / 32;         // words per key row
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TILE_LDS];
+  __shared__ uint32_t long_scratch[W][2 * ACC_WORDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int j = lane & 31;
+  const int cb = wave * CW;
+
+  // Resident A operand: S^T rows for this wave's coordinates.  Block b, row i
+  // holds coordinate cb + 32*((i >> 2) & 1) + 16*b + 4*(i >> 3) + (i & 3), so
+  // the 32x32 result places coordinate cb + 32*half + 16*b + r in register r
+  // of lane (j, half).
+  bf16x8_t a[2][8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int coord = cb + 32 * ((j >> 2) & 1) + 16 * b + 4 * (j >> 3) + (j & 3);
+    const uint4* row = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(coord) * D);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) a[b][s] = as_bf16x8(row[2 * s + half]);
+  }
+  const float smax = col_norm_max[wave];
+
+  uint4 pf[LOADS];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int c = tid + k * NT;
+      const int64_t r = static_cast<int64_t>(tile) * KT + (c >> 4);
+      pf[k] = r < R ? reinterpret_cast<const uint4*>(keys + r * D)[c & 15] : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  if (blockIdx.x < ntiles) load_tile(blockIdx.x);
+  int buf = 0;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    uint8_t* tl = lds + buf * TILE_LDS;
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int c = tid + k * NT;
+      *reinterpret_cast<uint4*>(tl + (c >> 4) * LDS_ROW + (c & 15) * 16) = pf[k];
+    }
+    __syncthreads();
+    if (tile + static_cast<int>(gridDim.x) < ntiles) load_tile(tile + gridDim.x);
+
+    // ---- projection on the matrix cores, norm from the same fragments ----
+    f32x16_t acc0 = {}, acc1 = {};
+    float n2 = 0.f;
+    const uint8_t* krow = tl + j * LDS_ROW + 16 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint4 bv = *reinterpret_cast<const uint4*>(krow + 32 * s);
+      const bf16x8_t bf = as_bf16x8(bv);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], bf, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], bf, acc1, 0, 0, 0);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.x), as_bf16x2(bv.x), n2, false);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.y), as_bf16x2(bv.y), n2, false);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.z), as_bf16x2(bv.z), n2, false);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.w), as_bf16x2(bv.w), n2, false);
+    }
+    n2 += __shfl_xor(n2, 32);
+
+    // ---- certification threshold for this lane's key ----
+    // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
+    // squares plus squares lost below the fp32 normal range (with margin).
+    const float knorm_up = __builtin_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f));
+    const float tau = __builtin_fmaf(c1 * knorm_up, smax, c2);
+
+    // ---- sign and flag words, highest coordinate shifted in first ----
+    uint32_t sw = 0, fw = 0;
+#pragma unroll
+    for (int r = 15; r >= 0; --r) {
+      sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc1[r]), 31);
+      fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
+    }
+#pragma unroll
+    for (int r = 15; r >= 0; --r) {
+      sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc0[r]), 31);
+      fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
+    }
+    uint32_t word = ~sw;
+    uint32_t flags = ~fw;
+    // keys so large that products can overflow fp32: certify every bit
+    if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
+    const int64_t r = static_cast<int64_t>(tile) * KT + j;
+    if (r >= R) flags = 0;  // zero padding of a ragged last tile
+
+    // ---- exact re-evaluation of flagged (key, coordinate) pairs ----
+    uint64_t todo = __ballot(flags != 0);
+    while (todo) {
+      const int src = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      uint32_t fsrc = __shfl(flags, src);
+      const int jsrc = src & 31;
+      const int hsrc = src >> 5;
+      const uint16_t* key_lds = reinterpret_cast<const uint16_t*>(tl + jsrc * LDS_ROW);
+      const uint32_t kpair = reinterpret_cast<const uint32_t*>(key_lds)[lane];
+      if (__ballot((kpair & 0x7FFF7FFFu) != 0) == 0) {
+        // the key is all (+/-) zeros: every projection is exactly 0 -> bit 1
+        if (lane == src) word |= fsrc;
+        continue;
+      }
+      while (fsrc) {
+        const int p = __builtin_ctz(fsrc);
+        fsrc &= fsrc - 1;
+        const int coord = cb + 32 * hsrc + p;
+        const uint16_t* s_row = s_md + static_cast<int64_t>(coord) * D;
+        const uint32_t spair = reinterpret_cast<const uint32_t*>(s_row)[lane];
+        // 128 products split two per lane; each is exact in fp64.
+        const double p0 = bf16_to_f64(kpair & 0xFFFF) * bf16_to_f64(spair & 0xFFFF);
+        const double p1 = bf16_to_f64(kpair >> 16) * bf16_to_f64(spair >> 16);
+        // 7-level tree: |sum - exact| <= 7 * 2^-53 * sum|p| (+ rounding of asum)
+        const double sum = __shfl(wave_sum_f64(p0 + p1), 0);
+        const double asum = __shfl(wave_sum_f64(__builtin_fabs(p0) + __builtin_fabs(p1)), 0);
+        bool bit;
+        if (asum == 0.0) {
+          bit = true;
+        } else if (__builtin_fabs(sum) > 0x1.0p-47 * asum) {
+          bit = sum > 0.0;
+        } else {
+          bool b = false;
+          if (lane == 0) b = exact_sign_long(key_lds, s_row, long_scratch[wave]);
+          bit = __shfl(static_cast<int>(b), 0) != 0;
+        }
+        if (lane == src) word = bit ? (word | (1u << p)) : (word & ~(1u << p));
+      }
+    }
+
+    // ---- stores ----
+    if (r < R) {
+      const int64_t bh = r / n;
+      const int64_t dst = bh * cap + pos + (r - bh * n);
+      signs[dst * WPR + (cb >> 5) + half] = word;
+      if (wave == 0 && half == 0) {
+        float nrm = __builtin_sqrtf(n2);
+        if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) {
+          nrm = scaled_norm(reinterpret_cast<const uint16_t*>(tl + j * LDS_ROW));
+        }
+        norms[dst] = nrm;
+      }
+    }
+    buf ^= 1;
+  }
+}
+
+template <int M>
+int launch_encode_m(const DeviceSketch& s, const void* keys, int64_t R, int n, uint32_t* signs,
+                    float* norms, int cap, int pos, hipStream_t stream) {
+  constexpr int NT = 64 * (M / CW);
+  const int ntiles = static_cast<int>((R + KT - 1) / KT);
+  static int max_grid = 0;  // resident workgroups on this device (fixed per template)
+  if (max_grid == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_kernel<M>, NT, 0) !=
+        hipSuccess)
+      return hipErrorInvalidDeviceFunction;
+    max_grid = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  const int grid = ntiles < max_grid ? ntiles : max_grid;
+  // Error bound of an fp32 sum of D exact products, with a factor 4 margin
+  // over round-to-nearest (covers truncating or blocked accumulation).
+  const float c1 = static_cast<float>(4.0 * D * 0x1.0p-24 * (1.0 + 0x1.0p-10));
+  const float c2 = 0x1.0p-110f;  // absolute floor: subnormal flushes
+  hipLaunchKernelGGL(encode_kernel<M>, dim3(grid), dim3(NT), 0, stream,
+                     static_cast<const uint16_t*>(keys), s.s_md, s.col_norm_max, signs, norms, R,
+                     n, cap, pos, ntiles, c1, c2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int n, uint32_t* signs,
+                  float* norms, int cap, int pos, void* stream) {
+  const int64_t R = static_cast<int64_t>(B) * H_kv * n;
+  if (R == 0) return hipSuccess;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.m == 256) return launch_encode_m<256>(s, keys, R, n, signs, norms, cap, pos, st);
+  return launch_encode_m<512>(s, keys, R, n, signs, norms, cap, pos, st);
+}
+
+}  // namespace qjl

@@ -1,0 +1,44 @@
+// Internal interfaces between the C ABI layer (qjl_abi.hip), the host sketch
+// generator (sketch.cpp) and the kernel launchers (encode.hip, decode.hip).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace qjl {
+
+constexpr int kHeadDim = 128;
+
+// bf16 bit patterns of S ([d][m] row-major) for a seed; see sketch.cpp.
+void generate_sketch_bf16(uint64_t seed, int d, int m, uint16_t* out);
+
+// Device-resident copies of one S, kept by the cache in qjl_abi.hip.
+struct DeviceSketch {
+  const uint16_t* s_dm = nullptr;   // [d][m]  bf16 bits (decode: S^T q)
+  const uint16_t* s_md = nullptr;   // [m][d]  bf16 bits (encode: matrix-core A operand)
+  const float* col_norm_max = nullptr;  // [m/64] max_{i in group} ||S[:, i]||_2, rounded up
+  int d = 0;
+  int m = 0;
+};
+
+// Decode split geometry, shared by the workspace query and the launch.
+struct DecodePlan {
+  int n_split = 0;          // context splits per (batch, kv head)
+  int tokens_per_split = 0; // multiple of the token tile
+  size_t counter_bytes = 0; // B*H_kv uint32, padded to 256 B
+  size_t partial_bytes = 0; // B*H_q*n_split*(d + 2) floats
+  size_t total_bytes = 0;
+};
+
+bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan* plan);
+
+// Kernel launchers; return the HIP error code (0 == hipSuccess).
+int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int n, uint32_t* signs,
+                  float* norms, int cap, int pos, void* stream);
+
+int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,
+                  const uint32_t* signs, const float* norms, const void* values, int B, int H_q,
+                  int H_kv, int N, int cap, float scale, float* out, void* workspace,
+                  void* stream);
+
+}  // namespace qjl

@@ -1,0 +1,54 @@
+"""Helpers for the GPU parity tests: host <-> device marshalling and metrics."""
+
+import sys
+
+import numpy as np
+
+SENTINEL = 0x5A5A5A5A
+
+
+def say(*args):
+    """Names the case about to run on the GPU (flushed, so it survives a crash)."""
+    print("[gpu]", *args, flush=True, file=sys.stderr)
+
+
+def dev_u16(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def dev_u32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).cuda()
+
+
+def host_u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def gpu_encode(qjl, keys_u16, m, seed, cap=None, pos=0, signs=None, norms=None):
+    """keys_u16: [B][H][n][d].  Returns device (signs int32, norms fp32) caches."""
+    import torch
+    B, H, n, d = keys_u16.shape
+    cap = n + pos if cap is None else cap
+    if signs is None:
+        signs = torch.full((B, H, cap, m // 32), SENTINEL, dtype=torch.int32, device="cuda")
+    if norms is None:
+        norms = torch.full((B, H, cap), float("nan"), dtype=torch.float32, device="cuda")
+    qjl.encode_keys(dev_u16(keys_u16), signs, norms, pos, seed, m)
+    torch.cuda.synchronize()
+    return signs, norms
+
+
+def row_rel_l2(got, ref):
+    """max over rows of ||got - ref|| / ||ref|| (rows = all but the last axis)."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, got.shape[-1])
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.maximum(np.linalg.norm(r, axis=1), 1e-300)
+    return float((num / den).max())
