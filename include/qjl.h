@@ -125,11 +125,12 @@ QJL_API size_t qjl_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, 
  *   out          device fp32 [B][H_q][d], 16-byte aligned, written whole.
  *   workspace    device, 256-byte aligned, at least
  *                qjl_decode_workspace_bytes(...) bytes, zero-filled before
- *                its first use.  Its first B*H_kv uint32 are arrival counters
- *                that every call returns to zero; the rest is scratch that
- *                each call overwrites.  A workspace can therefore be reused
- *                by later calls on the same stream; calls that may overlap
- *                (other streams) must not share one.
+ *                its first use.  Its first 4096 bytes hold arrival counters
+ *                (one uint32 per (batch, kv head)) that every call returns
+ *                to zero; the rest is scratch that each call overwrites.  A
+ *                workspace can therefore be reused by later calls of any
+ *                size on the same stream; calls that may overlap (other
+ *                streams) must not share one.
  * Returns QJL_OK, QJL_EINVAL, QJL_EUNSUPPORTED, QJL_EWORKSPACE, QJL_ENOMEM or
  * QJL_EHIP. */
 QJL_API qjl_status qjl_decode_attention(const float *q, const uint32_t *signs, const float *norms,

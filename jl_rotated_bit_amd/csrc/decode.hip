@@ -379,6 +379,7 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
   constexpr int64_t kTargetWorkgroups = 512;
   constexpr int kMinTokens = NW * TILE;
   int64_t want = (kTargetWorkgroups + streams - 1) / streams;
+  if (streams > kMaxCounters) want = 1;   // splits (and counters) only for few streams
   const int64_t most = (N + kMinTokens - 1) / kMinTokens;
   if (want > most) want = most;
   if (want > MAX_SPLITS) want = MAX_SPLITS;
@@ -388,7 +389,10 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
   const int64_t n_split = (N + tps - 1) / tps;
   plan->n_split = static_cast<int>(n_split);
   plan->tokens_per_split = static_cast<int>(tps);
-  plan->counter_bytes = (static_cast<size_t>(streams) * 4 + 255) / 256 * 256;
+  // A fixed-size counter region keeps the counters of every plan clear of the
+  // partials of any other plan, so one zero-filled workspace serves calls of
+  // all sizes.
+  plan->counter_bytes = kCounterRegionBytes;
   const size_t parts = static_cast<size_t>(B) * H_q * n_split;
   plan->partial_bytes = parts * (D + 2) * sizeof(float);
   plan->total_bytes = plan->counter_bytes + plan->partial_bytes;

@@ -21,11 +21,16 @@ struct DeviceSketch {
   int m = 0;
 };
 
+// The decode workspace starts with a fixed region of arrival counters (one
+// uint32 per (batch, kv head)); calls with more streams than that never split.
+constexpr size_t kCounterRegionBytes = 4096;
+constexpr int64_t kMaxCounters = kCounterRegionBytes / 4;
+
 // Decode split geometry, shared by the workspace query and the launch.
 struct DecodePlan {
   int n_split = 0;          // context splits per (batch, kv head)
   int tokens_per_split = 0; // multiple of the token tile
-  size_t counter_bytes = 0; // B*H_kv uint32, padded to 256 B
+  size_t counter_bytes = 0; // kCounterRegionBytes
   size_t partial_bytes = 0; // B*H_q*n_split*(d + 2) floats
   size_t total_bytes = 0;
 };
