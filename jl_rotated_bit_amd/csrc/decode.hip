@@ -44,6 +44,14 @@ constexpr int TILE = 64;         // tokens per wave per step
 constexpr int VCH = TILE * D * 2 / 16 / 64;  // 16-byte value chunks per lane per tile (16)
 constexpr int MAX_SPLITS = 1024;
 
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
@@ -59,16 +67,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // G floats read or written as one LDS access (b32 / b64 / b128; two b128 for G = 8).
+// Coherent (agent-scope) loads of data written by other workgroups.
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_coherent4(const float* p) {
+  return make_float4(ld_coherent(p), ld_coherent(p + 1), ld_coherent(p + 2), ld_coherent(p + 3));
+}
+
 template <int G>
 struct alignas(G >= 4 ? 16 : 4 * G) VecG {
   float v[G];
 };
 
 template <int M, int G>
-__global__ __launch_bounds__(NT) void decode_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1))) void decode_kernel(
     const float* __restrict__ q, const uint32_t* __restrict__ signs,
     const float* __restrict__ norms, const uint16_t* __restrict__ values,
-    const uint16_t* __restrict__ s_dm, int H_kv, int N, int cap, int n_split, int tps,
+    const uint16_t* __restrict__ s_md, int H_kv, int N, int cap, int n_split, int tps,
     float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
     float* __restrict__ part_acc, float* __restrict__ part_ml) {
   constexpr int WPR = M / 32;        // sign words per token
@@ -80,7 +96,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   __shared__ __attribute__((aligned(16))) float qs[G][D];
   __shared__ __attribute__((aligned(16))) float sq[G][M];
   __shared__ __attribute__((aligned(16))) float pbuf[NW][TILE][G];
-  __shared__ float red_acc[NW][G][D];
+  // wave partials [NW][G][D] after the loop; merge replicas [REP][G*D/4] float4 later
+  constexpr int RED_FLOATS = (NW * G * D > 4 * NT) ? NW * G * D : 4 * NT;
+  __shared__ __attribute__((aligned(16))) float red_buf[RED_FLOATS];
   __shared__ float red_ml[NW][G][2];
   __shared__ int is_last;
 
@@ -125,35 +143,87 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   int t0 = t_begin + wave * TILE;
   if (t0 < t_end) load_tile(t0, vc, sc, nc);
 
-  // ---- prologue: q -> LDS, S^T q, nibble table ----
+  // ---- prologue: q -> LDS, S^T q on the matrix cores, nibble table ----
+  // q is split into three bf16 parts (hi + mid + lo reproduces fp32 q to
+  // within 2^-24 relative); column 3*... of the B operand holds part p of head
+  // g at column p*G + g, so one 32x32x16 MFMA chain per block of 32 sketch
+  // coordinates yields all parts of all heads, with fp32 accumulation.
+  constexpr int NBLK = M / 32;            // blocks of 32 sketch coordinates
+  constexpr int BPW = NBLK / NW;          // blocks per wave (2 or 4)
+  constexpr int BATCH = 2;                // blocks whose S^T fragments are in flight together
+  static_assert(BPW % BATCH == 0, "blocks per wave must be a multiple of the batch");
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  uint4 af[BATCH][8];
+  auto load_frags = [&](int batch) {
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) {
+      const int blk = wave + NW * (batch * BATCH + bb);
+      const uint4* arow = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(32 * blk + col) * D);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) af[bb][st] = arow[2 * st + half];
+    }
+  };
+  load_frags(0);
+
   const float* qb = q + (static_cast<int64_t>(b) * H_kv + kvh) * G * D;
   for (int i = tid; i < G * D; i += NT) qs[i / D][i % D] = qb[i];
   __syncthreads();
-  for (int i = tid; i < M; i += NT) {
-    float acc[G];
+  {
+    const int part = col / G;
+    const int g = col % G;
+    bf16x8_t bq[8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-#pragma unroll 8
-    for (int jj = 0; jj < D; ++jj) {
-      const float s = __uint_as_float(static_cast<uint32_t>(s_dm[jj * M + i]) << 16);
+    for (int st = 0; st < 8; ++st) {
+      uint32_t pk[4];
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = __builtin_fmaf(s, qs[g][jj], acc[g]);
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t h2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float x = part < 3 ? qs[g][16 * st + 8 * half + e + u] : 0.f;
+          const uint32_t hi = f32_to_bf16_rne(x);
+          const float r1 = x - __uint_as_float(hi << 16);
+          const uint32_t mid = f32_to_bf16_rne(r1);
+          const float r2 = r1 - __uint_as_float(mid << 16);
+          const uint32_t lo = f32_to_bf16_rne(r2);
+          h2[u] = part == 0 ? hi : (part == 1 ? mid : lo);
+        }
+        pk[e / 2] = h2[0] | (h2[1] << 16);
+      }
+      bq[st] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) sq[g][i] = acc[g];
+    for (int batch = 0; batch < BPW / BATCH; ++batch) {
+      if (batch > 0) load_frags(batch);
+#pragma unroll
+      for (int bb = 0; bb < BATCH; ++bb) {
+        const int blk = wave + NW * (batch * BATCH + bb);
+        f32x16_t acc = {};
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[bb][st]), bq[st], acc, 0, 0, 0);
+        // lane (col, half), register r -> coordinate 32*blk + 8*(r/4) + 4*half + r%4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = acc[r] + __shfl(acc[r], lane + G) + __shfl(acc[r], lane + 2 * G);
+          if (col < G) sq[col][32 * blk + 8 * (r >> 2) + 4 * half + (r & 3)] = v;
+        }
+      }
+    }
   }
   __syncthreads();
   for (int e = tid; e < NPOS * 16; e += NT) {
     const int p = e >> 4, v = e & 15;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float s = 0.f;
+      float sacc = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float x = sq[g][4 * p + k];
-        s += ((v >> k) & 1) ? x : -x;
+        sacc += ((v >> k) & 1) ? x : -x;
       }
-      lut[e * G + g] = s;
+      lut[e * G + g] = sacc;
     }
   }
   __syncthreads();
@@ -253,7 +323,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red_acc[wave][g][8 * lane + e] = acc[g][e];
+      for (int e = 0; e < 8; ++e) red_buf[(wave * G + g) * D + 8 * lane + e] = acc[g][e];
     }
   }
   if (lane == 0) {
@@ -277,42 +347,50 @@ __global__ __launch_bounds__(NT) void decode_kernel(
       const float mw = red_ml[w][g][0];
       const float f = mw == -INFINITY ? 0.f : exp2f(mw - mx);
       L += red_ml[w][g][1] * f;
-      A += red_acc[w][g][dd] * f;
+      A += red_buf[(w * G + g) * D + dd] * f;
     }
     if (n_split == 1) {
       out[(bh * G + g) * D + dd] = A / L;
     } else {
-      part_acc[(slot0 * G + g) * D + dd] = A;
+      // coherent (sc1) stores: visible to every XCD once complete, with no
+      // L2-wide write-back (an agent-scope fence would flush the whole L2)
+      __hip_atomic_store(&part_acc[(slot0 * G + g) * D + dd], A, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
       if (dd == 0) {
-        part_ml[(slot0 * G + g) * 2 + 0] = mx;
-        part_ml[(slot0 * G + g) * 2 + 1] = L;
+        __hip_atomic_store(&part_ml[(slot0 * G + g) * 2 + 0], mx, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&part_ml[(slot0 * G + g) * 2 + 1], L, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   if (n_split == 1) return;
 
   // ---- last workgroup of this (batch, kv head) merges the splits ----
-  __threadfence();
+  // Release: wait until this thread's coherent partial stores are complete,
+  // then (after the barrier) count this workgroup in.  Acquire: the merge
+  // below reads partials only with coherent loads issued after the count.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(&counters[bh], 1u);
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == static_cast<uint32_t>(n_split - 1));
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
 
   // weights w_s,g = exp2(m_s - M) / L  (reuse the table memory)
   float* wts = lut;   // n_split * G floats (n_split <= MAX_SPLITS)
   __shared__ float gmax[G], gsum[G];
   for (int g = wave; g < G; g += NW) {
     float mx = -INFINITY;
-    for (int s = lane; s < n_split; s += 64) mx = fmaxf(mx, part_ml[((bh * n_split + s) * G + g) * 2]);
+    for (int s = lane; s < n_split; s += 64) mx = fmaxf(mx, ld_coherent(&part_ml[((bh * n_split + s) * G + g) * 2]));
     mx = wave_max(mx);
     float L = 0.f;
     for (int s = lane; s < n_split; s += 64) {
       const float* ml = part_ml + ((bh * n_split + s) * G + g) * 2;
-      L += ml[1] * exp2f(ml[0] - mx);
+      L += ld_coherent(ml + 1) * exp2f(ld_coherent(ml) - mx);
     }
     L = wave_sum(L);
     if (lane == 0) {
@@ -324,18 +402,67 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   for (int i = tid; i < n_split * G; i += NT) {
     const int s = i / G, g = i % G;
     const float* ml = part_ml + ((bh * n_split + s) * G + g) * 2;
-    wts[i] = exp2f(ml[0] - gmax[g]) / gsum[g];
+    wts[i] = exp2f(ld_coherent(ml) - gmax[g]) / gsum[g];
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += NT) {
-    const int g = i / D, dd = i % D;
-    float o = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      o = __builtin_fmaf(wts[s * G + g], part_acc[((bh * n_split + s) * G + g) * D + dd], o);
+  // Threads own (head, 4 channels) pairs; with fewer pairs than threads the
+  // splits are divided among REP replicas whose sums meet in LDS.  Loads go
+  // out 8 splits at a time.
+  {
+    constexpr int PAIRS = G * D / 4;
+    constexpr int REP = PAIRS >= NT ? 1 : NT / PAIRS;
+    static_assert(REP == 1 || REP * PAIRS * 4 <= RED_FLOATS, "merge replicas exceed the LDS buffer");
+    float4* rbuf = reinterpret_cast<float4*>(red_buf);   // REP * PAIRS <= NT float4 <= RED_FLOATS / 4
+    const float* pa = part_acc;
+    for (int i = tid; i < PAIRS * REP; i += NT) {
+      const int pr = i % PAIRS, rep = i / PAIRS;
+      const int g = pr / (D / 4), c4 = pr % (D / 4);
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      int s = rep;
+      for (; s + 7 * REP < n_split; s += 8 * REP) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ld_coherent4(pa + (((bh * n_split + s + u * REP) * G + g) * (D / 4) + c4) * 4);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wgt = wts[(s + u * REP) * G + g];
+          o.x = __builtin_fmaf(wgt, v[u].x, o.x);
+          o.y = __builtin_fmaf(wgt, v[u].y, o.y);
+          o.z = __builtin_fmaf(wgt, v[u].z, o.z);
+          o.w = __builtin_fmaf(wgt, v[u].w, o.w);
+        }
+      }
+      for (; s < n_split; s += REP) {
+        const float4 v = ld_coherent4(pa + (((bh * n_split + s) * G + g) * (D / 4) + c4) * 4);
+        const float wgt = wts[s * G + g];
+        o.x = __builtin_fmaf(wgt, v.x, o.x);
+        o.y = __builtin_fmaf(wgt, v.y, o.y);
+        o.z = __builtin_fmaf(wgt, v.z, o.z);
+        o.w = __builtin_fmaf(wgt, v.w, o.w);
+      }
+      if (REP == 1) {
+        reinterpret_cast<float4*>(out)[(bh * G + g) * (D / 4) + c4] = o;
+      } else {
+        rbuf[rep * PAIRS + pr] = o;
+      }
     }
-    out[(bh * G + g) * D + dd] = o;
+    if (REP > 1) {
+      __syncthreads();
+      for (int pr = tid; pr < PAIRS; pr += NT) {
+        float4 o = rbuf[pr];
+        for (int rep = 1; rep < REP; ++rep) {
+          const float4 v = rbuf[rep * PAIRS + pr];
+          o.x += v.x;
+          o.y += v.y;
+          o.z += v.z;
+          o.w += v.w;
+        }
+        const int g = pr / (D / 4), c4 = pr % (D / 4);
+        reinterpret_cast<float4*>(out)[(bh * G + g) * (D / 4) + c4] = o;
+      }
+    }
   }
-  if (tid == 0) counters[bh] = 0u;
+  if (tid == 0) __hip_atomic_store(&counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int M, int G>
@@ -349,7 +476,7 @@ int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float*
   float* part_ml = part_acc + static_cast<size_t>(B) * H_kv * G * plan.n_split * D;
   dim3 grid(plan.n_split, H_kv, B);
   hipLaunchKernelGGL((decode_kernel<M, G>), grid, dim3(NT), 0, stream, q, signs, norms,
-                     static_cast<const uint16_t*>(values), s.s_dm, H_kv, N, cap, plan.n_split,
+                     static_cast<const uint16_t*>(values), s.s_md, H_kv, N, cap, plan.n_split,
                      plan.tokens_per_split, coef, out, counters, part_acc, part_ml);
   return hipGetLastError();
 }

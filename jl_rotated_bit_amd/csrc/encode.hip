@@ -42,12 +42,14 @@ typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int D = kHeadDim;          // 128 key channels
-constexpr int KT = 32;               // keys per tile = MFMA N block
+constexpr int KB = 32;               // keys per MFMA column block
+constexpr int NBLK = 4;              // column blocks per tile
+constexpr int KT = KB * NBLK;        // keys per tile (128)
 constexpr int CW = 64;               // sketch coordinates per wave
 constexpr int ROW_B = D * 2;         // 256 bytes per key
 constexpr int LDS_ROW = ROW_B + 16;  // padded LDS row: spreads lanes over banks
 constexpr int TILE_LDS = KT * LDS_ROW;
-constexpr int CHUNKS = KT * ROW_B / 16;  // 16-byte chunks per key tile (512)
+constexpr int CHUNKS = KT * ROW_B / 16;  // 16-byte chunks per key tile (2048)
 constexpr int ACC_WORDS = 18;        // long accumulator: 576 bits
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -136,7 +138,7 @@ __device__ float scaled_norm(const uint16_t* key_lds) {
 }
 
 template <int M>
-__global__ __launch_bounds__(64 * (M / CW)) void encode_kernel(
+__global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2))) void encode_kernel(
     const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md,
     const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
     float* __restrict__ norms, int64_t R, int n, int cap, int pos, int ntiles, float c1,
@@ -192,100 +194,102 @@ __global__ __launch_bounds__(64 * (M / CW)) void encode_kernel(
     __syncthreads();
     if (tile + static_cast<int>(gridDim.x) < ntiles) load_tile(tile + gridDim.x);
 
-    // ---- projection on the matrix cores, norm from the same fragments ----
-    f32x16_t acc0 = {}, acc1 = {};
-    float n2 = 0.f;
-    const uint8_t* krow = tl + j * LDS_ROW + 16 * half;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4 bv = *reinterpret_cast<const uint4*>(krow + 32 * s);
-      const bf16x8_t bf = as_bf16x8(bv);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], bf, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], bf, acc1, 0, 0, 0);
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.x), as_bf16x2(bv.x), n2, false);
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.y), as_bf16x2(bv.y), n2, false);
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.z), as_bf16x2(bv.z), n2, false);
-      n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.w), as_bf16x2(bv.w), n2, false);
-    }
-    n2 += __shfl_xor(n2, 32);
-
-    // ---- certification threshold for this lane's key ----
-    // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
-    // squares plus squares lost below the fp32 normal range (with margin).
-    const float knorm_up = __builtin_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f));
-    const float tau = __builtin_fmaf(c1 * knorm_up, smax, c2);
-
-    // ---- sign and flag words, highest coordinate shifted in first ----
-    uint32_t sw = 0, fw = 0;
-#pragma unroll
-    for (int r = 15; r >= 0; --r) {
-      sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc1[r]), 31);
-      fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
-    }
-#pragma unroll
-    for (int r = 15; r >= 0; --r) {
-      sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc0[r]), 31);
-      fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
-    }
-    uint32_t word = ~sw;
-    uint32_t flags = ~fw;
-    // keys so large that products can overflow fp32: certify every bit
-    if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
-    const int64_t r = static_cast<int64_t>(tile) * KT + j;
-    if (r >= R) flags = 0;  // zero padding of a ragged last tile
-
-    // ---- exact re-evaluation of flagged (key, coordinate) pairs ----
-    uint64_t todo = __ballot(flags != 0);
-    while (todo) {
-      const int src = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      uint32_t fsrc = __shfl(flags, src);
-      const int jsrc = src & 31;
-      const int hsrc = src >> 5;
-      const uint16_t* key_lds = reinterpret_cast<const uint16_t*>(tl + jsrc * LDS_ROW);
-      const uint32_t kpair = reinterpret_cast<const uint32_t*>(key_lds)[lane];
-      if (__ballot((kpair & 0x7FFF7FFFu) != 0) == 0) {
-        // the key is all (+/-) zeros: every projection is exactly 0 -> bit 1
-        if (lane == src) word |= fsrc;
-        continue;
+    for (int nb = 0; nb < NBLK; ++nb) {
+      // ---- projection on the matrix cores, norm from the same fragments ----
+      f32x16_t acc0 = {}, acc1 = {};
+      float n2 = 0.f;
+      const uint8_t* krow = tl + (nb * KB + j) * LDS_ROW + 16 * half;
+  #pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint4 bv = *reinterpret_cast<const uint4*>(krow + 32 * s);
+        const bf16x8_t bf = as_bf16x8(bv);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], bf, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], bf, acc1, 0, 0, 0);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.x), as_bf16x2(bv.x), n2, false);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.y), as_bf16x2(bv.y), n2, false);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.z), as_bf16x2(bv.z), n2, false);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.w), as_bf16x2(bv.w), n2, false);
       }
-      while (fsrc) {
-        const int p = __builtin_ctz(fsrc);
-        fsrc &= fsrc - 1;
-        const int coord = cb + 32 * hsrc + p;
-        const uint16_t* s_row = s_md + static_cast<int64_t>(coord) * D;
-        const uint32_t spair = reinterpret_cast<const uint32_t*>(s_row)[lane];
-        // 128 products split two per lane; each is exact in fp64.
-        const double p0 = bf16_to_f64(kpair & 0xFFFF) * bf16_to_f64(spair & 0xFFFF);
-        const double p1 = bf16_to_f64(kpair >> 16) * bf16_to_f64(spair >> 16);
-        // 7-level tree: |sum - exact| <= 7 * 2^-53 * sum|p| (+ rounding of asum)
-        const double sum = __shfl(wave_sum_f64(p0 + p1), 0);
-        const double asum = __shfl(wave_sum_f64(__builtin_fabs(p0) + __builtin_fabs(p1)), 0);
-        bool bit;
-        if (asum == 0.0) {
-          bit = true;
-        } else if (__builtin_fabs(sum) > 0x1.0p-47 * asum) {
-          bit = sum > 0.0;
-        } else {
-          bool b = false;
-          if (lane == 0) b = exact_sign_long(key_lds, s_row, long_scratch[wave]);
-          bit = __shfl(static_cast<int>(b), 0) != 0;
-        }
-        if (lane == src) word = bit ? (word | (1u << p)) : (word & ~(1u << p));
-      }
-    }
+      n2 += __shfl_xor(n2, 32);
 
-    // ---- stores ----
-    if (r < R) {
-      const int64_t bh = r / n;
-      const int64_t dst = bh * cap + pos + (r - bh * n);
-      signs[dst * WPR + (cb >> 5) + half] = word;
-      if (wave == 0 && half == 0) {
-        float nrm = __builtin_sqrtf(n2);
-        if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) {
-          nrm = scaled_norm(reinterpret_cast<const uint16_t*>(tl + j * LDS_ROW));
+      // ---- certification threshold for this lane's key ----
+      // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
+      // squares plus squares lost below the fp32 normal range (with margin).
+      const float knorm_up = __builtin_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f));
+      const float tau = __builtin_fmaf(c1 * knorm_up, smax, c2);
+
+      // ---- sign and flag words, highest coordinate shifted in first ----
+      uint32_t sw = 0, fw = 0;
+  #pragma unroll
+      for (int r = 15; r >= 0; --r) {
+        sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc1[r]), 31);
+        fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
+      }
+  #pragma unroll
+      for (int r = 15; r >= 0; --r) {
+        sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc0[r]), 31);
+        fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
+      }
+      uint32_t word = ~sw;
+      uint32_t flags = ~fw;
+      // keys so large that products can overflow fp32: certify every bit
+      if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
+      const int64_t r = static_cast<int64_t>(tile) * KT + nb * KB + j;
+      if (r >= R) flags = 0;  // zero padding of a ragged last tile
+
+      // ---- exact re-evaluation of flagged (key, coordinate) pairs ----
+      uint64_t todo = __ballot(flags != 0);
+      while (todo) {
+        const int src = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        uint32_t fsrc = __shfl(flags, src);
+        const int jsrc = src & 31;
+        const int hsrc = src >> 5;
+        const uint16_t* key_lds = reinterpret_cast<const uint16_t*>(tl + (nb * KB + jsrc) * LDS_ROW);
+        const uint32_t kpair = reinterpret_cast<const uint32_t*>(key_lds)[lane];
+        if (__ballot((kpair & 0x7FFF7FFFu) != 0) == 0) {
+          // the key is all (+/-) zeros: every projection is exactly 0 -> bit 1
+          if (lane == src) word |= fsrc;
+          continue;
         }
-        norms[dst] = nrm;
+        while (fsrc) {
+          const int p = __builtin_ctz(fsrc);
+          fsrc &= fsrc - 1;
+          const int coord = cb + 32 * hsrc + p;
+          const uint16_t* s_row = s_md + static_cast<int64_t>(coord) * D;
+          const uint32_t spair = reinterpret_cast<const uint32_t*>(s_row)[lane];
+          // 128 products split two per lane; each is exact in fp64.
+          const double p0 = bf16_to_f64(kpair & 0xFFFF) * bf16_to_f64(spair & 0xFFFF);
+          const double p1 = bf16_to_f64(kpair >> 16) * bf16_to_f64(spair >> 16);
+          // 7-level tree: |sum - exact| <= 7 * 2^-53 * sum|p| (+ rounding of asum)
+          const double sum = __shfl(wave_sum_f64(p0 + p1), 0);
+          const double asum = __shfl(wave_sum_f64(__builtin_fabs(p0) + __builtin_fabs(p1)), 0);
+          bool bit;
+          if (asum == 0.0) {
+            bit = true;
+          } else if (__builtin_fabs(sum) > 0x1.0p-47 * asum) {
+            bit = sum > 0.0;
+          } else {
+            bool b = false;
+            if (lane == 0) b = exact_sign_long(key_lds, s_row, long_scratch[wave]);
+            bit = __shfl(static_cast<int>(b), 0) != 0;
+          }
+          if (lane == src) word = bit ? (word | (1u << p)) : (word & ~(1u << p));
+        }
+      }
+
+      // ---- stores ----
+      if (r < R) {
+        const int64_t bh = r / n;
+        const int64_t dst = bh * cap + pos + (r - bh * n);
+        signs[dst * WPR + (cb >> 5) + half] = word;
+        if (wave == 0 && half == 0) {
+          float nrm = __builtin_sqrtf(n2);
+          if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) {
+            nrm = scaled_norm(reinterpret_cast<const uint16_t*>(tl + (nb * KB + j) * LDS_ROW));
+          }
+          norms[dst] = nrm;
+        }
       }
     }
     buf ^= 1;
