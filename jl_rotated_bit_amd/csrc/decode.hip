@@ -42,7 +42,7 @@ constexpr int NW = 4;            // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr int TILE = 64;         // tokens per wave per step
 constexpr int VCH = TILE * D * 2 / 16 / 64;  // 16-byte value chunks per lane per tile (16)
-constexpr int MAX_SPLITS = 1024;
+constexpr int MAX_SPLITS = 256;
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
@@ -67,14 +67,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // G floats read or written as one LDS access (b32 / b64 / b128; two b128 for G = 8).
-// Coherent (agent-scope) loads of data written by other workgroups.
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float4 ld_coherent4(const float* p) {
-  return make_float4(ld_coherent(p), ld_coherent(p + 1), ld_coherent(p + 2), ld_coherent(p + 3));
-}
-
 template <int G>
 struct alignas(G >= 4 ? 16 : 4 * G) VecG {
   float v[G];
@@ -141,7 +133,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
     }
   };
   int t0 = t_begin + wave * TILE;
-  if (t0 < t_end) load_tile(t0, vc, sc, nc);
 
   // ---- prologue: q -> LDS, S^T q on the matrix cores, nibble table ----
   // q is split into three bf16 parts (hi + mid + lo reproduces fp32 q to
@@ -166,8 +157,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
   };
   load_frags(0);
 
+  // Issue order matters: the S^T fragments and q are loaded before the first
+  // tile, so waiting for q (memory counters drain in order) does not also
+  // wait for the tile, which stays in flight through the whole prologue.
   const float* qb = q + (static_cast<int64_t>(b) * H_kv + kvh) * G * D;
-  for (int i = tid; i < G * D; i += NT) qs[i / D][i % D] = qb[i];
+  constexpr int QPT = (G * D + NT - 1) / NT;
+  float qv[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) qv[k] = (tid + k * NT < G * D) ? qb[tid + k * NT] : 0.f;
+  if (t0 < t_end) load_tile(t0, vc, sc, nc);
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * NT;
+    if (i < G * D) qs[i / D][i % D] = qv[k];
+  }
   __syncthreads();
   {
     const int part = col / G;
@@ -368,8 +371,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
 
   // ---- last workgroup of this (batch, kv head) merges the splits ----
   // Release: wait until this thread's coherent partial stores are complete,
-  // then (after the barrier) count this workgroup in.  Acquire: the merge
-  // below reads partials only with coherent loads issued after the count.
+  // then (after the barrier) count this workgroup in.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -380,18 +382,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
   __syncthreads();
   if (!is_last) return;
 
-  // weights w_s,g = exp2(m_s - M) / L  (reuse the table memory)
-  float* wts = lut;   // n_split * G floats (n_split <= MAX_SPLITS)
+  // Acquire for this workgroup only: drop stale cache lines, after which
+  // plain (vector) loads see the partials the other workgroups stored
+  // coherently.  Only the last workgroup of each (batch, kv head) pays it.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // (1) all (max, sum) pairs into LDS in one round of loads
+  float* ml_l = lut;                      // 2 * n_split * G floats
+  float* wts = lut + 2 * MAX_SPLITS * G;  // n_split * G floats
+  static_assert(3 * MAX_SPLITS * G <= LUT_FLOATS, "merge scratch exceeds the table");
+  {
+    const float2* src = reinterpret_cast<const float2*>(part_ml + bh * n_split * G * 2);
+    for (int i = tid; i < n_split * G; i += NT) reinterpret_cast<float2*>(ml_l)[i] = src[i];
+  }
+  __syncthreads();
+  // (2) per head: global max and normalizer, then per-split weights
   __shared__ float gmax[G], gsum[G];
   for (int g = wave; g < G; g += NW) {
     float mx = -INFINITY;
-    for (int s = lane; s < n_split; s += 64) mx = fmaxf(mx, ld_coherent(&part_ml[((bh * n_split + s) * G + g) * 2]));
+    for (int s = lane; s < n_split; s += 64) mx = fmaxf(mx, ml_l[(s * G + g) * 2]);
     mx = wave_max(mx);
     float L = 0.f;
-    for (int s = lane; s < n_split; s += 64) {
-      const float* ml = part_ml + ((bh * n_split + s) * G + g) * 2;
-      L += ld_coherent(ml + 1) * exp2f(ld_coherent(ml) - mx);
-    }
+    for (int s = lane; s < n_split; s += 64) L += ml_l[(s * G + g) * 2 + 1] * exp2f(ml_l[(s * G + g) * 2] - mx);
     L = wave_sum(L);
     if (lane == 0) {
       gmax[g] = mx;
@@ -399,21 +410,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
     }
   }
   __syncthreads();
-  for (int i = tid; i < n_split * G; i += NT) {
-    const int s = i / G, g = i % G;
-    const float* ml = part_ml + ((bh * n_split + s) * G + g) * 2;
-    wts[i] = exp2f(ld_coherent(ml) - gmax[g]) / gsum[g];
-  }
+  for (int i = tid; i < n_split * G; i += NT) wts[i] = exp2f(ml_l[2 * i] - gmax[i % G]) / gsum[i % G];
   __syncthreads();
-  // Threads own (head, 4 channels) pairs; with fewer pairs than threads the
-  // splits are divided among REP replicas whose sums meet in LDS.  Loads go
-  // out 8 splits at a time.
+  // (3) weighted sum of the partial accumulators.  Threads own (head, 4
+  // channels) pairs; with fewer pairs than threads the splits are divided
+  // among REP replicas whose sums meet in LDS.  Loads go out 8 at a time.
   {
     constexpr int PAIRS = G * D / 4;
     constexpr int REP = PAIRS >= NT ? 1 : NT / PAIRS;
     static_assert(REP == 1 || REP * PAIRS * 4 <= RED_FLOATS, "merge replicas exceed the LDS buffer");
-    float4* rbuf = reinterpret_cast<float4*>(red_buf);   // REP * PAIRS <= NT float4 <= RED_FLOATS / 4
-    const float* pa = part_acc;
+    float4* rbuf = reinterpret_cast<float4*>(red_buf);
+    const float4* pa = reinterpret_cast<const float4*>(part_acc);
     for (int i = tid; i < PAIRS * REP; i += NT) {
       const int pr = i % PAIRS, rep = i / PAIRS;
       const int g = pr / (D / 4), c4 = pr % (D / 4);
@@ -422,7 +429,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
       for (; s + 7 * REP < n_split; s += 8 * REP) {
         float4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = ld_coherent4(pa + (((bh * n_split + s + u * REP) * G + g) * (D / 4) + c4) * 4);
+        for (int u = 0; u < 8; ++u) v[u] = pa[((bh * n_split + s + u * REP) * G + g) * (D / 4) + c4];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const float wgt = wts[(s + u * REP) * G + g];
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
         }
       }
       for (; s < n_split; s += REP) {
-        const float4 v = ld_coherent4(pa + (((bh * n_split + s) * G + g) * (D / 4) + c4) * 4);
+        const float4 v = pa[((bh * n_split + s) * G + g) * (D / 4) + c4];
         const float wgt = wts[s * G + g];
         o.x = __builtin_fmaf(wgt, v.x, o.x);
         o.y = __builtin_fmaf(wgt, v.y, o.y);
