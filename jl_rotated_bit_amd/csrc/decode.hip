@@ -14,19 +14,24 @@
 // bytes of sign words, 4 bytes of norm and 2d bytes of bf16 values.
 // * Grid = (context split, kv head, batch).  A workgroup (4 waves) serves the
 //   G query heads of one kv head over one token range.
-// * Prologue: S^T q for the G heads (fp32) and, from it, a table in LDS of the
-//   16 possible signed sums of every group of 4 consecutive sketch
-//   coordinates (per head).  The bit dot product of a token then costs m/4
-//   table reads and adds per head instead of m masked adds.
-// * Main loop: a wave takes 64 tokens at a time.  Lane t of the wave scores
-//   token t (its m/32 sign words and norm arrive with 16-byte loads); the
-//   wave does the online-softmax update; then lanes regroup to 16 per token
-//   row and accumulate p * v over 16-byte value chunks.  The next tile's loads
-//   are issued before the current tile is used.
-// * Epilogue: waves merge in LDS; the workgroup writes its partial
-//   (max, sum, acc) per head; the last workgroup of a (batch, kv head) to
-//   arrive (atomic counter) merges all splits by log-sum-exp and writes out,
-//   then returns the counter to zero.
+// * Prologue: q is split once per workgroup into three bf16 parts; S^T q for
+//   the G heads then runs on the matrix cores (fp32 accumulation), and feeds
+//   an LDS table of the 16 signed sums of every group of 4 consecutive sketch
+//   coordinates, per head.  A token's bit dot product then costs m/4 table
+//   reads and adds per head instead of m masked adds.  The first token tile's
+//   loads are in flight during the whole prologue.
+// * Main loop, per wave and 64-token tile: lane t scores token t (its sign
+//   words and norm arrive with 16-byte loads) and does the online-softmax
+//   update; the probabilities, split into bf16 hi + lo parts, go to LDS.  The
+//   value rows (16-byte loads, 16 lanes per row) go to a wave-private,
+//   padded, row-permuted LDS tile, are read back transposed (ds_read_b64_tr_b16) as
+//   the B operand of v_mfma_f32_16x16x32_bf16, and P (rows = head x part) V
+//   accumulates on the matrix cores.  The next tile's loads are issued
+//   before the current tile is used.
+// * Epilogue: waves merge in LDS; the workgroup stores its partial
+//   (max, sum, acc) per head with coherent stores; the last workgroup of a
+//   (batch, kv head) to arrive (atomic counter) merges all splits by
+//   log-sum-exp and writes out, then returns the counter to zero.
 
 #include <hip/hip_runtime.h>
 
@@ -41,19 +46,22 @@ constexpr int D = kHeadDim;
 constexpr int NW = 4;            // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr int TILE = 64;         // tokens per wave per step
+constexpr int HALF = 32;         // tokens per P.V matrix step (MFMA K)
 constexpr int VCH = TILE * D * 2 / 16 / 64;  // 16-byte value chunks per lane per tile (16)
+constexpr int NDB = D / 16;      // 16-column blocks of the output (8)
+constexpr int VROW = D * 2 + 32; // bytes per value row in LDS (256 + 32 padding)
+constexpr int VBUF = HALF * VROW;            // wave-private value tile (9 KB)
 constexpr int MAX_SPLITS = 256;
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-
-__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -66,6 +74,13 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// LDS row of token t (0..31) of a half tile.  A transposed read by 32 lanes
+// touches tokens {0..3, 8..11} (+4, +16 variants); with 288-byte rows, row r
+// starts on bank 8*(r mod 8), so swapping rows 8..11 with 12..15 (and 24..27
+// with 28..31) puts those 8 tokens on 8 distinct bank groups.  Every column
+// offset stays an immediate.
+__device__ __forceinline__ constexpr int vrow(int t) { return t ^ ((t & 8) >> 1); }
+
 // G floats read or written as one LDS access (b32 / b64 / b128; two b128 for G = 8).
 template <int G>
 struct alignas(G >= 4 ? 16 : 4 * G) VecG {
@@ -73,26 +88,43 @@ struct alignas(G >= 4 ? 16 : 4 * G) VecG {
 };
 
 template <int M, int G>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1))) void decode_kernel(
+struct DecodeLds {
+  static constexpr int NPOS = M / 4;                 // nibble positions
+  static constexpr int LUT_FLOATS = NPOS * 16 * G;
+  static constexpr int LUT_BYTES = LUT_FLOATS * 4;
+  static constexpr int PB_BYTES = NW * 2 * G * TILE * 2;   // bf16 P parts
+  static constexpr int VB_BYTES = NW * VBUF;               // value tiles
+  // prologue scratch (aliases the value tiles)
+  static constexpr int QS_BYTES = G * D * 4;
+  static constexpr int QF_BYTES = 8 * 2 * 32 * 16;         // q parts as MFMA operand
+  static constexpr int SQ_BYTES = G * M * 4;
+  static_assert(QS_BYTES + QF_BYTES + SQ_BYTES <= VB_BYTES, "prologue scratch exceeds the value tiles");
+  static_assert(G * D * 4 <= VBUF, "wave partial exceeds its value tile");
+  static constexpr int TOTAL = LUT_BYTES + PB_BYTES + VB_BYTES;
+};
+
+template <int M, int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     const float* __restrict__ q, const uint32_t* __restrict__ signs,
     const float* __restrict__ norms, const uint16_t* __restrict__ values,
     const uint16_t* __restrict__ s_md, int H_kv, int N, int cap, int n_split, int tps,
     float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
     float* __restrict__ part_acc, float* __restrict__ part_ml) {
+  using L = DecodeLds<M, G>;
   constexpr int WPR = M / 32;        // sign words per token
   constexpr int SV = WPR / 4;        // 16-byte sign loads per token
-  constexpr int NPOS = M / 4;        // nibble positions
-  constexpr int LUT_FLOATS = NPOS * 16 * G;
+  constexpr int NPOS = L::NPOS;
+  static_assert(2 * G <= 16, "P rows (head x part) must fit one 16-row MFMA block");
 
-  __shared__ __attribute__((aligned(16))) float lut[LUT_FLOATS];
-  __shared__ __attribute__((aligned(16))) float qs[G][D];
-  __shared__ __attribute__((aligned(16))) float sq[G][M];
-  __shared__ __attribute__((aligned(16))) float pbuf[NW][TILE][G];
-  // wave partials [NW][G][D] after the loop; merge replicas [REP][G*D/4] float4 later
-  constexpr int RED_FLOATS = (NW * G * D > 4 * NT) ? NW * G * D : 4 * NT;
-  __shared__ __attribute__((aligned(16))) float red_buf[RED_FLOATS];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::TOTAL];
   __shared__ float red_ml[NW][G][2];
   __shared__ int is_last;
+  float* lut = reinterpret_cast<float*>(smem);
+  uint8_t* pb_all = smem + L::LUT_BYTES;
+  uint8_t* vb_all = smem + L::LUT_BYTES + L::PB_BYTES;
+  float* qs = reinterpret_cast<float*>(vb_all);                                  // [G][D]
+  uint4* qfrag = reinterpret_cast<uint4*>(vb_all + L::QS_BYTES);                 // [8][2][32]
+  float* sq = reinterpret_cast<float*>(vb_all + L::QS_BYTES + L::QF_BYTES);      // [G][M]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,12 +139,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
   const uint32_t* sg_base = signs + bh * cap * WPR;
   const float* nm_base = norms + bh * cap;
   const uint16_t* v_base = values + bh * cap * D;
+  uint16_t* pbh = reinterpret_cast<uint16_t*>(pb_all) + wave * 2 * G * TILE;  // [2][G][TILE]
+  uint8_t* vbuf = vb_all + wave * VBUF;
 
-  // ---- first tile's loads go out before the prologue ----
   uint4 vc[VCH];
   uint4 sc[SV];
-  float nc;
-  auto load_tile = [&](int t0, uint4* vv, uint4* ss, float& nn) {
+  float nc = 0.f;
+  auto load_signs = [&](int t0, uint4* ss, float& nn) {
     const int ts = t0 + lane;
     if (ts < t_end) {
       const uint4* p = reinterpret_cast<const uint4*>(sg_base + static_cast<int64_t>(ts) * WPR);
@@ -124,24 +157,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
       for (int k = 0; k < SV; ++k) ss[k] = make_uint4(0, 0, 0, 0);
       nn = 0.f;
     }
+  };
+  // value chunk c of a tile: token t0 + 4c + lane/16, channels 8*(lane%16) .. +7
+  auto load_values = [&](int t0, int c_begin) {
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
+    for (int c = c_begin; c < c_begin + VCH / 2; ++c) {
       const int tv = t0 + 4 * c + (lane >> 4);
-      vv[c] = tv < t_end
+      vc[c] = tv < t_end
                   ? reinterpret_cast<const uint4*>(v_base + static_cast<int64_t>(tv) * D)[lane & 15]
                   : make_uint4(0, 0, 0, 0);
     }
   };
   int t0 = t_begin + wave * TILE;
 
-  // ---- prologue: q -> LDS, S^T q on the matrix cores, nibble table ----
-  // q is split into three bf16 parts (hi + mid + lo reproduces fp32 q to
-  // within 2^-24 relative); column 3*... of the B operand holds part p of head
-  // g at column p*G + g, so one 32x32x16 MFMA chain per block of 32 sketch
-  // coordinates yields all parts of all heads, with fp32 accumulation.
+  // ---- prologue ----
+  // S^T fragments and q are requested before the first tile, so waiting for q
+  // (memory counters drain in order) leaves the tile in flight.
   constexpr int NBLK = M / 32;            // blocks of 32 sketch coordinates
   constexpr int BPW = NBLK / NW;          // blocks per wave (2 or 4)
-  constexpr int BATCH = 2;                // blocks whose S^T fragments are in flight together
+  constexpr int BATCH = 2;
   static_assert(BPW % BATCH == 0, "blocks per wave must be a multiple of the batch");
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -156,46 +190,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
     }
   };
   load_frags(0);
-
-  // Issue order matters: the S^T fragments and q are loaded before the first
-  // tile, so waiting for q (memory counters drain in order) does not also
-  // wait for the tile, which stays in flight through the whole prologue.
-  const float* qb = q + (static_cast<int64_t>(b) * H_kv + kvh) * G * D;
+  const float* qb = q + bh * G * D;
   constexpr int QPT = (G * D + NT - 1) / NT;
   float qv[QPT];
 #pragma unroll
   for (int k = 0; k < QPT; ++k) qv[k] = (tid + k * NT < G * D) ? qb[tid + k * NT] : 0.f;
-  if (t0 < t_end) load_tile(t0, vc, sc, nc);
+  if (t0 < t_end) {
+    load_signs(t0, sc, nc);
+    load_values(t0, 0);
+    load_values(t0, VCH / 2);
+  }
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int i = tid + k * NT;
-    if (i < G * D) qs[i / D][i % D] = qv[k];
+    if (i < G * D) qs[i] = qv[k];
+  }
+  __syncthreads();
+  // q -> three bf16 parts (hi + mid + lo equals fp32 q to within 2^-24
+  // relative), laid out as the MFMA B operand: column c = part * G + head.
+  for (int e = tid; e < 8 * 2 * 32; e += NT) {
+    const int st = e >> 6, hf = (e >> 5) & 1, c = e & 31;
+    const int part = c / G, g = c % G;
+    uint32_t pk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t h2[2];
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const float x = part < 3 ? qs[g * D + 16 * st + 8 * hf + 2 * u + v] : 0.f;
+        const uint32_t hi = f32_to_bf16_rne(x);
+        const float r1 = x - __uint_as_float(hi << 16);
+        const uint32_t mid = f32_to_bf16_rne(r1);
+        const float r2 = r1 - __uint_as_float(mid << 16);
+        const uint32_t lo = f32_to_bf16_rne(r2);
+        h2[v] = part == 0 ? hi : (part == 1 ? mid : lo);
+      }
+      pk[u] = h2[0] | (h2[1] << 16);
+    }
+    qfrag[e] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   }
   __syncthreads();
   {
-    const int part = col / G;
-    const int g = col % G;
-    bf16x8_t bq[8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        uint32_t h2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float x = part < 3 ? qs[g][16 * st + 8 * half + e + u] : 0.f;
-          const uint32_t hi = f32_to_bf16_rne(x);
-          const float r1 = x - __uint_as_float(hi << 16);
-          const uint32_t mid = f32_to_bf16_rne(r1);
-          const float r2 = r1 - __uint_as_float(mid << 16);
-          const uint32_t lo = f32_to_bf16_rne(r2);
-          h2[u] = part == 0 ? hi : (part == 1 ? mid : lo);
-        }
-        pk[e / 2] = h2[0] | (h2[1] << 16);
-      }
-      bq[st] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    }
 #pragma unroll
     for (int batch = 0; batch < BPW / BATCH; ++batch) {
       if (batch > 0) load_frags(batch);
@@ -205,12 +240,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
         f32x16_t acc = {};
 #pragma unroll
         for (int st = 0; st < 8; ++st)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[bb][st]), bq[st], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[bb][st]),
+                                                        __builtin_bit_cast(bf16x8_t, qfrag[(st * 2 + half) * 32 + col]),
+                                                        acc, 0, 0, 0);
         // lane (col, half), register r -> coordinate 32*blk + 8*(r/4) + 4*half + r%4
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float v = acc[r] + __shfl(acc[r], lane + G) + __shfl(acc[r], lane + 2 * G);
-          if (col < G) sq[col][32 * blk + 8 * (r >> 2) + 4 * half + (r & 3)] = v;
+          if (col < G) sq[col * M + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3)] = v;
         }
       }
     }
@@ -223,7 +260,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
       float sacc = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float x = sq[g][4 * p + k];
+        const float x = sq[g * M + 4 * p + k];
         sacc += ((v >> k) & 1) ? x : -x;
       }
       lut[e * G + g] = sacc;
@@ -232,21 +269,39 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
   __syncthreads();
 
   // ---- main loop ----
-  float m_run[G], l_run[G], acc[G][8];
+  float m_run[G], l_run[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m_run[g] = -INFINITY;
     l_run[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
+  f32x4_t acc[NDB];
+#pragma unroll
+  for (int nb = 0; nb < NDB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // P operand rows: row = part * G + head for row < 2G (lane & 15 = row)
+  const int prow = lane & 15;
+  const int ppart = prow / G, phead = prow % G;
+  const bool prow_live = prow < 2 * G;
+  const int kgrp = lane >> 4;       // MFMA k group: tokens 8*kgrp .. +7 of the step
+  int row_head[4];                  // head of accumulator row 4*kgrp + r, or -1
+#pragma unroll
+  for (int r = 0; r < 4; ++r) row_head[r] = (4 * kgrp + r < 2 * G) ? (4 * kgrp + r) % G : -1;
+  // transposed-read source: lane s of a 16-lane group addresses token
+  // 8*kgrp + s/4 (+4 for the second read), columns 4*(s%4) .. +3 of the block
+  const int tr_tok = 8 * kgrp + ((lane & 15) >> 2);
+  const uint8_t* tr_base0 = vbuf + vrow(tr_tok) * VROW + 8 * (lane & 3);
+  const uint8_t* tr_base1 = vbuf + vrow(tr_tok + 4) * VROW + 8 * (lane & 3);
 
+  // Only one tile of values lives in registers: each half is reloaded with
+  // the next tile's rows as soon as it has been copied into LDS.  Sign words
+  // and norms of the next tile are requested first, so waiting for them does
+  // not wait for the values.
   while (t0 < t_end) {
     const int t_next = t0 + NW * TILE;
-    uint4 vn[VCH];
+    const bool has_next = t_next < t_end;
     uint4 sn[SV];
     float nn = 0.f;
-    if (t_next < t_end) load_tile(t_next, vn, sn, nn);
+    if (has_next) load_signs(t_next, sn, nn);
 
     // scores: lane <-> token t0 + lane
     float sc_g[G];
@@ -266,10 +321,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
 #pragma unroll
           for (int g = 0; g < G; ++g) sc_g[g] += t.v[g];
         }
+        // keep at most one word's table reads in flight (register pressure)
+        __asm__ __volatile__("" ::: "memory");
       }
     }
     const bool valid = (t0 + lane) < t_end;
-    VecG<G> pw;
+    float alpha_g[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float logit = valid ? sc_g[g] * (coef * nc) : -INFINITY;
@@ -279,54 +336,86 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
       const float p = valid ? exp2f(logit - m_new) : 0.f;
       l_run[g] = l_run[g] * alpha + p;
       m_run[g] = m_new;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
-      pw.v[g] = p;
+      // P as bf16 hi + lo (about 16 significant bits)
+      const uint32_t hi = f32_to_bf16_rne(p);
+      const uint32_t lo = f32_to_bf16_rne(p - __uint_as_float(hi << 16));
+      pbh[g * TILE + lane] = static_cast<uint16_t>(hi);
+      pbh[(G + g) * TILE + lane] = static_cast<uint16_t>(lo);
+      alpha_g[g] = alpha;
     }
-    *reinterpret_cast<VecG<G>*>(&pbuf[wave][lane][0]) = pw;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // rescale the running output: register r of this lane holds row
+    // 4*kgrp + r, i.e. head row_head[r] (rows >= 2G are unused)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float a = 1.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) a = (row_head[r] == g) ? alpha_g[g] : a;
+#pragma unroll
+      for (int nb = 0; nb < NDB; ++nb) acc[nb][r] *= a;
+    }
 
-    // p * v: lane <-> (token 4c + lane/16, channels 8*(lane%16) .. +7)
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const VecG<G> pt = *reinterpret_cast<const VecG<G>*>(&pbuf[wave][4 * c + (lane >> 4)][0]);
-      const float v8[8] = {bf16lo(vc[c].x), bf16hi(vc[c].x), bf16lo(vc[c].y), bf16hi(vc[c].y),
-                           bf16lo(vc[c].z), bf16hi(vc[c].z), bf16lo(vc[c].w), bf16hi(vc[c].w)};
+    for (int hstep = 0; hstep < 2; ++hstep) {
+      // value rows 32*hstep .. +31 of the tile -> wave-private LDS tile
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = __builtin_fmaf(pt.v[g], v8[e], acc[g][e]);
+      for (int u = 0; u < 8; ++u) {
+        // token 4u + lane/16 of the half tile; vrow() only permutes the
+        // groups of 4 rows, so the lane part stays a per-lane base
+        const int row = vrow(4 * u) + (lane >> 4);
+        *reinterpret_cast<uint4*>(vbuf + row * VROW + (lane & 15) * 16) = vc[8 * hstep + u];
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (has_next) load_values(t_next, 8 * hstep);
+      // A operand: P rows, tokens 32*hstep + 8*kgrp .. +7
+      uint4 pa = make_uint4(0, 0, 0, 0);
+      if (prow_live)
+        pa = *reinterpret_cast<const uint4*>(pbh + (ppart * G + phead) * TILE + HALF * hstep + 8 * kgrp);
+      const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, pa);
+#pragma unroll
+      for (int nb = 0; nb < NDB; ++nb) {
+        const uint8_t* p0 = tr_base0 + 32 * nb;
+        const uint8_t* p1 = tr_base1 + 32 * nb;
+        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(p0));
+        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(p1));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo4);
+        const uint2 h2 = __builtin_bit_cast(uint2, hi4);
+        const uint4 bv = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, __builtin_bit_cast(bf16x8_t, bv), acc[nb], 0, 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_wave_barrier();
 
     t0 = t_next;
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) vc[c] = vn[c];
 #pragma unroll
     for (int k = 0; k < SV; ++k) sc[k] = sn[k];
     nc = nn;
   }
 
-  // ---- merge within the wave, then across waves ----
+  // ---- wave result: out row = hi row + lo row, into this wave's LDS tile ----
+  // Accumulator block nb: lane l holds row 4*(l/16) + r, column l%16.  Row g
+  // (hi part of head g) pairs with row G + g (lo part): for G >= 4 the lo row
+  // sits G/4 lane groups later in the same register; for G < 4 both rows are
+  // registers of lanes 0..15.
+  float* wacc = reinterpret_cast<float*>(vbuf);   // [G][D]
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l_run[g] = wave_sum(l_run[g]);
+  for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = acc[g][e];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[g][e] = x;
-    }
-  }
-  if (lane < 16) {
+  for (int nb = 0; nb < NDB; ++nb) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red_buf[(wave * G + g) * D + 8 * lane + e] = acc[g][e];
+    for (int r = 0; r < 4; ++r) {
+      if (G >= 4) {
+        const float v = acc[nb][r] + __shfl(acc[nb][r], (lane + 16 * (G / 4)) & 63);
+        const int row = 4 * kgrp + r;
+        if (row < G) wacc[row * D + 16 * nb + (lane & 15)] = v;
+      } else if (r < G) {
+        if (kgrp == 0) wacc[r * D + 16 * nb + (lane & 15)] = acc[nb][r] + acc[nb][(r + G) & 3];
+      }
     }
   }
   if (lane == 0) {
@@ -344,16 +433,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_ml[w][g][0]);
-    float L = 0.f, A = 0.f;
+    float Ls = 0.f, A = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float mw = red_ml[w][g][0];
       const float f = mw == -INFINITY ? 0.f : exp2f(mw - mx);
-      L += red_ml[w][g][1] * f;
-      A += red_buf[(w * G + g) * D + dd] * f;
+      Ls += red_ml[w][g][1] * f;
+      A += reinterpret_cast<const float*>(vb_all + w * VBUF)[g * D + dd] * f;
     }
     if (n_split == 1) {
-      out[(bh * G + g) * D + dd] = A / L;
+      out[(bh * G + g) * D + dd] = A / Ls;
     } else {
       // coherent (sc1) stores: visible to every XCD once complete, with no
       // L2-wide write-back (an agent-scope fence would flush the whole L2)
@@ -362,7 +451,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
       if (dd == 0) {
         __hip_atomic_store(&part_ml[(slot0 * G + g) * 2 + 0], mx, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&part_ml[(slot0 * G + g) * 2 + 1], L, __ATOMIC_RELAXED,
+        __hip_atomic_store(&part_ml[(slot0 * G + g) * 2 + 1], Ls, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -389,7 +478,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
   // (1) all (max, sum) pairs into LDS in one round of loads
   float* ml_l = lut;                      // 2 * n_split * G floats
   float* wts = lut + 2 * MAX_SPLITS * G;  // n_split * G floats
-  static_assert(3 * MAX_SPLITS * G <= LUT_FLOATS, "merge scratch exceeds the table");
+  static_assert(3 * MAX_SPLITS * G <= L::LUT_FLOATS, "merge scratch exceeds the table");
   {
     const float2* src = reinterpret_cast<const float2*>(part_ml + bh * n_split * G * 2);
     for (int i = tid; i < n_split * G; i += NT) reinterpret_cast<float2*>(ml_l)[i] = src[i];
@@ -401,12 +490,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
     float mx = -INFINITY;
     for (int s = lane; s < n_split; s += 64) mx = fmaxf(mx, ml_l[(s * G + g) * 2]);
     mx = wave_max(mx);
-    float L = 0.f;
-    for (int s = lane; s < n_split; s += 64) L += ml_l[(s * G + g) * 2 + 1] * exp2f(ml_l[(s * G + g) * 2] - mx);
-    L = wave_sum(L);
+    float Ls = 0.f;
+    for (int s = lane; s < n_split; s += 64) Ls += ml_l[(s * G + g) * 2 + 1] * exp2f(ml_l[(s * G + g) * 2] - mx);
+    Ls = wave_sum(Ls);
     if (lane == 0) {
       gmax[g] = mx;
-      gsum[g] = L;
+      gsum[g] = Ls;
     }
   }
   __syncthreads();
@@ -418,8 +507,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 :
   {
     constexpr int PAIRS = G * D / 4;
     constexpr int REP = PAIRS >= NT ? 1 : NT / PAIRS;
-    static_assert(REP == 1 || REP * PAIRS * 4 <= RED_FLOATS, "merge replicas exceed the LDS buffer");
-    float4* rbuf = reinterpret_cast<float4*>(red_buf);
+    static_assert(REP == 1 || REP * PAIRS * 16 <= L::VB_BYTES, "merge replicas exceed the LDS buffer");
+    float4* rbuf = reinterpret_cast<float4*>(vb_all);
     const float4* pa = reinterpret_cast<const float4*>(part_acc);
     for (int i = tid; i < PAIRS * REP; i += NT) {
       const int pr = i % PAIRS, rep = i / PAIRS;
