@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -58,20 +59,53 @@ typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global load as a native vector (a struct copy would become a
+// memcpy that keeps the destination array out of registers)
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Cross-lane moves through DPP (VALU, no LDS round trip).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;    // lane 15 of each row -> next row
+constexpr int kRowBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+constexpr int kRowShl = 0x100;        // + n: lane l reads lane l + n of its row
+
+// Reductions over the 64 lanes: quad, half-row, row, then two row
+// broadcasts leave the total in lane 63, which is read back as a uniform.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  x = fmaxf(x, dpp<kRowBcast15, 0xA>(x));
+  x = fmaxf(x, dpp<kRowBcast31, 0xC>(x));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  x += dpp<kRowBcast15, 0xA>(x);
+  x += dpp<kRowBcast31, 0xC>(x);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // LDS row of token t (0..31) of a half tile.  A transposed read by 32 lanes
@@ -107,7 +141,7 @@ template <int M, int G>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     const float* __restrict__ q, const uint32_t* __restrict__ signs,
     const float* __restrict__ norms, const uint16_t* __restrict__ values,
-    const uint16_t* __restrict__ s_md, int H_kv, int N, int cap, int n_split, int tps,
+    const uint16_t* __restrict__ s_frag, int H_kv, int N, int cap, int n_split, int tps,
     float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
     float* __restrict__ part_acc, float* __restrict__ part_ml) {
   using L = DecodeLds<M, G>;
@@ -145,48 +179,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   uint4 vc[VCH];
   uint4 sc[SV];
   float nc = 0.f;
+  // Tile loads are branch-free: rows past the end of the split are clamped to
+  // its last row (masked later: logit -inf, probability 0).  Branches around
+  // loads would make the compiler's memory-counter waits conservative (a full
+  // drain), which would serialize the prologue behind the tile prefetch.
   auto load_signs = [&](int t0, uint4* ss, float& nn) {
-    const int ts = t0 + lane;
-    if (ts < t_end) {
-      const uint4* p = reinterpret_cast<const uint4*>(sg_base + static_cast<int64_t>(ts) * WPR);
+    const int ts = min(t0 + lane, t_end - 1);
+    const uint4* p = reinterpret_cast<const uint4*>(sg_base + static_cast<int64_t>(ts) * WPR);
 #pragma unroll
-      for (int k = 0; k < SV; ++k) ss[k] = p[k];
-      nn = nm_base[ts];
-    } else {
-#pragma unroll
-      for (int k = 0; k < SV; ++k) ss[k] = make_uint4(0, 0, 0, 0);
-      nn = 0.f;
-    }
+    for (int k = 0; k < SV; ++k) ss[k] = ld16(p + k);
+    nn = nm_base[ts];
   };
   // value chunk c of a tile: token t0 + 4c + lane/16, channels 8*(lane%16) .. +7
-  auto load_values = [&](int t0, int c_begin) {
+  auto load_values = [&](int t0, auto half_const) {
+    constexpr int c_begin = decltype(half_const)::value * (VCH / 2);
 #pragma unroll
-    for (int c = c_begin; c < c_begin + VCH / 2; ++c) {
-      const int tv = t0 + 4 * c + (lane >> 4);
-      vc[c] = tv < t_end
-                  ? reinterpret_cast<const uint4*>(v_base + static_cast<int64_t>(tv) * D)[lane & 15]
-                  : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < VCH / 2; ++u) {
+      const int tv = min(t0 + 4 * (c_begin + u) + (lane >> 4), t_end - 1);
+      vc[c_begin + u] = ld16(reinterpret_cast<const uint4*>(v_base + static_cast<int64_t>(tv) * D) + (lane & 15));
     }
   };
   int t0 = t_begin + wave * TILE;
 
   // ---- prologue ----
-  // S^T fragments and q are requested before the first tile, so waiting for q
-  // (memory counters drain in order) leaves the tile in flight.
+  // S^T fragments and q are requested first; memory counters drain in
+  // order, so waiting for q leaves the later tile loads in flight.
   constexpr int NBLK = M / 32;            // blocks of 32 sketch coordinates
   constexpr int BPW = NBLK / NW;          // blocks per wave (2 or 4)
-  constexpr int BATCH = 2;
+  constexpr int BATCH = BPW;             // all fragments go out before the tile loads
   static_assert(BPW % BATCH == 0, "blocks per wave must be a multiple of the batch");
   const int col = lane & 31;
   const int half = lane >> 5;
+  // S^T comes in fragment order (see DeviceSketch::s_frag): the operand of
+  // (block, k-step) is 64 lanes x 16 contiguous bytes, one 1 KB load.
   uint4 af[BATCH][8];
   auto load_frags = [&](int batch) {
 #pragma unroll
     for (int bb = 0; bb < BATCH; ++bb) {
       const int blk = wave + NW * (batch * BATCH + bb);
-      const uint4* arow = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(32 * blk + col) * D);
+      const uint4* fr = reinterpret_cast<const uint4*>(s_frag) + static_cast<int64_t>(blk) * 8 * 64 + lane;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) af[bb][st] = arow[2 * st + half];
+      for (int st = 0; st < 8; ++st) af[bb][st] = fr[st * 64];
     }
   };
   load_frags(0);
@@ -195,11 +228,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   float qv[QPT];
 #pragma unroll
   for (int k = 0; k < QPT; ++k) qv[k] = (tid + k * NT < G * D) ? qb[tid + k * NT] : 0.f;
-  if (t0 < t_end) {
-    load_signs(t0, sc, nc);
-    load_values(t0, 0);
-    load_values(t0, VCH / 2);
-  }
+  load_signs(t0, sc, nc);
+  load_values(t0, std::integral_constant<int, 0>{});
+  load_values(t0, std::integral_constant<int, 1>{});
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int i = tid + k * NT;
@@ -246,25 +277,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
         // lane (col, half), register r -> coordinate 32*blk + 8*(r/4) + 4*half + r%4
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float v = acc[r] + __shfl(acc[r], lane + G) + __shfl(acc[r], lane + 2 * G);
+          float v;
+          if (G < 8) {   // columns col + G and col + 2G lie in the same 16-lane row
+            v = acc[r] + dpp<kRowShl + G>(acc[r]) + dpp<kRowShl + 2 * G>(acc[r]);
+          } else {
+            v = acc[r] + __shfl(acc[r], lane + G) + __shfl(acc[r], lane + 2 * G);
+          }
           if (col < G) sq[col * M + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3)] = v;
         }
       }
     }
   }
   __syncthreads();
-  for (int e = tid; e < NPOS * 16; e += NT) {
-    const int p = e >> 4, v = e & 15;
+  // entry v of group p: sum_k (bit k of v ? +1 : -1) * sq[4p + k]
+  //   = base + 2 * sum_{k in v} sq[4p + k],  base = -sum_k sq[4p + k]
+  for (int e = tid; e < NPOS * G; e += NT) {
+    const int p = e / G, g = e % G;
+    const float4 x = *reinterpret_cast<const float4*>(&sq[g * M + 4 * p]);
+    float t[16];
+    t[0] = -(x.x + x.y + x.z + x.w);
+    t[1] = t[0] + 2.f * x.x;
+    t[2] = t[0] + 2.f * x.y;
+    t[3] = t[1] + 2.f * x.y;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float sacc = 0.f;
+    for (int v = 4; v < 8; ++v) t[v] = t[v - 4] + 2.f * x.z;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x = sq[g * M + 4 * p + k];
-        sacc += ((v >> k) & 1) ? x : -x;
-      }
-      lut[e * G + g] = sacc;
-    }
+    for (int v = 8; v < 16; ++v) t[v] = t[v - 8] + 2.f * x.w;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) lut[(p * 16 + v) * G + g] = t[v];
   }
   __syncthreads();
 
@@ -298,10 +338,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   // not wait for the values.
   while (t0 < t_end) {
     const int t_next = t0 + NW * TILE;
-    const bool has_next = t_next < t_end;
     uint4 sn[SV];
-    float nn = 0.f;
-    if (has_next) load_signs(t_next, sn, nn);
+    float nn;
+    load_signs(t_next, sn, nn);
 
     // scores: lane <-> token t0 + lane
     float sc_g[G];
@@ -354,8 +393,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int nb = 0; nb < NDB; ++nb) acc[nb][r] *= a;
     }
 
-#pragma unroll
-    for (int hstep = 0; hstep < 2; ++hstep) {
+    // P.V for rows 32*HS .. +31 of the tile (HS = 0, 1 as constants, so the
+    // value registers are addressed statically)
+    auto pv_half = [&](auto hs_const) {
+      constexpr int hstep = decltype(hs_const)::value;
       // value rows 32*hstep .. +31 of the tile -> wave-private LDS tile
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -367,7 +408,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (has_next) load_values(t_next, 8 * hstep);
+      load_values(t_next, hs_const);
       // A operand: P rows, tokens 32*hstep + 8*kgrp .. +7
       uint4 pa = make_uint4(0, 0, 0, 0);
       if (prow_live)
@@ -389,7 +430,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    };
+    pv_half(std::integral_constant<int, 0>{});
+    pv_half(std::integral_constant<int, 1>{});
 
     t0 = t_next;
 #pragma unroll
@@ -475,16 +518,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   // plain (vector) loads see the partials the other workgroups stored
   // coherently.  Only the last workgroup of each (batch, kv head) pays it.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // (1) all (max, sum) pairs into LDS in one round of loads
+  // Threads own (head, 4 channels) pairs; with fewer pairs than threads the
+  // splits are divided among REP replicas whose sums meet in LDS.  The
+  // (max, sum) pairs and the first MCH partial accumulators of every thread
+  // are requested together, so the merge costs one round trip to memory.
+  constexpr int PAIRS = G * D / 4;
+  constexpr int REP = PAIRS >= NT ? 1 : NT / PAIRS;
+  constexpr int MCH = 32;                 // float4 loads in flight per thread
+  static_assert(REP == 1 || REP * PAIRS * 16 <= L::VB_BYTES, "merge replicas exceed the LDS buffer");
   float* ml_l = lut;                      // 2 * n_split * G floats
   float* wts = lut + 2 * MAX_SPLITS * G;  // n_split * G floats
   static_assert(3 * MAX_SPLITS * G <= L::LUT_FLOATS, "merge scratch exceeds the table");
-  {
-    const float2* src = reinterpret_cast<const float2*>(part_ml + bh * n_split * G * 2);
-    for (int i = tid; i < n_split * G; i += NT) reinterpret_cast<float2*>(ml_l)[i] = src[i];
+  const float2* ml_src = reinterpret_cast<const float2*>(part_ml + bh * n_split * G * 2);
+  const float4* pa = reinterpret_cast<const float4*>(part_acc);
+  constexpr int ML_PT = (MAX_SPLITS * G + NT - 1) / NT;
+  float2 mlv[ML_PT];
+#pragma unroll
+  for (int k = 0; k < ML_PT; ++k) {
+    const int i = tid + k * NT;
+    if (i < n_split * G) mlv[k] = ml_src[i];
+  }
+  const int pr = tid % PAIRS, rep = tid / PAIRS;       // valid when tid < PAIRS * REP
+  const int mg = pr / (D / 4), c4 = pr % (D / 4);
+  float4 av[MCH];
+#pragma unroll
+  for (int u = 0; u < MCH; ++u) {
+    const int s = rep + u * REP;
+    if (tid < PAIRS * REP && s < n_split) av[u] = pa[((bh * n_split + s) * G + mg) * (D / 4) + c4];
+  }
+#pragma unroll
+  for (int k = 0; k < ML_PT; ++k) {
+    const int i = tid + k * NT;
+    if (i < n_split * G) reinterpret_cast<float2*>(ml_l)[i] = mlv[k];
   }
   __syncthreads();
-  // (2) per head: global max and normalizer, then per-split weights
+  // per head: global max and normalizer, then per-split weights
   __shared__ float gmax[G], gsum[G];
   for (int g = wave; g < G; g += NW) {
     float mx = -INFINITY;
@@ -501,61 +569,46 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   __syncthreads();
   for (int i = tid; i < n_split * G; i += NT) wts[i] = exp2f(ml_l[2 * i] - gmax[i % G]) / gsum[i % G];
   __syncthreads();
-  // (3) weighted sum of the partial accumulators.  Threads own (head, 4
-  // channels) pairs; with fewer pairs than threads the splits are divided
-  // among REP replicas whose sums meet in LDS.  Loads go out 8 at a time.
-  {
-    constexpr int PAIRS = G * D / 4;
-    constexpr int REP = PAIRS >= NT ? 1 : NT / PAIRS;
-    static_assert(REP == 1 || REP * PAIRS * 16 <= L::VB_BYTES, "merge replicas exceed the LDS buffer");
-    float4* rbuf = reinterpret_cast<float4*>(vb_all);
-    const float4* pa = reinterpret_cast<const float4*>(part_acc);
-    for (int i = tid; i < PAIRS * REP; i += NT) {
-      const int pr = i % PAIRS, rep = i / PAIRS;
-      const int g = pr / (D / 4), c4 = pr % (D / 4);
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      int s = rep;
-      for (; s + 7 * REP < n_split; s += 8 * REP) {
-        float4 v[8];
+  if (tid < PAIRS * REP) {
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = pa[((bh * n_split + s + u * REP) * G + g) * (D / 4) + c4];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float wgt = wts[(s + u * REP) * G + g];
-          o.x = __builtin_fmaf(wgt, v[u].x, o.x);
-          o.y = __builtin_fmaf(wgt, v[u].y, o.y);
-          o.z = __builtin_fmaf(wgt, v[u].z, o.z);
-          o.w = __builtin_fmaf(wgt, v[u].w, o.w);
-        }
-      }
-      for (; s < n_split; s += REP) {
-        const float4 v = pa[((bh * n_split + s) * G + g) * (D / 4) + c4];
-        const float wgt = wts[s * G + g];
-        o.x = __builtin_fmaf(wgt, v.x, o.x);
-        o.y = __builtin_fmaf(wgt, v.y, o.y);
-        o.z = __builtin_fmaf(wgt, v.z, o.z);
-        o.w = __builtin_fmaf(wgt, v.w, o.w);
-      }
-      if (REP == 1) {
-        reinterpret_cast<float4*>(out)[(bh * G + g) * (D / 4) + c4] = o;
-      } else {
-        rbuf[rep * PAIRS + pr] = o;
+    for (int u = 0; u < MCH; ++u) {
+      const int s = rep + u * REP;
+      if (s < n_split) {
+        const float wgt = wts[s * G + mg];
+        o.x = __builtin_fmaf(wgt, av[u].x, o.x);
+        o.y = __builtin_fmaf(wgt, av[u].y, o.y);
+        o.z = __builtin_fmaf(wgt, av[u].z, o.z);
+        o.w = __builtin_fmaf(wgt, av[u].w, o.w);
       }
     }
-    if (REP > 1) {
-      __syncthreads();
-      for (int pr = tid; pr < PAIRS; pr += NT) {
-        float4 o = rbuf[pr];
-        for (int rep = 1; rep < REP; ++rep) {
-          const float4 v = rbuf[rep * PAIRS + pr];
-          o.x += v.x;
-          o.y += v.y;
-          o.z += v.z;
-          o.w += v.w;
-        }
-        const int g = pr / (D / 4), c4 = pr % (D / 4);
-        reinterpret_cast<float4*>(out)[(bh * G + g) * (D / 4) + c4] = o;
+    for (int s = rep + MCH * REP; s < n_split; s += REP) {   // splits beyond the first batch
+      const float4 v = pa[((bh * n_split + s) * G + mg) * (D / 4) + c4];
+      const float wgt = wts[s * G + mg];
+      o.x = __builtin_fmaf(wgt, v.x, o.x);
+      o.y = __builtin_fmaf(wgt, v.y, o.y);
+      o.z = __builtin_fmaf(wgt, v.z, o.z);
+      o.w = __builtin_fmaf(wgt, v.w, o.w);
+    }
+    if (REP == 1) {
+      reinterpret_cast<float4*>(out)[(bh * G + mg) * (D / 4) + c4] = o;
+    } else {
+      reinterpret_cast<float4*>(vb_all)[rep * PAIRS + pr] = o;
+    }
+  }
+  if (REP > 1) {
+    __syncthreads();
+    for (int p2 = tid; p2 < PAIRS; p2 += NT) {
+      float4 o = reinterpret_cast<const float4*>(vb_all)[p2];
+      for (int r2 = 1; r2 < REP; ++r2) {
+        const float4 v = reinterpret_cast<const float4*>(vb_all)[r2 * PAIRS + p2];
+        o.x += v.x;
+        o.y += v.y;
+        o.z += v.z;
+        o.w += v.w;
       }
+      const int g = p2 / (D / 4), cc = p2 % (D / 4);
+      reinterpret_cast<float4*>(out)[(bh * G + g) * (D / 4) + cc] = o;
     }
   }
   if (tid == 0) __hip_atomic_store(&counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -572,7 +625,7 @@ int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float*
   float* part_ml = part_acc + static_cast<size_t>(B) * H_kv * G * plan.n_split * D;
   dim3 grid(plan.n_split, H_kv, B);
   hipLaunchKernelGGL((decode_kernel<M, G>), grid, dim3(NT), 0, stream, q, signs, norms,
-                     static_cast<const uint16_t*>(values), s.s_md, H_kv, N, cap, plan.n_split,
+                     static_cast<const uint16_t*>(values), s.s_frag, H_kv, N, cap, plan.n_split,
                      plan.tokens_per_split, coef, out, counters, part_acc, part_ml);
   return hipGetLastError();
 }

@@ -16,6 +16,10 @@ void generate_sketch_bf16(uint64_t seed, int d, int m, uint16_t* out);
 struct DeviceSketch {
   const uint16_t* s_dm = nullptr;   // [d][m]  bf16 bits (decode: S^T q)
   const uint16_t* s_md = nullptr;   // [m][d]  bf16 bits (encode: matrix-core A operand)
+  // S^T in the lane order of the A operand of v_mfma_f32_32x32x16_bf16:
+  // [m/32 blocks][8 k-steps][64 lanes][8 bf16], lane l holding
+  // S^T[32*block + l%32][16*kstep + 8*(l/32) .. +7] (decode: S^T q)
+  const uint16_t* s_frag = nullptr;
   const float* col_norm_max = nullptr;  // [m/64] max_{i in group} ||S[:, i]||_2, rounded up
   int d = 0;
   int m = 0;

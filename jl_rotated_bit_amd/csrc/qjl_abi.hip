@@ -78,9 +78,18 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
     }
     cmax[g] = std::nextafter(static_cast<float>(best), INFINITY);
   }
+  std::vector<uint16_t> s_frag(n);
+  for (int blk = 0; blk < m / 32; ++blk)
+    for (int st = 0; st < d / 16; ++st)
+      for (int l = 0; l < 64; ++l)
+        for (int e = 0; e < 8; ++e)
+          s_frag[((static_cast<size_t>(blk) * (d / 16) + st) * 64 + l) * 8 + e] =
+              s_md[static_cast<size_t>(32 * blk + l % 32) * d + 16 * st + 8 * (l / 32) + e];
   const size_t bytes_s = n * sizeof(uint16_t);
-  const size_t off_md = (bytes_s + 255) / 256 * 256;
-  const size_t off_cm = off_md + (bytes_s + 255) / 256 * 256;
+  const size_t padded = (bytes_s + 255) / 256 * 256;
+  const size_t off_md = padded;
+  const size_t off_fr = off_md + padded;
+  const size_t off_cm = off_fr + padded;
   const size_t total = off_cm + cmax.size() * sizeof(float);
   void* mem = nullptr;
   e = hipMalloc(&mem, total);
@@ -88,6 +97,7 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
   auto* base = static_cast<uint8_t*>(mem);
   e = hipMemcpy(base, s_dm.data(), bytes_s, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + off_md, s_md.data(), bytes_s, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + off_fr, s_frag.data(), bytes_s, hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(base + off_cm, cmax.data(), cmax.size() * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
@@ -98,6 +108,7 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
   ce.mem = mem;
   ce.view.s_dm = reinterpret_cast<const uint16_t*>(base);
   ce.view.s_md = reinterpret_cast<const uint16_t*>(base + off_md);
+  ce.view.s_frag = reinterpret_cast<const uint16_t*>(base + off_fr);
   ce.view.col_norm_max = reinterpret_cast<const float*>(base + off_cm);
   ce.view.d = d;
   ce.view.m = m;
