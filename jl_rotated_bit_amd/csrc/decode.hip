@@ -202,8 +202,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   int t0 = t_begin + wave * TILE;
 
   // ---- prologue ----
-  // S^T fragments and q are requested first; memory counters drain in
-  // order, so waiting for q leaves the later tile loads in flight.
+  // q and the S^T fragments are requested first; memory counters drain in
+  // order, so waiting for them leaves the later tile loads in flight.
   constexpr int NBLK = M / 32;            // blocks of 32 sketch coordinates
   constexpr int BPW = NBLK / NW;          // blocks per wave (2 or 4)
   constexpr int BATCH = BPW;             // all fragments go out before the tile loads
@@ -222,12 +222,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int st = 0; st < 8; ++st) af[bb][st] = fr[st * 64];
     }
   };
-  load_frags(0);
   const float* qb = q + bh * G * D;
   constexpr int QPT = (G * D + NT - 1) / NT;
   float qv[QPT];
 #pragma unroll
   for (int k = 0; k < QPT; ++k) qv[k] = (tid + k * NT < G * D) ? qb[tid + k * NT] : 0.f;
+  // every wave has requested q before any wave requests S^T or its tile, so
+  // q is at the head of this compute unit's memory queue
+  __syncthreads();
+  load_frags(0);
   load_signs(t0, sc, nc);
   load_values(t0, std::integral_constant<int, 0>{});
   load_values(t0, std::integral_constant<int, 1>{});
