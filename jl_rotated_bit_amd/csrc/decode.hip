@@ -15,19 +15,22 @@
 // * Grid = (context split, kv head, batch).  A workgroup (4 waves) serves the
 //   G query heads of one kv head over one token range.
 // * Prologue: q is split once per workgroup into three bf16 parts; S^T q for
-//   the G heads then runs on the matrix cores (fp32 accumulation), and feeds
-//   an LDS table of the 16 signed sums of every group of 4 consecutive sketch
-//   coordinates, per head.  A token's bit dot product then costs m/4 table
-//   reads and adds per head instead of m masked adds.  The first token tile's
-//   loads are in flight during the whole prologue.
-// * Main loop, per wave and 64-token tile: lane t scores token t (its sign
-//   words and norm arrive with 16-byte loads) and does the online-softmax
-//   update; the probabilities, split into bf16 hi + lo parts, go to LDS.  The
-//   value rows (16-byte loads, 16 lanes per row) go to a wave-private,
-//   padded, row-permuted LDS tile, are read back transposed (ds_read_b64_tr_b16) as
-//   the B operand of v_mfma_f32_16x16x32_bf16, and P (rows = head x part) V
-//   accumulates on the matrix cores.  The next tile's loads are issued
-//   before the current tile is used.
+//   the G heads runs on the matrix cores (fp32 accumulation).  Each head's
+//   S^T q is then written as integers Q_i = round(Sq_i / 2^E) with |Q_i| <=
+//   2^21, where 2^(E+21) bounds ||s_i|| ||q|| (Cauchy-Schwarz), as three signed
+//   byte limbs (Q = a 2^16 + b 2^8 + c) in LDS.  The first token tile's loads
+//   are in flight during the whole prologue.
+// * Scores on the int8 matrix cores: per 16-token block, A = the tokens' sign
+//   bits spread to 0/1 bytes (rows = tokens), B = the limbs (columns = limb x
+//   head), so sum_i b_ti Q_i is exact in int32.  Limb columns are combined with
+//   shifts and row rotations (DPP), and est = (2 sum_i b_ti Q_i - sum_i Q_i)
+//   2^E.  Each lane then holds the scores of 16 tokens for one head.
+// * Online softmax per head in registers; the probabilities, split into bf16
+//   hi + lo parts, are already laid out as the A operand (rows = part x head,
+//   k = tokens) of v_mfma_f32_16x16x32_bf16.  The value rows (16-byte loads,
+//   16 lanes per row) go to a wave-private padded LDS tile and are read back
+//   transposed (ds_read_b64_tr_b16) as its B operand.  The next tile's loads
+//   are issued before the current tile is used.
 // * Epilogue: waves merge in LDS; the workgroup stores its partial
 //   (max, sum, acc) per head with coherent stores; the last workgroup of a
 //   (batch, kv head) to arrive (atomic counter) merges all splits by
@@ -44,33 +47,58 @@ namespace qjl {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int NW = 4;            // waves per workgroup
+#ifndef QJL_DECODE_WAVES
+#define QJL_DECODE_WAVES 4
+#endif
+constexpr int NW = QJL_DECODE_WAVES;   // waves per workgroup
 constexpr int NT = 64 * NW;
-constexpr int TILE = 64;         // tokens per wave per step
+constexpr int TILE = 64;         // tokens per wave per step (4 blocks of 16)
 constexpr int HALF = 32;         // tokens per P.V matrix step (MFMA K)
 constexpr int VCH = TILE * D * 2 / 16 / 64;  // 16-byte value chunks per lane per tile (16)
 constexpr int NDB = D / 16;      // 16-column blocks of the output (8)
 constexpr int VROW = D * 2 + 32; // bytes per value row in LDS (256 + 32 padding)
 constexpr int VBUF = HALF * VROW;            // wave-private value tile (9 KB)
 constexpr int MAX_SPLITS = 256;
+constexpr int QBITS = 21;        // |Q_i| <= 2^21
+constexpr int PROW = 32;         // bytes per token of probability rows (16 bf16: head x part)
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef int i32x4_t __attribute__((__vector_size__(4 * sizeof(int))));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// 16-byte global load as a native vector (a struct copy would become a
-// memcpy that keeps the destination array out of registers)
+// 16- and 8-byte global loads as native vectors (a struct copy would become
+// a memcpy that keeps the destination array out of registers)
 __device__ __forceinline__ uint4 ld16(const void* p) {
   const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint2 ld8(const void* p) {
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+  return make_uint2(v.x, v.y);
+}
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Buffer descriptor over [base, base + bytes): loads at offsets past the end
+// return zero, so the rows past a split's end need no clamping.  base and
+// bytes must be wave-uniform.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, no swizzle
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  // readfirstlane keeps the (uniform) size in a scalar register; a vector
+  // register there would make the compiler loop over lanes around each load
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+// two floats -> two bf16 (round to nearest even) in one register, low first
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Cross-lane moves through DPP (VALU, no LDS round trip).
@@ -79,90 +107,143 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(
       __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
 }
-constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-constexpr int kRowBcast15 = 0x142;    // lane 15 of each row -> next row
-constexpr int kRowBcast31 = 0x143;    // lane 31 -> rows 2 and 3
 constexpr int kRowShl = 0x100;        // + n: lane l reads lane l + n of its row
+constexpr int kRowRor = 0x120;        // + n: rotate within the row by n lanes
 
-// Reductions over the 64 lanes: quad, half-row, row, then two row
-// broadcasts leave the total in lane 63, which is read back as a uniform.
+// DPP move with every lane enabled and no old value, so the compiler can fold
+// it into the consuming VALU instruction.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// wave-uniform value kept in a scalar register
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Reductions over the 64 lanes: rotations within each 16-lane row, then a
+// 16-lane and a 32-lane row swap; the result is read back as a uniform.
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kQuadSwap1>(x));
-  x = fmaxf(x, dpp<kQuadSwap2>(x));
-  x = fmaxf(x, dpp<kRowHalfMirror>(x));
-  x = fmaxf(x, dpp<kRowMirror>(x));
-  x = fmaxf(x, dpp<kRowBcast15, 0xA>(x));
-  x = fmaxf(x, dpp<kRowBcast31, 0xC>(x));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  x = fmaxf(x, dpp_f<kRowRor + 8>(x));
+  x = fmaxf(x, dpp_f<kRowRor + 4>(x));
+  x = fmaxf(x, dpp_f<kRowRor + 2>(x));
+  x = fmaxf(x, dpp_f<kRowRor + 1>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  return uniform(x);
 }
 __device__ __forceinline__ float wave_sum(float x) {
-  x += dpp<kQuadSwap1>(x);
-  x += dpp<kQuadSwap2>(x);
-  x += dpp<kRowHalfMirror>(x);
-  x += dpp<kRowMirror>(x);
-  x += dpp<kRowBcast15, 0xA>(x);
-  x += dpp<kRowBcast31, 0xC>(x);
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  x += dpp_f<kRowRor + 8>(x);
+  x += dpp_f<kRowRor + 4>(x);
+  x += dpp_f<kRowRor + 2>(x);
+  x += dpp_f<kRowRor + 1>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  return uniform(x);
 }
 
-// LDS row of token t (0..31) of a half tile.  A transposed read by 32 lanes
-// touches tokens {0..3, 8..11} (+4, +16 variants); with 288-byte rows, row r
-// starts on bank 8*(r mod 8), so swapping rows 8..11 with 12..15 (and 24..27
-// with 28..31) puts those 8 tokens on 8 distinct bank groups.  Every column
-// offset stays an immediate.
-__device__ __forceinline__ constexpr int vrow(int t) { return t ^ ((t & 8) >> 1); }
-
-// G floats read or written as one LDS access (b32 / b64 / b128; two b128 for G = 8).
+// Sum over the four 16-lane groups of x_j, leaving the total of x_g in
+// group g: two 16-lane and one 32-lane row swaps (VALU, no LDS).
+// max over each 16-lane row (result in every lane of the row)
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_f<kRowRor + 8>(x));
+  x = fmaxf(x, dpp_f<kRowRor + 4>(x));
+  x = fmaxf(x, dpp_f<kRowRor + 2>(x));
+  return fmaxf(x, dpp_f<kRowRor + 1>(x));
+}
+__device__ __forceinline__ float fmax_swap16(float a, float b) {   // [a g0|g1, b g0|g1, a g2|g3, b g2|g3]
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float fmax_swap32(float a, float b) {   // [a g0|g2, a g1|g3, b g0|g2, b g1|g3]
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+// Maxima over the 64 lanes of G per-lane values (G = 2, 4, 8), as uniforms.
 template <int G>
-struct alignas(G >= 4 ? 16 : 4 * G) VecG {
-  float v[G];
-};
+__device__ __forceinline__ void wave_max_heads(const float (&x)[G], float (&m)[G]) {
+  float y[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) y[h] = row_max(x[h]);
+  if constexpr (G == 2) {
+    const float z = fmax_swap16(y[0], y[1]);       // groups: h0 (01), h1 (01), h0 (23), h1 (23)
+    const float w = fmax_swap32(z, z);             // groups 0, 2: h0; groups 1, 3: h1
+    m[0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), 0));
+    m[1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), 16));
+  } else {
+#pragma unroll
+    for (int q = 0; q < G / 4; ++q) {
+      // group g ends with head 4q + g
+      const float w = fmax_swap32(fmax_swap16(y[4 * q], y[4 * q + 1]), fmax_swap16(y[4 * q + 2], y[4 * q + 3]));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) m[4 * q + g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), 16 * g));
+    }
+  }
+}
+
+__device__ __forceinline__ int reduce_scatter4(int x0, int x1, int x2, int x3) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);   // [x0 g0, x1 g0, x0 g2, x1 g2], [.. g1 .. g3]
+  const auto b = __builtin_amdgcn_permlane16_swap(x2, x3, false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(a[0] + a[1], b[0] + b[1], false, false);
+  return static_cast<int>(c[0] + c[1]);
+}
 
 template <int M, int G>
 struct DecodeLds {
-  static constexpr int NPOS = M / 4;                 // nibble positions
-  static constexpr int LUT_FLOATS = NPOS * 16 * G;
-  static constexpr int LUT_BYTES = LUT_FLOATS * 4;
-  static constexpr int PB_BYTES = NW * 2 * G * TILE * 2;   // bf16 P parts
-  static constexpr int VB_BYTES = NW * VBUF;               // value tiles
+  static constexpr int NSQ = (3 * G + 15) / 16;      // 16-column sets of limb columns
+  static constexpr int LROW = M + 16;                // bytes per limb row (padded)
+  static constexpr int LIMB_BYTES = 16 * NSQ * LROW; // rows = limb * G + head; others zero
+  static constexpr int P_BYTES = NW * TILE * PROW;   // per-wave probability rows
+  static constexpr int VB_BYTES = NW * VBUF;         // value tiles
   // prologue scratch (aliases the value tiles)
-  static constexpr int QS_BYTES = G * D * 4;
-  static constexpr int QF_BYTES = 8 * 2 * 32 * 16;         // q parts as MFMA operand
-  static constexpr int SQ_BYTES = G * M * 4;
-  static_assert(QS_BYTES + QF_BYTES + SQ_BYTES <= VB_BYTES, "prologue scratch exceeds the value tiles");
+  static constexpr int QF_BYTES = 8 * 2 * 32 * 16;   // q parts as MFMA operand
+  static constexpr int QSS_BYTES = G * 16 * 4;       // partial sums of q^2
+  static_assert(QF_BYTES + QSS_BYTES <= VB_BYTES, "prologue scratch exceeds the value tiles");
   static_assert(G * D * 4 <= VBUF, "wave partial exceeds its value tile");
-  static constexpr int TOTAL = LUT_BYTES + PB_BYTES + VB_BYTES;
+  // split-merge scratch (aliases the value tiles once the wave partials are merged)
+  static constexpr int PAIRS = G * D / 4;
+  static constexpr int REP = PAIRS >= NT ? 1 : NT / PAIRS;
+  static constexpr int ML_FLOATS = 2 * MAX_SPLITS * G;
+  static constexpr int WT_FLOATS = MAX_SPLITS * G;
+  static_assert((ML_FLOATS + WT_FLOATS) * 4 + (REP > 1 ? REP * PAIRS * 16 : 0) <= VB_BYTES,
+                "merge scratch exceeds the value tiles");
+  static constexpr int TOTAL = VB_BYTES + LIMB_BYTES + P_BYTES;
 };
 
 template <int M, int G>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     const float* __restrict__ q, const uint32_t* __restrict__ signs,
     const float* __restrict__ norms, const uint16_t* __restrict__ values,
-    const uint16_t* __restrict__ s_frag, int H_kv, int N, int cap, int n_split, int tps,
-    float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
+    const uint16_t* __restrict__ s_frag, float cnmax, int H_kv, int N, int cap, int n_split,
+    int tps, float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
     float* __restrict__ part_acc, float* __restrict__ part_ml) {
   using L = DecodeLds<M, G>;
   constexpr int WPR = M / 32;        // sign words per token
-  constexpr int SV = WPR / 4;        // 16-byte sign loads per token
-  constexpr int NPOS = L::NPOS;
+  constexpr int CW = M / 128;        // sign words per lane per 16-token block
+  constexpr int KS = M / 64;         // score k-steps of 64 coordinates
+  constexpr int NSQ = L::NSQ;
   static_assert(2 * G <= 16, "P rows (head x part) must fit one 16-row MFMA block");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::TOTAL];
   __shared__ float red_ml[NW][G][2];
+  __shared__ int sumq[G];
   __shared__ int is_last;
-  float* lut = reinterpret_cast<float*>(smem);
-  uint8_t* pb_all = smem + L::LUT_BYTES;
-  uint8_t* vb_all = smem + L::LUT_BYTES + L::PB_BYTES;
-  float* qs = reinterpret_cast<float*>(vb_all);                                  // [G][D]
-  uint4* qfrag = reinterpret_cast<uint4*>(vb_all + L::QS_BYTES);                 // [8][2][32]
-  float* sq = reinterpret_cast<float*>(vb_all + L::QS_BYTES + L::QF_BYTES);      // [G][M]
+  uint8_t* vb_all = smem;
+  uint8_t* limbs = smem + L::VB_BYTES;
+  uint8_t* p_all = smem + L::VB_BYTES + L::LIMB_BYTES;
+  uint4* qfrag = reinterpret_cast<uint4*>(vb_all);                            // [8][2][32]
+  float* qss = reinterpret_cast<float*>(vb_all + L::QF_BYTES);                // [G][16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -173,250 +254,394 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   const uint32_t* sg_base = signs + bh * cap * WPR;
   const float* nm_base = norms + bh * cap;
   const uint16_t* v_base = values + bh * cap * D;
-  uint16_t* pbh = reinterpret_cast<uint16_t*>(pb_all) + wave * 2 * G * TILE;  // [2][G][TILE]
   uint8_t* vbuf = vb_all + wave * VBUF;
+  uint8_t* pbuf = p_all + wave * TILE * PROW;
 
   uint4 vc[VCH];
-  uint4 sc[SV];
-  float nc = 0.f;
-  // Tile loads are branch-free: rows past the end of the split are clamped to
-  // its last row (masked later: logit -inf, probability 0).  Branches around
-  // loads would make the compiler's memory-counter waits conservative (a full
-  // drain), which would serialize the prologue behind the tile prefetch.
-  auto load_signs = [&](int t0, uint4* ss, float& nn) {
-    const int ts = min(t0 + lane, t_end - 1);
-    const uint4* p = reinterpret_cast<const uint4*>(sg_base + static_cast<int64_t>(ts) * WPR);
+  uint32_t sw[4][CW];
+  float nv = 0.f;
+  // Tile loads go through buffer descriptors that start at the tile and end
+  // at the split's end: rows past the end read as zero (their logits are
+  // masked to -inf), with no per-lane clamping or 64-bit address arithmetic,
+  // and no branches (which would make the compiler's memory-counter waits
+  // conservative and serialize the prologue behind the tile prefetch).
+  // Sign words of block j: lane (row l16, group grp) takes token 16j + l16,
+  // coordinates (M/4) grp .. (M/4)(grp + 1) - 1 (CW words); lane t takes the
+  // norm of token t0 + t.
+  auto tile_rows = [&](int t0_) { return max(0, min(TILE, t_end - t0_)); };
+  const int so_lane = l16 * WPR * 4 + CW * 4 * grp;
+  auto load_signs = [&](int t0_, uint32_t (&s)[4][CW], float& n) {
+    const int rows = tile_rows(t0_);
+    const rsrc_t rs = make_rsrc(sg_base + static_cast<int64_t>(t0_) * WPR, rows * WPR * 4);
+    const rsrc_t rn = make_rsrc(nm_base + t0_, rows * 4);
 #pragma unroll
-    for (int k = 0; k < SV; ++k) ss[k] = ld16(p + k);
-    nn = nm_base[ts];
+    for (int j = 0; j < 4; ++j) {
+      const int off = so_lane + 16 * j * WPR * 4;
+      if constexpr (CW == 2) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        s[j][0] = v.x;
+        s[j][1] = v.y;
+      } else {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        s[j][0] = v.x;
+        s[j][1] = v.y;
+        s[j][2] = v.z;
+        s[j][3] = v.w;
+      }
+    }
+    n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, 0, 0));
   };
   // value chunk c of a tile: token t0 + 4c + lane/16, channels 8*(lane%16) .. +7
-  auto load_values = [&](int t0, auto half_const) {
+  const int vo_lane = grp * D * 2 + l16 * 16;
+  auto load_values = [&](int t0_, auto half_const) {
     constexpr int c_begin = decltype(half_const)::value * (VCH / 2);
+    const rsrc_t rv = make_rsrc(v_base + static_cast<int64_t>(t0_) * D, tile_rows(t0_) * D * 2);
 #pragma unroll
     for (int u = 0; u < VCH / 2; ++u) {
-      const int tv = min(t0 + 4 * (c_begin + u) + (lane >> 4), t_end - 1);
-      vc[c_begin + u] = ld16(reinterpret_cast<const uint4*>(v_base + static_cast<int64_t>(tv) * D) + (lane & 15));
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_lane + 4 * (c_begin + u) * D * 2, 0, 0);
+      vc[c_begin + u] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
   int t0 = t_begin + wave * TILE;
 
   // ---- prologue ----
-  // q and the S^T fragments are requested first; memory counters drain in
-  // order, so waiting for them leaves the later tile loads in flight.
+  // q (straight into the split entries), the S^T fragments and the first
+  // tile are requested in that order; memory counters drain in order, so
+  // waiting for q and S^T leaves the tile loads in flight.
   constexpr int NBLK = M / 32;            // blocks of 32 sketch coordinates
-  constexpr int BPW = NBLK / NW;          // blocks per wave (2 or 4)
-  constexpr int BATCH = BPW;             // all fragments go out before the tile loads
-  static_assert(BPW % BATCH == 0, "blocks per wave must be a multiple of the batch");
+  constexpr int BPW = NBLK / NW;          // blocks per wave
+  static_assert(NBLK % NW == 0, "sketch blocks must divide among the waves");
+  static_assert(8 * 2 * 32 % NT == 0, "q entries must divide among the threads");
   const int col = lane & 31;
   const int half = lane >> 5;
+  // q entry e = (k-step st, half hf, column c): q[head][16 st + 8 hf .. +7],
+  // column c = part * G + head (columns >= 3G are zero); every entry loads
+  // (the head index is valid for any c), so the loads need no branch.
+  constexpr int QE = 8 * 2 * 32;
+  constexpr int QEPT = QE / NT;
+  const float* qb = q + bh * G * D;
+  float4 qa[QEPT][2];
+#pragma unroll
+  for (int k = 0; k < QEPT; ++k) {
+    const int e = tid + k * NT;
+    const int c = e & 31, st = e >> 6, hf = (e >> 5) & 1;
+    const float4* src = reinterpret_cast<const float4*>(qb + (c % G) * D + 16 * st + 8 * hf);
+    qa[k][0] = src[0];
+    qa[k][1] = src[1];
+  }
   // S^T comes in fragment order (see DeviceSketch::s_frag): the operand of
   // (block, k-step) is 64 lanes x 16 contiguous bytes, one 1 KB load.
-  uint4 af[BATCH][8];
-  auto load_frags = [&](int batch) {
+  uint4 af[BPW][8];
 #pragma unroll
-    for (int bb = 0; bb < BATCH; ++bb) {
-      const int blk = wave + NW * (batch * BATCH + bb);
-      const uint4* fr = reinterpret_cast<const uint4*>(s_frag) + static_cast<int64_t>(blk) * 8 * 64 + lane;
+  for (int bb = 0; bb < BPW; ++bb) {
+    const int blk = wave + NW * bb;
+    const uint4* fr = reinterpret_cast<const uint4*>(s_frag) + static_cast<int64_t>(blk) * 8 * 64 + lane;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) af[bb][st] = fr[st * 64];
-    }
-  };
-  const float* qb = q + bh * G * D;
-  constexpr int QPT = (G * D + NT - 1) / NT;
-  float qv[QPT];
-#pragma unroll
-  for (int k = 0; k < QPT; ++k) qv[k] = (tid + k * NT < G * D) ? qb[tid + k * NT] : 0.f;
-  // every wave has requested q before any wave requests S^T or its tile, so
-  // q is at the head of this compute unit's memory queue
-  __syncthreads();
-  load_frags(0);
-  load_signs(t0, sc, nc);
-  load_values(t0, std::integral_constant<int, 0>{});
-  load_values(t0, std::integral_constant<int, 1>{});
-#pragma unroll
-  for (int k = 0; k < QPT; ++k) {
-    const int i = tid + k * NT;
-    if (i < G * D) qs[i] = qv[k];
+    for (int st = 0; st < 8; ++st) af[bb][st] = fr[st * 64];
   }
-  __syncthreads();
+  load_signs(t0, sw, nv);
+  load_values(t0, std::integral_constant<int, 0>{});
+  // with m = 512 the S^T fragments fill half the registers: the second half
+  // of the first tile's values is requested after S^T q
+  if constexpr (M == 256) load_values(t0, std::integral_constant<int, 1>{});
+
+  // limb rows >= 3G and probability rows >= 2G stay zero; the sums of Q
+  // start at zero
+  constexpr int ZERO_U4 = (16 * NSQ - 3 * G) * L::LROW / 16;
+  for (int i = tid; i < ZERO_U4; i += NT)
+    reinterpret_cast<uint4*>(limbs + 3 * G * L::LROW)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < L::P_BYTES / 16; i += NT) reinterpret_cast<uint4*>(p_all)[i] = make_uint4(0, 0, 0, 0);
+  if (tid < G) sumq[tid] = 0;
+
   // q -> three bf16 parts (hi + mid + lo equals fp32 q to within 2^-24
   // relative), laid out as the MFMA B operand: column c = part * G + head.
-  for (int e = tid; e < 8 * 2 * 32; e += NT) {
-    const int st = e >> 6, hf = (e >> 5) & 1, c = e & 31;
-    const int part = c / G, g = c % G;
+#pragma unroll
+  for (int k = 0; k < QEPT; ++k) {
+    const int e = tid + k * NT;
+    const int c = e & 31;
+    const int part = c / G;
+    const float x[8] = {qa[k][0].x, qa[k][0].y, qa[k][0].z, qa[k][0].w,
+                        qa[k][1].x, qa[k][1].y, qa[k][1].z, qa[k][1].w};
     uint32_t pk[4];
+    float ss = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      uint32_t h2[2];
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const float x = part < 3 ? qs[g * D + 16 * st + 8 * hf + 2 * u + v] : 0.f;
-        const uint32_t hi = f32_to_bf16_rne(x);
-        const float r1 = x - __uint_as_float(hi << 16);
-        const uint32_t mid = f32_to_bf16_rne(r1);
-        const float r2 = r1 - __uint_as_float(mid << 16);
-        const uint32_t lo = f32_to_bf16_rne(r2);
-        h2[v] = part == 0 ? hi : (part == 1 ? mid : lo);
-      }
-      pk[u] = h2[0] | (h2[1] << 16);
+      const float x0 = x[2 * u], x1 = x[2 * u + 1];
+      ss = __builtin_fmaf(x0, x0, ss);
+      ss = __builtin_fmaf(x1, x1, ss);
+      const uint32_t hi = cvt2_bf16(x0, x1);
+      const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+      const uint32_t mid = cvt2_bf16(r0, r1);
+      const uint32_t lo = cvt2_bf16(r0 - __uint_as_float(mid << 16), r1 - __uint_as_float(mid & 0xFFFF0000u));
+      pk[u] = part == 0 ? hi : (part == 1 ? mid : (part == 2 ? lo : 0u));
     }
     qfrag[e] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    if (c < G) qss[c * 16 + (e >> 5)] = ss;   // e >> 5 = 2 st + hf
   }
   __syncthreads();
+
+  // quantization step 2^E of head h: 2^(E + 21) exceeds ||q_h|| max_i ||s_i||
+  // (with margin for the rounding of S^T q and of the norm itself)
+  auto head_exp = [&](int h) -> int {
+    const float4* p = reinterpret_cast<const float4*>(qss + h * 16);
+    const float4 a0 = p[0], a1 = p[1], a2 = p[2], a3 = p[3];
+    const float s = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w)) +
+                    ((a2.x + a2.y) + (a2.z + a2.w)) + ((a3.x + a3.y) + (a3.z + a3.w));
+    const float bound = __builtin_sqrtf(s) * cnmax * (1.0f + 0x1p-10f) + 0x1p-100f;
+    int e = __builtin_amdgcn_frexp_expf(bound);   // bound < 2^e
+    e -= QBITS;
+    return min(100, max(-100, e));
+  };
+
+  // Exponents of all heads, and of the head of this lane's S^T q columns
+  // (col % G); taken here because the q^2 sums share LDS with the value tiles.
+  int e_all[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) e_all[h] = __builtin_amdgcn_readfirstlane(head_exp(h));
+  const int e_h = head_exp(col % G);
+
+  // S^T q on the matrix cores, then its limbs.  Lane (col, half), register r
+  // of block blk holds coordinate 32 blk + 8 (r/4) + 4 half + r%4.
   {
+    const float inv_s = __builtin_ldexpf(1.0f, -e_h);
+    int qsum = 0;
 #pragma unroll
-    for (int batch = 0; batch < BPW / BATCH; ++batch) {
-      if (batch > 0) load_frags(batch);
+    for (int bb = 0; bb < BPW; ++bb) {
+      const int blk = wave + NW * bb;
+      f32x16_t acc = {};
 #pragma unroll
-      for (int bb = 0; bb < BATCH; ++bb) {
-        const int blk = wave + NW * (batch * BATCH + bb);
-        f32x16_t acc = {};
+      for (int st = 0; st < 8; ++st)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[bb][st]),
+                                                      __builtin_bit_cast(bf16x8_t, qfrag[(st * 2 + half) * 32 + col]),
+                                                      acc, 0, 0, 0);
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[bb][st]),
-                                                        __builtin_bit_cast(bf16x8_t, qfrag[(st * 2 + half) * 32 + col]),
-                                                        acc, 0, 0, 0);
-        // lane (col, half), register r -> coordinate 32*blk + 8*(r/4) + 4*half + r%4
+      for (int a4 = 0; a4 < 4; ++a4) {
+        uint32_t pk[3] = {0u, 0u, 0u};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * a4 + i;
           float v;
           if (G < 8) {   // columns col + G and col + 2G lie in the same 16-lane row
             v = acc[r] + dpp<kRowShl + G>(acc[r]) + dpp<kRowShl + 2 * G>(acc[r]);
           } else {
             v = acc[r] + __shfl(acc[r], lane + G) + __shfl(acc[r], lane + 2 * G);
           }
-          if (col < G) sq[col * M + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3)] = v;
+          int Q = static_cast<int>(__builtin_rintf(v * inv_s));
+          Q = min(1 << QBITS, max(-(1 << QBITS), Q));
+          qsum += Q;
+          const int c0 = ((Q + 128) & 255) - 128;
+          const int q1 = (Q - c0) >> 8;
+          const int c1 = ((q1 + 128) & 255) - 128;
+          const int c2 = (q1 - c1) >> 8;
+          pk[0] |= (static_cast<uint32_t>(c2) & 255u) << (8 * i);
+          pk[1] |= (static_cast<uint32_t>(c1) & 255u) << (8 * i);
+          pk[2] |= (static_cast<uint32_t>(c0) & 255u) << (8 * i);
+        }
+        if (col < G) {
+          const int coord = 32 * blk + 8 * a4 + 4 * half;
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            *reinterpret_cast<uint32_t*>(limbs + (p * G + col) * L::LROW + coord) = pk[p];
         }
       }
     }
+    if (col < G) atomicAdd(&sumq[col], qsum);
   }
-  __syncthreads();
-  // entry v of group p: sum_k (bit k of v ? +1 : -1) * sq[4p + k]
-  //   = base + 2 * sum_{k in v} sq[4p + k],  base = -sum_k sq[4p + k]
-  for (int e = tid; e < NPOS * G; e += NT) {
-    const int p = e / G, g = e % G;
-    const float4 x = *reinterpret_cast<const float4*>(&sq[g * M + 4 * p]);
-    float t[16];
-    t[0] = -(x.x + x.y + x.z + x.w);
-    t[1] = t[0] + 2.f * x.x;
-    t[2] = t[0] + 2.f * x.y;
-    t[3] = t[1] + 2.f * x.y;
-#pragma unroll
-    for (int v = 4; v < 8; ++v) t[v] = t[v - 4] + 2.f * x.z;
-#pragma unroll
-    for (int v = 8; v < 16; ++v) t[v] = t[v - 8] + 2.f * x.w;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) lut[(p * 16 + v) * G + g] = t[v];
-  }
+  if constexpr (M != 256) load_values(t0, std::integral_constant<int, 1>{});
   __syncthreads();
 
-  // ---- main loop ----
+  // ---- main loop setup ----
+  // Per head: logit (base 2) = (kap[h] * sum_i b_i Q_i + bet[h]) * ||k||,
+  // kap = 2 coef 2^E, bet = -coef 2^E sum_i Q_i.
+  float kap[G], bet[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float s_h = __builtin_ldexpf(1.0f, e_all[h]);
+    kap[h] = uniform(2.0f * coef * s_h);
+    bet[h] = uniform(-coef * s_h * static_cast<float>(__builtin_amdgcn_readfirstlane(sumq[h])));
+  }
+  // A operand of the score product: limb row 16 cb + l16, coordinates
+  // (M/4) grp + 16 ks .. +15
+  const uint8_t* brow[NSQ];
+#pragma unroll
+  for (int cb = 0; cb < NSQ; ++cb) brow[cb] = limbs + (16 * cb + l16) * L::LROW + (M / 4) * grp;
+  // Score accumulator of block j: lane (grp, l16), register r holds limb row
+  // 16 cb + 4 grp + r (limb p = row / G, head row % G) for token 16 j + l16.
+  // Rows are weighted 2^16, 2^8, 1 by limb, then summed over the lane
+  // groups so that group g keeps block g: each lane ends with its token
+  // t0 + lane and all G heads.
+  const uint32_t sh_grp = grp == 0 ? 16u : (grp == 1 ? 8u : 0u);    // G = 4: limb = grp
+  const uint32_t sh_g2 = grp == 0 ? 16u : 0u;                         // G = 2: rows h, 4 + h
+  const uint32_t sh_g8 = grp < 2 ? 16u : 8u;                          // G = 8: limb 0 or 1
+  const int odd_mask = -(grp & 1);                                    // G = 8: heads 4..7 rows
+
   float m_run[G], l_run[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
   }
   f32x4_t acc[NDB];
 #pragma unroll
   for (int nb = 0; nb < NDB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // P operand rows: row = part * G + head for row < 2G (lane & 15 = row)
-  const int prow = lane & 15;
-  const int ppart = prow / G, phead = prow % G;
-  const bool prow_live = prow < 2 * G;
-  const int kgrp = lane >> 4;       // MFMA k group: tokens 8*kgrp .. +7 of the step
-  int row_head[4];                  // head of accumulator row 4*kgrp + r, or -1
-#pragma unroll
-  for (int r = 0; r < 4; ++r) row_head[r] = (4 * kgrp + r < 2 * G) ? (4 * kgrp + r) % G : -1;
-  // transposed-read source: lane s of a 16-lane group addresses token
-  // 8*kgrp + s/4 (+4 for the second read), columns 4*(s%4) .. +3 of the block
-  const int tr_tok = 8 * kgrp + ((lane & 15) >> 2);
-  const uint8_t* tr_base0 = vbuf + vrow(tr_tok) * VROW + 8 * (lane & 3);
-  const uint8_t* tr_base1 = vbuf + vrow(tr_tok + 4) * VROW + 8 * (lane & 3);
+  // transposed-read sources: lane s of group grp addresses token 4 grp + s/4
+  // of the half tile (first read) and 16 + 4 grp + s/4 (second read), at
+  // columns 4 (s%4) .. +3 of a 16-column block (values) or rows 4 (s%4) .. +3
+  // of the probability rows.  With 288-byte value rows (32-byte probability
+  // rows) the 8 rows touched by each 32 lanes fall on distinct banks.
+  const uint8_t* tr_base0 = vbuf + (4 * grp + (l16 >> 2)) * VROW + 8 * (lane & 3);
+  const uint8_t* tr_base1 = tr_base0 + 16 * VROW;
+  const uint8_t* pr_base0 = pbuf + (4 * grp + (l16 >> 2)) * PROW + 8 * (lane & 3);
+  const uint8_t* pr_base1 = pr_base0 + 16 * PROW;
 
-  // Only one tile of values lives in registers: each half is reloaded with
-  // the next tile's rows as soon as it has been copied into LDS.  Sign words
-  // and norms of the next tile are requested first, so waiting for them does
-  // not wait for the values.
-  while (t0 < t_end) {
+  auto body = [&](auto prefetch_const) {
+    constexpr bool PF = decltype(prefetch_const)::value;
     const int t_next = t0 + NW * TILE;
-    uint4 sn[SV];
-    float nn;
-    load_signs(t_next, sn, nn);
+    uint32_t swn[4][CW];
+    float nvn = 0.f;
+    if constexpr (PF) load_signs(t_next, swn, nvn);
 
-    // scores: lane <-> token t0 + lane
-    float sc_g[G];
+    // scores: block j, limb-row set cb (A = limbs, B = token bits)
+    i32x4_t sacc[NSQ][4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) sc_g[g] = 0.f;
+    for (int cb = 0; cb < NSQ; ++cb)
 #pragma unroll
-    for (int k = 0; k < SV; ++k) {
-      const uint32_t wv[4] = {sc[k].x, sc[k].y, sc[k].z, sc[k].w};
+      for (int j = 0; j < 4; ++j) sacc[cb][j] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t w = wv[u];
+    for (int ks = 0; ks < KS; ++ks) {
+      i32x4_t lop[NSQ];
 #pragma unroll
-        for (int nib = 0; nib < 8; ++nib) {
-          const int pos = (4 * k + u) * 8 + nib;
-          const uint32_t idx = (w >> (4 * nib)) & 15u;
-          const VecG<G> t = *reinterpret_cast<const VecG<G>*>(&lut[(pos * 16 + idx) * G]);
+      for (int cb = 0; cb < NSQ; ++cb) lop[cb] = *reinterpret_cast<const i32x4_t*>(brow[cb] + 16 * ks);
 #pragma unroll
-          for (int g = 0; g < G; ++g) sc_g[g] += t.v[g];
-        }
-        // keep at most one word's table reads in flight (register pressure)
-        __asm__ __volatile__("" ::: "memory");
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = sw[j][ks >> 1];
+        i32x4_t bits;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          bits[qd] = static_cast<int>((__builtin_amdgcn_ubfe(w, 16 * (ks & 1) + 4 * qd, 4) * 0x00204081u) &
+                                      0x01010101u);
+#pragma unroll
+        for (int cb = 0; cb < NSQ; ++cb)
+          sacc[cb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lop[cb], bits, sacc[cb][j], 0, 0, 0);
       }
     }
-    const bool valid = (t0 + lane) < t_end;
-    float alpha_g[G];
+    // sum_i b_i Q_i of token t0 + lane, per head
+    int tot[G];
+    auto u = [](int x) { return static_cast<uint32_t>(x); };
+    if constexpr (G == 1) {
+      int x[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float logit = valid ? sc_g[g] * (coef * nc) : -INFINITY;
-      const float tmax = wave_max(logit);
-      const float m_new = fmaxf(m_run[g], tmax);
-      const float alpha = exp2f(m_run[g] - m_new);
-      const float p = valid ? exp2f(logit - m_new) : 0.f;
-      l_run[g] = l_run[g] * alpha + p;
-      m_run[g] = m_new;
-      // P as bf16 hi + lo (about 16 significant bits)
-      const uint32_t hi = f32_to_bf16_rne(p);
-      const uint32_t lo = f32_to_bf16_rne(p - __uint_as_float(hi << 16));
-      pbh[g * TILE + lane] = static_cast<uint16_t>(hi);
-      pbh[(G + g) * TILE + lane] = static_cast<uint16_t>(lo);
-      alpha_g[g] = alpha;
+      for (int j = 0; j < 4; ++j)
+        x[j] = static_cast<int>((u(sacc[0][j][0]) << 16) + (u(sacc[0][j][1]) << 8) + u(sacc[0][j][2]));
+      tot[0] = reduce_scatter4(x[0], x[1], x[2], x[3]);
+    } else if constexpr (G == 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[j] = static_cast<int>((u(sacc[0][j][h]) << sh_g2) + (u(sacc[0][j][2 + h]) << 8));
+        tot[h] = reduce_scatter4(x[0], x[1], x[2], x[3]);
+      }
+    } else if constexpr (G == 4) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        tot[h] = reduce_scatter4(static_cast<int>(u(sacc[0][0][h]) << sh_grp), static_cast<int>(u(sacc[0][1][h]) << sh_grp),
+                                 static_cast<int>(u(sacc[0][2][h]) << sh_grp), static_cast<int>(u(sacc[0][3][h]) << sh_grp));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int z[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] = static_cast<int>((u(sacc[0][j][r]) << sh_g8) + u(sacc[1][j][r]));
+        const auto a01 = __builtin_amdgcn_permlane32_swap(z[0], z[1], false, false);
+        const auto a23 = __builtin_amdgcn_permlane32_swap(z[2], z[3], false, false);
+        const auto c = __builtin_amdgcn_permlane32_swap(a01[0] + a01[1], a23[0] + a23[1], false, false);
+        const auto d = __builtin_amdgcn_permlane16_swap(c[0], c[1], false, false);
+        tot[r] = static_cast<int>(d[0]);
+        tot[4 + r] = static_cast<int>(d[1]);
+      }
     }
-    // rescale the running output: register r of this lane holds row
-    // 4*kgrp + r, i.e. head row_head[r] (rows >= 2G are unused)
+    // online softmax per head (maxima and rescale factors are wave-uniform)
+    const bool live = PF || (t0 + lane < t_end);
+    float p[G], al[G], tmax[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float v = __builtin_fmaf(static_cast<float>(tot[h]), kap[h], bet[h]) * nv;
+      p[h] = live ? v : -INFINITY;   // logit
+    }
+    if constexpr (G == 1) {
+      tmax[0] = wave_max(p[0]);
+    } else {
+      wave_max_heads<G>(p, tmax);
+    }
+    bool rescale = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m_new = fmaxf(m_run[h], tmax[h]);
+      rescale |= m_new > m_run[h];
+      al[h] = uniform(__builtin_amdgcn_exp2f(m_run[h] - m_new));
+      m_run[h] = m_new;
+      p[h] = __builtin_amdgcn_exp2f(p[h] - m_new);
+      l_run[h] = __builtin_fmaf(l_run[h], al[h], p[h]);
+    }
+    // probabilities of this token as bf16 hi (rows 0..G-1) and lo (rows
+    // G..2G-1) parts; rows 2G..15 stay zero
+    {
+      uint32_t hi[(G + 1) / 2], lo[(G + 1) / 2];
+#pragma unroll
+      for (int i = 0; i < (G + 1) / 2; ++i) {
+        const float p0 = p[2 * i], p1 = 2 * i + 1 < G ? p[2 * i + 1] : 0.f;
+        hi[i] = cvt2_bf16(p0, p1);
+        lo[i] = cvt2_bf16(p0 - __uint_as_float(hi[i] << 16), p1 - __uint_as_float(hi[i] & 0xFFFF0000u));
+      }
+      uint8_t* prow = pbuf + lane * PROW;
+      if constexpr (G == 1) {
+        *reinterpret_cast<uint32_t*>(prow) = (hi[0] & 0xFFFFu) | (lo[0] << 16);
+      } else if constexpr (G == 2) {
+        *reinterpret_cast<uint2*>(prow) = make_uint2(hi[0], lo[0]);
+      } else if constexpr (G == 4) {
+        *reinterpret_cast<uint4*>(prow) = make_uint4(hi[0], hi[1], lo[0], lo[1]);
+      } else {
+        *reinterpret_cast<uint4*>(prow) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(prow + 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+    }
+    // rescale the running output (only when some head's maximum rose):
+    // accumulator row 4 grp + r belongs to head (4 grp + r) % G
+    if (rescale)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float a = 1.f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) a = (row_head[r] == g) ? alpha_g[g] : a;
+      float a;
+      if constexpr (G <= 4) {
+        a = al[r % G];
+      } else {   // bitwise select (a conditional here becomes an indexed private array)
+        a = __int_as_float((__float_as_int(al[4 + r]) & odd_mask) | (__float_as_int(al[r]) & ~odd_mask));
+      }
 #pragma unroll
       for (int nb = 0; nb < NDB; ++nb) acc[nb][r] *= a;
     }
 
-    // P.V for rows 32*HS .. +31 of the tile (HS = 0, 1 as constants, so the
+    // P.V for tokens 32*HS .. +31 of the tile (HS = 0, 1 as constants, so the
     // value registers are addressed statically)
     auto pv_half = [&](auto hs_const) {
       constexpr int hstep = decltype(hs_const)::value;
       // value rows 32*hstep .. +31 of the tile -> wave-private LDS tile
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        // token 4u + lane/16 of the half tile; vrow() only permutes the
-        // groups of 4 rows, so the lane part stays a per-lane base
-        const int row = vrow(4 * u) + (lane >> 4);
-        *reinterpret_cast<uint4*>(vbuf + row * VROW + (lane & 15) * 16) = vc[8 * hstep + u];
-      }
+      for (int u8 = 0; u8 < 8; ++u8)
+        *reinterpret_cast<uint4*>(vbuf + (4 * u8 + grp) * VROW + l16 * 16) = vc[8 * hstep + u8];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      load_values(t_next, hs_const);
-      // A operand: P rows, tokens 32*hstep + 8*kgrp .. +7
-      uint4 pa = make_uint4(0, 0, 0, 0);
-      if (prow_live)
-        pa = *reinterpret_cast<const uint4*>(pbh + (ppart * G + phead) * TILE + HALF * hstep + 8 * kgrp);
-      const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, pa);
+      if constexpr (PF) load_values(t_next, hs_const);
+      // A operand: probability rows, tokens as for the value reads
+      const i16x4_t pa0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(pr_base0 + 32 * PROW * hstep));
+      const i16x4_t pa1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(pr_base1 + 32 * PROW * hstep));
+      const uint2 pl = __builtin_bit_cast(uint2, pa0);
+      const uint2 ph = __builtin_bit_cast(uint2, pa1);
+      const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, make_uint4(pl.x, pl.y, ph.x, ph.y));
 #pragma unroll
       for (int nb = 0; nb < NDB; ++nb) {
         const uint8_t* p0 = tr_base0 + 32 * nb;
@@ -437,38 +662,46 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
     pv_half(std::integral_constant<int, 0>{});
     pv_half(std::integral_constant<int, 1>{});
 
-    t0 = t_next;
+    if constexpr (PF) {
+      t0 = t_next;
 #pragma unroll
-    for (int k = 0; k < SV; ++k) sc[k] = sn[k];
-    nc = nn;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int w = 0; w < CW; ++w) sw[j][w] = swn[j][w];
+      nv = nvn;
+    }
+  };
+  if (t0 < t_end) {
+    while (t0 + NW * TILE < t_end) body(std::true_type{});
+    body(std::false_type{});
   }
 
   // ---- wave result: out row = hi row + lo row, into this wave's LDS tile ----
+#pragma unroll
+  for (int h = 0; h < G; ++h) l_run[h] = wave_sum(l_run[h]);
   // Accumulator block nb: lane l holds row 4*(l/16) + r, column l%16.  Row g
   // (hi part of head g) pairs with row G + g (lo part): for G >= 4 the lo row
   // sits G/4 lane groups later in the same register; for G < 4 both rows are
   // registers of lanes 0..15.
   float* wacc = reinterpret_cast<float*>(vbuf);   // [G][D]
 #pragma unroll
-  for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
-#pragma unroll
   for (int nb = 0; nb < NDB; ++nb) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (G >= 4) {
         const float v = acc[nb][r] + __shfl(acc[nb][r], (lane + 16 * (G / 4)) & 63);
-        const int row = 4 * kgrp + r;
-        if (row < G) wacc[row * D + 16 * nb + (lane & 15)] = v;
+        const int row = 4 * grp + r;
+        if (row < G) wacc[row * D + 16 * nb + l16] = v;
       } else if (r < G) {
-        if (kgrp == 0) wacc[r * D + 16 * nb + (lane & 15)] = acc[nb][r] + acc[nb][(r + G) & 3];
+        if (grp == 0) wacc[r * D + 16 * nb + l16] = acc[nb][r] + acc[nb][(r + G) & 3];
       }
     }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      red_ml[wave][g][0] = m_run[g];
-      red_ml[wave][g][1] = l_run[g];
+    for (int h = 0; h < G; ++h) {
+      red_ml[wave][h][0] = m_run[h];
+      red_ml[wave][h][1] = l_run[h];
     }
   }
   __syncthreads();
@@ -525,13 +758,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   // splits are divided among REP replicas whose sums meet in LDS.  The
   // (max, sum) pairs and the first MCH partial accumulators of every thread
   // are requested together, so the merge costs one round trip to memory.
-  constexpr int PAIRS = G * D / 4;
-  constexpr int REP = PAIRS >= NT ? 1 : NT / PAIRS;
+  constexpr int PAIRS = L::PAIRS;
+  constexpr int REP = L::REP;
   constexpr int MCH = 32;                 // float4 loads in flight per thread
-  static_assert(REP == 1 || REP * PAIRS * 16 <= L::VB_BYTES, "merge replicas exceed the LDS buffer");
-  float* ml_l = lut;                      // 2 * n_split * G floats
-  float* wts = lut + 2 * MAX_SPLITS * G;  // n_split * G floats
-  static_assert(3 * MAX_SPLITS * G <= L::LUT_FLOATS, "merge scratch exceeds the table");
+  float* ml_l = reinterpret_cast<float*>(vb_all);   // 2 * n_split * G floats
+  float* wts = ml_l + L::ML_FLOATS;                 // n_split * G floats
+  float4* rep_sum = reinterpret_cast<float4*>(wts + L::WT_FLOATS);
   const float2* ml_src = reinterpret_cast<const float2*>(part_ml + bh * n_split * G * 2);
   const float4* pa = reinterpret_cast<const float4*>(part_acc);
   constexpr int ML_PT = (MAX_SPLITS * G + NT - 1) / NT;
@@ -596,15 +828,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
     if (REP == 1) {
       reinterpret_cast<float4*>(out)[(bh * G + mg) * (D / 4) + c4] = o;
     } else {
-      reinterpret_cast<float4*>(vb_all)[rep * PAIRS + pr] = o;
+      rep_sum[rep * PAIRS + pr] = o;
     }
   }
   if (REP > 1) {
     __syncthreads();
     for (int p2 = tid; p2 < PAIRS; p2 += NT) {
-      float4 o = reinterpret_cast<const float4*>(vb_all)[p2];
+      float4 o = rep_sum[p2];
       for (int r2 = 1; r2 < REP; ++r2) {
-        const float4 v = reinterpret_cast<const float4*>(vb_all)[r2 * PAIRS + p2];
+        const float4 v = rep_sum[r2 * PAIRS + p2];
         o.x += v.x;
         o.y += v.y;
         o.z += v.z;
@@ -628,8 +860,8 @@ int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float*
   float* part_ml = part_acc + static_cast<size_t>(B) * H_kv * G * plan.n_split * D;
   dim3 grid(plan.n_split, H_kv, B);
   hipLaunchKernelGGL((decode_kernel<M, G>), grid, dim3(NT), 0, stream, q, signs, norms,
-                     static_cast<const uint16_t*>(values), s.s_frag, H_kv, N, cap, plan.n_split,
-                     plan.tokens_per_split, coef, out, counters, part_acc, part_ml);
+                     static_cast<const uint16_t*>(values), s.s_frag, s.col_norm_all, H_kv, N, cap,
+                     plan.n_split, plan.tokens_per_split, coef, out, counters, part_acc, part_ml);
   return hipGetLastError();
 }
 
@@ -655,7 +887,7 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
   const int64_t streams = static_cast<int64_t>(B) * H_kv;
   // Aim for about two workgroups per compute unit (256 CUs) while keeping at
   // least one full step (4 waves x 64 tokens) per split.
-  constexpr int64_t kTargetWorkgroups = 512;
+  constexpr int64_t kTargetWorkgroups = 2048 / NW;
   constexpr int kMinTokens = NW * TILE;
   int64_t want = (kTargetWorkgroups + streams - 1) / streams;
   if (streams > kMaxCounters) want = 1;   // splits (and counters) only for few streams

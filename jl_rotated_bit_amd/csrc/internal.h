@@ -21,6 +21,7 @@ struct DeviceSketch {
   // S^T[32*block + l%32][16*kstep + 8*(l/32) .. +7] (decode: S^T q)
   const uint16_t* s_frag = nullptr;
   const float* col_norm_max = nullptr;  // [m/64] max_{i in group} ||S[:, i]||_2, rounded up
+  float col_norm_all = 0.f;             // max over all m columns of ||S[:, i]||_2, rounded up
   int d = 0;
   int m = 0;
 };

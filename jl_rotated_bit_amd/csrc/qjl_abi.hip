@@ -110,6 +110,7 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
   ce.view.s_md = reinterpret_cast<const uint16_t*>(base + off_md);
   ce.view.s_frag = reinterpret_cast<const uint16_t*>(base + off_fr);
   ce.view.col_norm_max = reinterpret_cast<const float*>(base + off_cm);
+  for (float c : cmax) ce.view.col_norm_all = std::max(ce.view.col_norm_all, c);
   ce.view.d = d;
   ce.view.m = m;
   g_cache.emplace(key, ce);
