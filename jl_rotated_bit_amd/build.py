@@ -23,10 +23,11 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqjl.so")
 
 HIP_SOURCES = ["qjl_abi.hip", "encode.hip", "decode.hip"]
-# Per-source extras.  Decode: NaN inputs are outside its contract, and without
-# NaNs every max needs no operand canonicalization (which would otherwise cost
-# an instruction per operand and block folding cross-lane moves into the max).
-HIP_EXTRA = {"decode.hip": ["-fno-honor-nans"]}
+# Per-source extras.  NaN inputs are outside the contract of both kernels, and
+# without NaNs a min/max needs no operand canonicalization (which would
+# otherwise cost an instruction per operand and block folding cross-lane
+# moves into the max).
+HIP_EXTRA = {"decode.hip": ["-fno-honor-nans"], "encode.hip": ["-fno-honor-nans"]}
 HOST_SOURCES = ["sketch.cpp"]
 ARCH = "gfx950"
 

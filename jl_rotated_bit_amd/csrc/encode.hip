@@ -51,6 +51,8 @@ constexpr int LDS_ROW = ROW_B + 16;  // padded LDS row: spreads lanes over banks
 constexpr int TILE_LDS = KT * LDS_ROW;
 constexpr int CHUNKS = KT * ROW_B / 16;  // 16-byte chunks per key tile (2048)
 constexpr int ACC_WORDS = 18;        // long accumulator: 576 bits
+constexpr int QCAP = 64;             // deferred-fix queue entries per wave
+constexpr int FIXB = 16;             // (word, bit) fixes per batch of loads
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
@@ -82,7 +84,8 @@ __device__ void long_add(uint32_t* acc, int w, uint64_t v) {
 // each product is an integer sig_k*sig_s < 2^16 times 2^(Ek + Es - 268):
 // it is added, shifted by Ek + Es - 2 bits, into one of two 576-bit
 // magnitudes (positive / negative terms), which are compared at the end.
-__device__ bool exact_sign_long(const uint16_t* key_lds, const uint16_t* s_row, uint32_t* scratch) {
+__device__ __attribute__((noinline)) bool exact_sign_long(const uint16_t* key_lds, const uint16_t* s_row,
+                                                          uint32_t* scratch) {
   uint32_t* pos = scratch;
   uint32_t* neg = scratch + ACC_WORDS;
   for (int i = 0; i < 2 * ACC_WORDS; ++i) scratch[i] = 0;
@@ -105,10 +108,84 @@ __device__ bool exact_sign_long(const uint16_t* key_lds, const uint16_t* s_row, 
   return true;  // exact zero: sign(0) = +1
 }
 
-__device__ __forceinline__ double wave_sum_f64(double x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+// The same pairwise tree over the 64 lanes, through DPP row rotations and
+// 16-/32-lane row swaps (VALU only, no LDS round trips): every lane ends
+// with the sum of all 64 inputs, formed with 6 levels of additions.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), CTRL, 0xF, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+// x + (x of the lane 16 (WIDE: 32) lanes away): with both operands equal, a
+// row swap returns [x g0, x g0, x g2, x g2] and [x g1, x g1, x g3, x g3]
+// (16-lane groups g); their sum is the butterfly step in every lane.
+template <bool WIDE>
+__device__ __forceinline__ double swap_add_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  uint32_t l0, l1, h0, h1;
+  if constexpr (WIDE) {
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto c = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    l0 = a[0]; l1 = a[1]; h0 = c[0]; h1 = c[1];
+  } else {
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    l0 = a[0]; l1 = a[1]; h0 = c[0]; h1 = c[1];
+  }
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(h0) << 32) | l0)) +
+         __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(h1) << 32) | l1));
+}
+__device__ __forceinline__ double wave_sum_f64_dpp(double x) {
+  x += dpp_f64<0x128>(x);   // row_ror:8
+  x += dpp_f64<0x124>(x);   // row_ror:4
+  x += dpp_f64<0x122>(x);   // row_ror:2
+  x += dpp_f64<0x121>(x);   // row_ror:1
+  x = swap_add_f64<false>(x);
+  return swap_add_f64<true>(x);
+}
+
+// Exact bf16 -> fp64 via fp32: a bf16 value is an fp32 value whose low 16
+// bits are zero (normal or subnormal), and fp32 -> fp64 is exact.
+__device__ __forceinline__ double bf16_lo_f64(uint32_t pair) {
+  return static_cast<double>(__uint_as_float(pair << 16));
+}
+__device__ __forceinline__ double bf16_hi_f64(uint32_t pair) {
+  return static_cast<double>(__uint_as_float(pair & 0xFFFF0000u));
+}
+
+// lane 0's value as a wave-uniform double
+__device__ __forceinline__ double uniform_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Exact sign bit of sum_c key[c] * s[c] for one (key, coordinate): lane l
+// holds channels 2l and 2l+1 of both as bf16 pairs.  The 128 products are
+// exact in fp64; pair_sum adds them in a 7-level tree, so
+// |sum - exact| <= 7 * 2^-53 * sum|p| < 2^-50 * bnd for any bnd >= sum|p|,
+// such as ||k|| max_i ||s_i|| (Cauchy-Schwarz).  decide() takes the bit when
+// |sum| > 2^-49 * bnd and otherwise asks the exact integer accumulator.
+__device__ __forceinline__ double pair_sum(uint32_t kpair, uint32_t spair) {
+  const double p = bf16_lo_f64(kpair) * bf16_lo_f64(spair) + bf16_hi_f64(kpair) * bf16_hi_f64(spair);
+  return wave_sum_f64_dpp(p);
+}
+__device__ bool decide(double sum, double bnd, uint32_t kpair, uint32_t spair, const uint16_t* key_row,
+                       const uint16_t* s_row, uint32_t* scratch, int lane) {
+  if (!(bnd < INFINITY)) {
+    // the key norm left the fp32 range: bound from the magnitudes instead
+    const double m = __builtin_fabs(bf16_lo_f64(kpair) * bf16_lo_f64(spair)) +
+                     __builtin_fabs(bf16_hi_f64(kpair) * bf16_hi_f64(spair));
+    bnd = uniform_f64(wave_sum_f64_dpp(m)) * (1.0 + 0x1.0p-40);
+  }
+  if (__builtin_fabs(sum) > 0x1.0p-49 * bnd) return sum > 0.0;
+  bool b = false;
+  if (lane == 0) b = exact_sign_long(key_row, s_row, scratch);
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(b)) != 0;
 }
 
 // Norm of a key whose fp32 sum of squares under- or overflowed: scale by a
@@ -150,6 +227,12 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TILE_LDS];
   __shared__ uint32_t long_scratch[W][2 * ACC_WORDS];
+  // Sign words with bits to certify, queued per wave for an exact fix after
+  // the last tile: {row lo, row hi | half << 31, word, flags}.  The fixes
+  // then issue their loads in batches instead of one round trip each.
+  __shared__ uint4 fixq[W][QCAP];
+  __shared__ float fixn[W][QCAP];   // upper bound of ||k|| of the entry's key
+  int qn = 0;   // queued entries of this wave (uniform)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,10 +277,11 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     __syncthreads();
     if (tile + static_cast<int>(gridDim.x) < ntiles) load_tile(tile + gridDim.x);
 
-    for (int nb = 0; nb < NBLK; ++nb) {
-      // ---- projection on the matrix cores, norm from the same fragments ----
-      f32x16_t acc0 = {}, acc1 = {};
-      float n2 = 0.f;
+    // ---- projection on the matrix cores, norm from the same fragments ----
+    auto project = [&](int nb, f32x16_t& acc0, f32x16_t& acc1, float& n2) {
+      acc0 = f32x16_t{};
+      acc1 = f32x16_t{};
+      float n2a = 0.f, n2b = 0.f, n2c = 0.f, n2d = 0.f;
       const uint8_t* krow = tl + (nb * KB + j) * LDS_ROW + 16 * half;
   #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -205,12 +289,17 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
         const bf16x8_t bf = as_bf16x8(bv);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], bf, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], bf, acc1, 0, 0, 0);
-        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.x), as_bf16x2(bv.x), n2, false);
-        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.y), as_bf16x2(bv.y), n2, false);
-        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.z), as_bf16x2(bv.z), n2, false);
-        n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.w), as_bf16x2(bv.w), n2, false);
+        n2a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.x), as_bf16x2(bv.x), n2a, false);
+        n2b = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.y), as_bf16x2(bv.y), n2b, false);
+        n2c = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.z), as_bf16x2(bv.z), n2c, false);
+        n2d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.w), as_bf16x2(bv.w), n2d, false);
       }
+      n2 = (n2a + n2b) + (n2c + n2d);
       n2 += __shfl_xor(n2, 32);
+    };
+
+    // ---- bits of one block: signs, certification, stores ----
+    auto process = [&](int nb, const f32x16_t& acc0, const f32x16_t& acc1, float n2) {
 
       // ---- certification threshold for this lane's key ----
       // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
@@ -218,63 +307,79 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       const float knorm_up = __builtin_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f));
       const float tau = __builtin_fmaf(c1 * knorm_up, smax, c2);
 
-      // ---- sign and flag words, highest coordinate shifted in first ----
-      uint32_t sw = 0, fw = 0;
+      // ---- sign word, highest coordinate shifted in first ----
+      uint32_t sw = 0;
+      float amin = __builtin_fabsf(acc0[0]);
   #pragma unroll
       for (int r = 15; r >= 0; --r) {
         sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc1[r]), 31);
-        fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
+        amin = fminf(amin, __builtin_fabsf(acc1[r]));
       }
   #pragma unroll
       for (int r = 15; r >= 0; --r) {
         sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc0[r]), 31);
-        fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
+        amin = fminf(amin, __builtin_fabsf(acc0[r]));
       }
       uint32_t word = ~sw;
-      uint32_t flags = ~fw;
+      // ---- flag word (|acc| <= tau), only when some lane of the wave has one ----
+      uint32_t flags = 0;
+      if (__ballot(amin <= tau) != 0) {
+        uint32_t fw = 0;
+  #pragma unroll
+        for (int r = 15; r >= 0; --r) fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
+  #pragma unroll
+        for (int r = 15; r >= 0; --r) fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
+        flags = ~fw;
+      }
       // keys so large that products can overflow fp32: certify every bit
       if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
       const int64_t r = static_cast<int64_t>(tile) * KT + nb * KB + j;
       if (r >= R) flags = 0;  // zero padding of a ragged last tile
 
-      // ---- exact re-evaluation of flagged (key, coordinate) pairs ----
-      uint64_t todo = __ballot(flags != 0);
-      while (todo) {
-        const int src = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        uint32_t fsrc = __shfl(flags, src);
-        const int jsrc = src & 31;
-        const int hsrc = src >> 5;
-        const uint16_t* key_lds = reinterpret_cast<const uint16_t*>(tl + (nb * KB + jsrc) * LDS_ROW);
-        const uint32_t kpair = reinterpret_cast<const uint32_t*>(key_lds)[lane];
-        if (__ballot((kpair & 0x7FFF7FFFu) != 0) == 0) {
-          // the key is all (+/-) zeros: every projection is exactly 0 -> bit 1
-          if (lane == src) word |= fsrc;
-          continue;
-        }
-        while (fsrc) {
-          const int p = __builtin_ctz(fsrc);
-          fsrc &= fsrc - 1;
-          const int coord = cb + 32 * hsrc + p;
-          const uint16_t* s_row = s_md + static_cast<int64_t>(coord) * D;
-          const uint32_t spair = reinterpret_cast<const uint32_t*>(s_row)[lane];
-          // 128 products split two per lane; each is exact in fp64.
-          const double p0 = bf16_to_f64(kpair & 0xFFFF) * bf16_to_f64(spair & 0xFFFF);
-          const double p1 = bf16_to_f64(kpair >> 16) * bf16_to_f64(spair >> 16);
-          // 7-level tree: |sum - exact| <= 7 * 2^-53 * sum|p| (+ rounding of asum)
-          const double sum = __shfl(wave_sum_f64(p0 + p1), 0);
-          const double asum = __shfl(wave_sum_f64(__builtin_fabs(p0) + __builtin_fabs(p1)), 0);
-          bool bit;
-          if (asum == 0.0) {
-            bit = true;
-          } else if (__builtin_fabs(sum) > 0x1.0p-47 * asum) {
-            bit = sum > 0.0;
-          } else {
-            bool b = false;
-            if (lane == 0) b = exact_sign_long(key_lds, s_row, long_scratch[wave]);
-            bit = __shfl(static_cast<int>(b), 0) != 0;
+      // ---- flagged words: queued for the exact fix after the last tile, or
+      // (queue full) fixed here, one (key, coordinate) pair at a time ----
+      const uint64_t need = __ballot(flags != 0);
+      bool deferred = false;
+      if (need) {
+        const int cnt = __popcll(need);
+        if (qn + cnt <= QCAP) {
+          if (flags != 0) {
+            const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                      static_cast<uint32_t>(need >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(need), 0u)));
+            fixq[wave][slot] = make_uint4(static_cast<uint32_t>(r),
+                                          static_cast<uint32_t>(r >> 32) | (static_cast<uint32_t>(half) << 31),
+                                          word, flags);
+            fixn[wave][slot] = knorm_up;
+            deferred = true;
           }
-          if (lane == src) word = bit ? (word | (1u << p)) : (word & ~(1u << p));
+          qn += cnt;
+        } else {
+          uint64_t todo = need;
+          while (todo) {
+            const int src = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            uint32_t fsrc = __shfl(flags, src);
+            const int jsrc = src & 31;
+            const int hsrc = src >> 5;
+            const uint16_t* key_lds = reinterpret_cast<const uint16_t*>(tl + (nb * KB + jsrc) * LDS_ROW);
+            const uint32_t kpair = reinterpret_cast<const uint32_t*>(key_lds)[lane];
+            if (__ballot((kpair & 0x7FFF7FFFu) != 0) == 0) {
+              // the key is all (+/-) zeros: every projection is exactly 0 -> bit 1
+              if (lane == src) word |= fsrc;
+              continue;
+            }
+            while (fsrc) {
+              const int p = __builtin_ctz(fsrc);
+              fsrc &= fsrc - 1;
+              const uint16_t* s_row = s_md + static_cast<int64_t>(cb + 32 * hsrc + p) * D;
+              const uint32_t spair = reinterpret_cast<const uint32_t*>(s_row)[lane];
+              const double bnd = static_cast<double>(__shfl(knorm_up, src)) * smax;
+              const bool bit = decide(uniform_f64(pair_sum(kpair, spair)), bnd, kpair, spair, key_lds, s_row,
+                                      long_scratch[wave], lane);
+              if (lane == src) word = bit ? (word | (1u << p)) : (word & ~(1u << p));
+            }
+          }
         }
       }
 
@@ -282,7 +387,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       if (r < R) {
         const int64_t bh = r / n;
         const int64_t dst = bh * cap + pos + (r - bh * n);
-        signs[dst * WPR + (cb >> 5) + half] = word;
+        if (!deferred) signs[dst * WPR + (cb >> 5) + half] = word;
         if (wave == 0 && half == 0) {
           float nrm = __builtin_sqrtf(n2);
           if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) {
@@ -291,8 +396,90 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
           norms[dst] = nrm;
         }
       }
+    };
+
+    // Software pipeline over the blocks of the tile: the next block's matrix
+    // products are issued before this block's bit extraction, so they run
+    // while it executes.
+    f32x16_t c0, c1, d0, d1;
+    float cn2, dn2;
+    project(0, c0, c1, cn2);
+  #pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb) {
+      if (nb + 1 < NBLK) project(nb + 1, d0, d1, dn2);
+      process(nb, c0, c1, cn2);
+      c0 = d0;
+      c1 = d1;
+      cn2 = dn2;
     }
     buf ^= 1;
+  }
+
+  // ---- deferred exact fixes.  Lane e holds queue entry e (QCAP <= 64).
+  // Entries go FIXB at a time; each pass decides the lowest flagged bit of
+  // every entry of the group, with all key and S^T row loads issued together
+  // and the tree sums interleaved. ----
+  if (qn > 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint4 ent = lane < qn ? fixq[wave][lane] : make_uint4(0, 0, 0, 0);
+    const float knu = lane < qn ? fixn[wave][lane] : 0.f;
+    uint32_t qword = ent.z;
+    uint32_t qflags = ent.w;
+    for (int base = 0; base < qn; base += FIXB) {
+      for (;;) {
+        uint32_t fl[FIXB];
+        uint32_t any = 0;
+#pragma unroll
+        for (int i = 0; i < FIXB; ++i) {
+          fl[i] = base + i < qn ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(qflags), base + i)) : 0u;
+          any |= fl[i];
+        }
+        if (any == 0) break;
+        uint32_t kp[FIXB], sp[FIXB];
+        const uint16_t* krow[FIXB];
+        const uint16_t* srow[FIXB];
+#pragma unroll
+        for (int i = 0; i < FIXB; ++i) {   // every slot loads (the last entry if past the end): no branches
+          const int e = min(base + i, qn - 1);
+          const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ent.x), e));
+          const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ent.y), e));
+          const int64_t r = static_cast<int64_t>(lo) | (static_cast<int64_t>(hi & 0x7FFFFFFFu) << 32);
+          const int bitp = fl[i] ? __builtin_ctz(fl[i]) : 0;
+          krow[i] = keys + r * D;
+          srow[i] = s_md + static_cast<int64_t>(cb + 32 * static_cast<int>(hi >> 31) + bitp) * D;
+          kp[i] = reinterpret_cast<const uint32_t*>(krow[i])[lane];
+          sp[i] = reinterpret_cast<const uint32_t*>(srow[i])[lane];
+        }
+        double sums[FIXB];
+#pragma unroll
+        for (int i = 0; i < FIXB; ++i) sums[i] = pair_sum(kp[i], sp[i]);   // independent: interleaved
+#pragma unroll
+        for (int i = 0; i < FIXB; ++i) {
+          if (fl[i] == 0) continue;
+          const int e = base + i;
+          // all (+/-) zero keys project to exactly 0: bit 1
+          bool bit = true;
+          if (__ballot((kp[i] & 0x7FFF7FFFu) != 0) != 0) {
+            const float kn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(knu), e));
+            bit = decide(uniform_f64(sums[i]), static_cast<double>(kn) * smax, kp[i], sp[i], krow[i], srow[i],
+                         long_scratch[wave], lane);
+          }
+          if (lane == e) {
+            const uint32_t m = qflags & (0u - qflags);   // lowest flagged bit
+            qword = bit ? (qword | m) : (qword & ~m);
+            qflags &= qflags - 1;
+          }
+        }
+      }
+    }
+    if (lane < qn) {
+      const int64_t r = static_cast<int64_t>(ent.x) | (static_cast<int64_t>(ent.y & 0x7FFFFFFFu) << 32);
+      const int64_t bh = r / n;
+      const int64_t dst = bh * cap + pos + (r - bh * n);
+      signs[dst * WPR + (cb >> 5) + static_cast<int>(ent.y >> 31)] = qword;
+    }
   }
 }
 
