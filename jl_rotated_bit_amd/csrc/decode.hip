@@ -47,11 +47,6 @@ namespace qjl {
 namespace {
 
 constexpr int D = kHeadDim;
-#ifndef QJL_DECODE_WAVES
-#define QJL_DECODE_WAVES 4
-#endif
-constexpr int NW = QJL_DECODE_WAVES;   // waves per workgroup
-constexpr int NT = 64 * NW;
 constexpr int TILE = 64;         // tokens per wave per step (4 blocks of 16)
 constexpr int HALF = 32;         // tokens per P.V matrix step (MFMA K)
 constexpr int VCH = TILE * D * 2 / 16 / 64;  // 16-byte value chunks per lane per tile (16)
@@ -193,8 +188,9 @@ __device__ __forceinline__ int reduce_scatter4(int x0, int x1, int x2, int x3) {
   return static_cast<int>(c[0] + c[1]);
 }
 
-template <int M, int G>
+template <int M, int G, int NW>
 struct DecodeLds {
+  static constexpr int NT = 64 * NW;
   static constexpr int NSQ = (3 * G + 15) / 16;      // 16-column sets of limb columns
   static constexpr int LROW = M + 16;                // bytes per limb row (padded)
   static constexpr int LIMB_BYTES = 16 * NSQ * LROW; // rows = limb * G + head; others zero
@@ -215,14 +211,15 @@ struct DecodeLds {
   static constexpr int TOTAL = VB_BYTES + LIMB_BYTES + P_BYTES;
 };
 
-template <int M, int G>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
+template <int M, int G, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     const float* __restrict__ q, const uint32_t* __restrict__ signs,
     const float* __restrict__ norms, const uint16_t* __restrict__ values,
     const uint16_t* __restrict__ s_frag, float cnmax, int H_kv, int N, int cap, int n_split,
     int tps, float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
     float* __restrict__ part_acc, float* __restrict__ part_ml) {
-  using L = DecodeLds<M, G>;
+  using L = DecodeLds<M, G, NW>;
+  constexpr int NT = 64 * NW;
   constexpr int WPR = M / 32;        // sign words per token
   constexpr int CW = M / 128;        // sign words per lane per 16-token block
   constexpr int KS = M / 64;         // score k-steps of 64 coordinates
@@ -849,8 +846,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void de
   if (tid == 0) __hip_atomic_store(&counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int M, int G>
-int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float* q,
+template <int M, int G, int NW>
+int launch_decode_mgw(const DeviceSketch& s, const DecodePlan& plan, const float* q,
                      const uint32_t* signs, const float* norms, const void* values, int B,
                      int H_kv, int N, int cap, float coef, float* out, void* workspace,
                      hipStream_t stream) {
@@ -859,10 +856,20 @@ int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float*
   float* part_acc = reinterpret_cast<float*>(ws + plan.counter_bytes);
   float* part_ml = part_acc + static_cast<size_t>(B) * H_kv * G * plan.n_split * D;
   dim3 grid(plan.n_split, H_kv, B);
-  hipLaunchKernelGGL((decode_kernel<M, G>), grid, dim3(NT), 0, stream, q, signs, norms,
+  hipLaunchKernelGGL((decode_kernel<M, G, NW>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
                      static_cast<const uint16_t*>(values), s.s_frag, s.col_norm_all, H_kv, N, cap,
                      plan.n_split, plan.tokens_per_split, coef, out, counters, part_acc, part_ml);
   return hipGetLastError();
+}
+
+template <int M, int G>
+int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float* q,
+                     const uint32_t* signs, const float* norms, const void* values, int B,
+                     int H_kv, int N, int cap, float coef, float* out, void* workspace,
+                     hipStream_t stream) {
+  if (plan.waves == 8)
+    return launch_decode_mgw<M, G, 8>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, stream);
+  return launch_decode_mgw<M, G, 4>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, stream);
 }
 
 template <int M>
@@ -881,23 +888,41 @@ int launch_decode_m(int G, const DeviceSketch& s, const DecodePlan& plan, const 
 
 }  // namespace
 
+namespace {
+// Context splits for workgroups of nw waves: about 2048 / nw workgroups
+// (every compute unit busy), at least one full step (nw x 64 tokens) per
+// split, splits only for few streams.
+void split_plan(int64_t streams, int N, int nw, int64_t* n_split, int64_t* tps) {
+  const int64_t target = 2048 / nw;
+  const int min_tokens = nw * TILE;
+  int64_t want = (target + streams - 1) / streams;
+  if (streams > kMaxCounters) want = 1;   // splits (and counters) only for few streams
+  const int64_t most = (N + min_tokens - 1) / min_tokens;
+  if (want > most) want = most;
+  if (want > MAX_SPLITS) want = MAX_SPLITS;
+  if (want < 1) want = 1;
+  int64_t t = (N + want - 1) / want;
+  t = (t + TILE - 1) / TILE * TILE;
+  *tps = t;
+  *n_split = (N + t - 1) / t;
+}
+}  // namespace
+
 bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan* plan) {
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || N <= 0 || d != D || (m != 256 && m != 512)) return false;
   if (H_q % H_kv) return false;
   const int64_t streams = static_cast<int64_t>(B) * H_kv;
-  // Aim for about two workgroups per compute unit (256 CUs) while keeping at
-  // least one full step (4 waves x 64 tokens) per split.
-  constexpr int64_t kTargetWorkgroups = 2048 / NW;
-  constexpr int kMinTokens = NW * TILE;
-  int64_t want = (kTargetWorkgroups + streams - 1) / streams;
-  if (streams > kMaxCounters) want = 1;   // splits (and counters) only for few streams
-  const int64_t most = (N + kMinTokens - 1) / kMinTokens;
-  if (want > most) want = most;
-  if (want > MAX_SPLITS) want = MAX_SPLITS;
-  if (want < 1) want = 1;
-  int64_t tps = (N + want - 1) / want;
-  tps = (tps + TILE - 1) / TILE * TILE;
-  const int64_t n_split = (N + tps - 1) / tps;
+  // Eight-wave workgroups (one per compute unit) when the context must be
+  // split and that still fills the chip: half the S^T fragment traffic per
+  // compute unit and half the partials to merge.  Otherwise four waves.
+  int64_t n_split = 0, tps = 0;
+  split_plan(streams, N, 8, &n_split, &tps);
+  int waves = 8;
+  if (!(n_split > 1 && streams * n_split >= 224)) {
+    waves = 4;
+    split_plan(streams, N, 4, &n_split, &tps);
+  }
+  plan->waves = waves;
   plan->n_split = static_cast<int>(n_split);
   plan->tokens_per_split = static_cast<int>(tps);
   // A fixed-size counter region keeps the counters of every plan clear of the

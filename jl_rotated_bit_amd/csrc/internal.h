@@ -33,6 +33,7 @@ constexpr int64_t kMaxCounters = kCounterRegionBytes / 4;
 
 // Decode split geometry, shared by the workspace query and the launch.
 struct DecodePlan {
+  int waves = 4;            // waves per workgroup (4 or 8)
   int n_split = 0;          // context splits per (batch, kv head)
   int tokens_per_split = 0; // multiple of the token tile
   size_t counter_bytes = 0; // kCounterRegionBytes

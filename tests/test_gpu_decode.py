@@ -131,6 +131,21 @@ def test_shapes_ragged(gpu_lib, m, G, N, cap):
     check_decode(gpu_lib, q, words, norms, values, N, m, label=f"ragged G={G}")
 
 
+@pytest.mark.parametrize("m", [256, 512])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_eight_wave_workgroups(gpu_lib, m, G):
+    """Few streams with a long context take the eight-wave workgroups (29
+    splits here; four-wave workgroups would use 52), for every G and m."""
+    rng = np.random.default_rng(500 + 10 * G + m)
+    B, Hkv, d, N, cap = 1, 8, 128, 16421, 16432
+    assert gpu_lib.decode_num_splits(B, Hkv * G, Hkv, N, d, m) == 29
+    keys = wl.gaussian_keys(rng, B * Hkv * cap, scale=2.0).reshape(B, Hkv, cap, d)
+    values = wl.gaussian_keys(rng, B * Hkv * cap).reshape(B, Hkv, cap, d)
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    words, norms = oracle_cache(keys, m)
+    check_decode(gpu_lib, q, words, norms, values, N, m, label=f"eight waves G={G}")
+
+
 def test_unused_cache_rows_are_not_read(gpu_lib):
     rng = np.random.default_rng(8)
     B, Hkv, G, cap, N, m = 1, 2, 4, 3000, 2049, 256
