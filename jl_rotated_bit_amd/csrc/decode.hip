@@ -12,7 +12,8 @@
 //
 // Kernel design.  The step is bound by HBM: per (token, kv head) it reads m/8
 // bytes of sign words, 4 bytes of norm and 2d bytes of bf16 values.
-// * Grid = (context split, kv head, batch).  A workgroup (4 waves) serves the
+// * Grid = (context split, kv head, batch).  A workgroup (4 waves, or 8
+//   when the context is split and the grid still fills the chip) serves the
 //   G query heads of one kv head over one token range.
 // * Prologue: q is split once per workgroup into three bf16 parts; S^T q for
 //   the G heads runs on the matrix cores (fp32 accumulation).  Each head's
@@ -34,7 +35,8 @@
 // * Epilogue: waves merge in LDS; the workgroup stores its partial
 //   (max, sum, acc) per head with coherent stores; the last workgroup of a
 //   (batch, kv head) to arrive (atomic counter) merges all splits by
-//   log-sum-exp and writes out, then returns the counter to zero.
+//   log-sum-exp (reading the partials with coherent loads, no cache
+//   invalidation) and writes out, then returns the counter to zero.
 
 #include <hip/hip_runtime.h>
 
@@ -302,9 +304,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   int t0 = t_begin + wave * TILE;
 
   // ---- prologue ----
-  // q (straight into the split entries), the S^T fragments and the first
-  // tile are requested in that order; memory counters drain in order, so
-  // waiting for q and S^T leaves the tile loads in flight.
+  // q (straight into the split entries) and the S^T fragments are requested
+  // first; the first tile is requested once q is split, so that q does not
+  // queue behind the whole chip's tile traffic.  Memory counters drain in
+  // order, so S^T q waits for the fragments only and leaves the tile loads
+  // in flight.
   constexpr int NBLK = M / 32;            // blocks of 32 sketch coordinates
   constexpr int BPW = NBLK / NW;          // blocks per wave
   static_assert(NBLK % NW == 0, "sketch blocks must divide among the waves");
@@ -336,11 +340,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int st = 0; st < 8; ++st) af[bb][st] = fr[st * 64];
   }
-  load_signs(t0, sw, nv);
-  load_values(t0, std::integral_constant<int, 0>{});
-  // with m = 512 the S^T fragments fill half the registers: the second half
-  // of the first tile's values is requested after S^T q
-  if constexpr (M == 256) load_values(t0, std::integral_constant<int, 1>{});
 
   // limb rows >= 3G and probability rows >= 2G stay zero; the sums of Q
   // start at zero
@@ -376,6 +375,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (c < G) qss[c * 16 + (e >> 5)] = ss;   // e >> 5 = 2 st + hf
   }
   __syncthreads();
+  load_signs(t0, sw, nv);
+  load_values(t0, std::integral_constant<int, 0>{});
+  // with m = 512 the S^T fragments fill half the registers: the second half
+  // of the first tile's values is requested after S^T q
+  if constexpr (M == 256) load_values(t0, std::integral_constant<int, 1>{});
 
   // quantization step 2^E of head h: 2^(E + 21) exceeds ||q_h|| max_i ||s_i||
   // (with margin for the rounding of S^T q and of the norm itself)
@@ -747,10 +751,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   __syncthreads();
   if (!is_last) return;
 
-  // Acquire for this workgroup only: drop stale cache lines, after which
-  // plain (vector) loads see the partials the other workgroups stored
-  // coherently.  Only the last workgroup of each (batch, kv head) pays it.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // The partials are read with device-coherent (sc1) loads, the load side of
+  // the coherent stores above: each reads the value at the device's
+  // coherence point, and every store it must see completed before its
+  // workgroup counted in, which happened before this workgroup's count
+  // returned.  No cache invalidation is needed (an acquire fence would drop
+  // the whole L2 of this XCD).
   // Threads own (head, 4 channels) pairs; with fewer pairs than threads the
   // splits are divided among REP replicas whose sums meet in LDS.  The
   // (max, sum) pairs and the first MCH partial accumulators of every thread
@@ -761,22 +767,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   float* ml_l = reinterpret_cast<float*>(vb_all);   // 2 * n_split * G floats
   float* wts = ml_l + L::ML_FLOATS;                 // n_split * G floats
   float4* rep_sum = reinterpret_cast<float4*>(wts + L::WT_FLOATS);
-  const float2* ml_src = reinterpret_cast<const float2*>(part_ml + bh * n_split * G * 2);
-  const float4* pa = reinterpret_cast<const float4*>(part_acc);
+  constexpr int kCoherent = 16;   // sc1: device-scope coherent access
+  const rsrc_t ml_rs = make_rsrc(part_ml + bh * n_split * G * 2, n_split * G * 8);
+  const rsrc_t pa_rs = make_rsrc(part_acc + bh * n_split * G * D, n_split * G * D * 4);
   constexpr int ML_PT = (MAX_SPLITS * G + NT - 1) / NT;
   float2 mlv[ML_PT];
 #pragma unroll
   for (int k = 0; k < ML_PT; ++k) {
     const int i = tid + k * NT;
-    if (i < n_split * G) mlv[k] = ml_src[i];
+    if (i < n_split * G) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(ml_rs, i * 8, 0, kCoherent);
+      mlv[k] = make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+    }
   }
   const int pr = tid % PAIRS, rep = tid / PAIRS;       // valid when tid < PAIRS * REP
   const int mg = pr / (D / 4), c4 = pr % (D / 4);
+  auto load_partial = [&](int s_) {   // float4 c4 of head mg of split s_
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(pa_rs, ((s_ * G + mg) * (D / 4) + c4) * 16, 0, kCoherent);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  };
   float4 av[MCH];
 #pragma unroll
   for (int u = 0; u < MCH; ++u) {
     const int s = rep + u * REP;
-    if (tid < PAIRS * REP && s < n_split) av[u] = pa[((bh * n_split + s) * G + mg) * (D / 4) + c4];
+    if (tid < PAIRS * REP && s < n_split) av[u] = load_partial(s);
   }
 #pragma unroll
   for (int k = 0; k < ML_PT; ++k) {
@@ -815,7 +829,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     for (int s = rep + MCH * REP; s < n_split; s += REP) {   // splits beyond the first batch
-      const float4 v = pa[((bh * n_split + s) * G + mg) * (D / 4) + c4];
+      const float4 v = load_partial(s);
       const float wgt = wts[s * G + mg];
       o.x = __builtin_fmaf(wgt, v.x, o.x);
       o.y = __builtin_fmaf(wgt, v.y, o.y);
