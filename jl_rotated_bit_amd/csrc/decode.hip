@@ -309,9 +309,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // queue behind the whole chip's tile traffic.  Memory counters drain in
   // order, so S^T q waits for the fragments only and leaves the tile loads
   // in flight.
+  // S^T q runs on the first SQW waves only: with eight waves, the younger
+  // four would reach it only after their (lower-priority) tile requests,
+  // holding up the whole workgroup.
+  constexpr int SQW = NW < 4 ? NW : 4;
   constexpr int NBLK = M / 32;            // blocks of 32 sketch coordinates
-  constexpr int BPW = NBLK / NW;          // blocks per wave
-  static_assert(NBLK % NW == 0, "sketch blocks must divide among the waves");
+  constexpr int BPW = NBLK / SQW;         // blocks per S^T q wave
+  static_assert(NBLK % SQW == 0, "sketch blocks must divide among the waves");
   static_assert(8 * 2 * 32 % NT == 0, "q entries must divide among the threads");
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -333,9 +337,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // S^T comes in fragment order (see DeviceSketch::s_frag): the operand of
   // (block, k-step) is 64 lanes x 16 contiguous bytes, one 1 KB load.
   uint4 af[BPW][8];
+  if (wave < SQW)
 #pragma unroll
   for (int bb = 0; bb < BPW; ++bb) {
-    const int blk = wave + NW * bb;
+    const int blk = wave + SQW * bb;
     const uint4* fr = reinterpret_cast<const uint4*>(s_frag) + static_cast<int64_t>(blk) * 8 * 64 + lane;
 #pragma unroll
     for (int st = 0; st < 8; ++st) af[bb][st] = fr[st * 64];
@@ -403,12 +408,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // S^T q on the matrix cores, then its limbs.  Lane (col, half), register r
   // of block blk holds coordinate 32 blk + 8 (r/4) + 4 half + r%4.
-  {
+  if (wave < SQW) {
     const float inv_s = __builtin_ldexpf(1.0f, -e_h);
     int qsum = 0;
 #pragma unroll
     for (int bb = 0; bb < BPW; ++bb) {
-      const int blk = wave + NW * bb;
+      const int blk = wave + SQW * bb;
       f32x16_t acc = {};
 #pragma unroll
       for (int st = 0; st < 8; ++st)
@@ -685,18 +690,29 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // sits G/4 lane groups later in the same register; for G < 4 both rows are
   // registers of lanes 0..15.
   float* wacc = reinterpret_cast<float*>(vbuf);   // [G][D]
+  if constexpr (G >= 4) {
+    // a 16-lane (G = 4) or 32-lane (G = 8) row swap brings each lo row next
+    // to its hi row (VALU, no LDS round trip)
+    float v[NDB][4];
 #pragma unroll
-  for (int nb = 0; nb < NDB; ++nb) {
+    for (int nb = 0; nb < NDB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (G >= 4) {
-        const float v = acc[nb][r] + __shfl(acc[nb][r], (lane + 16 * (G / 4)) & 63);
-        const int row = 4 * grp + r;
-        if (row < G) wacc[row * D + 16 * nb + l16] = v;
-      } else if (r < G) {
-        if (grp == 0) wacc[r * D + 16 * nb + l16] = acc[nb][r] + acc[nb][(r + G) & 3];
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t x = __float_as_uint(acc[nb][r]);
+        const auto t = G == 4 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                              : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        v[nb][r] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
       }
-    }
+    if (grp < G / 4)
+#pragma unroll
+      for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wacc[(4 * grp + r) * D + 16 * nb + l16] = v[nb][r];
+  } else if (grp == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+      for (int r = 0; r < G; ++r) wacc[r * D + 16 * nb + l16] = acc[nb][r] + acc[nb][r + G];
   }
   if (lane == 0) {
 #pragma unroll
