@@ -108,6 +108,21 @@ __device__ __attribute__((noinline)) bool exact_sign_long(const uint16_t* key_ld
   return true;  // exact zero: sign(0) = +1
 }
 
+// DPP move of a float with every lane enabled and no old value (the
+// compiler folds it into the consuming add)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// lane src's pointer, as a wave-uniform value
+__device__ __forceinline__ const uint16_t* readlane_ptr(const uint16_t* p, int src) {
+  const uint64_t u = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), src));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), src));
+  return reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // The same pairwise tree over the 64 lanes, through DPP row rotations and
 // 16-/32-lane row swaps (VALU only, no LDS round trips): every lane ends
 // with the sum of all 64 inputs, formed with 6 levels of additions.
@@ -214,22 +229,64 @@ __device__ float scaled_norm(const uint16_t* key_lds) {
   return __builtin_ldexpf(__builtin_sqrtf(s), e);
 }
 
+// Sign of sum_c key[c] * s[c] for one (key, coordinate) in one lane: kr
+// holds the key's 128 bf16 values, s_row points at the sketch row.  Every
+// product of two bf16 values is exact in fp64; four running sums of 32
+// products each and their total form a summation tree of height 34, so the
+// result is off by at most 34 * 2^-53 * sum|p| < 2^-47 * bnd for any
+// bnd >= sum|p| (such as ||k|| max_i ||s_i||, by Cauchy-Schwarz).  Returns
+// the bit (1 for a positive sum) when |sum| > 2^-46 * bnd, else -1.
+// (Each 8-product group's conversions stay next to its products; hoisted,
+// the 256 doubles would not fit in registers.)
+__device__ __forceinline__ int serial_sign(const uint4 (&kr)[D / 8], const uint4* s_row, double bnd) {
+  uint4 sv[D / 8];
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) sv[i] = s_row[i];
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  double mag = 0.0;
+  const bool need_mag = !(bnd < INFINITY);   // the key norm left the fp32 range
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+    // opaque to the optimizer: the caller loops over bits with kr fixed, and
+    // hoisting these conversions out of that loop would need 256 doubles
+    asm volatile("" : "+v"(kw[0]), "+v"(kw[1]), "+v"(kw[2]), "+v"(kw[3]));
+    const uint32_t sw[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const double p0 = bf16_lo_f64(kw[u]) * bf16_lo_f64(sw[u]);
+      const double p1 = bf16_hi_f64(kw[u]) * bf16_hi_f64(sw[u]);
+      acc[u] += p0;
+      acc[u] += p1;
+      if (need_mag) mag += __builtin_fabs(p0) + __builtin_fabs(p1);
+    }
+  }
+  const double sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  // magnitude bound: sum|p| computed with relative error below 2^-46
+  if (need_mag) bnd = mag * (1.0 + 0x1.0p-40);
+  if (__builtin_fabs(sum) > 0x1.0p-46 * bnd) return sum > 0.0 ? 1 : 0;
+  return -1;
+}
+
 template <int M>
 __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2))) void encode_kernel(
     const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md,
     const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
-    float* __restrict__ norms, int64_t R, int n, int cap, int pos, int ntiles, float c1,
+    float* __restrict__ norms, int R, int n, int cap, int pos, int ntiles, float c1,
     float c2) {
   constexpr int W = M / CW;
   constexpr int NT = 64 * W;
   constexpr int LOADS = CHUNKS / NT;  // 16-byte loads per thread per tile
   constexpr int WPR = M / 32;         // words per key row
+  static_assert(NT % 16 == 0, "the 16 chunks of a key row must sit in one 16-lane row");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TILE_LDS];
+  __shared__ float n2buf[2][KT];   // squared key norms of the tile
   __shared__ uint32_t long_scratch[W][2 * ACC_WORDS];
   // Sign words with bits to certify, queued per wave for an exact fix after
-  // the last tile: {row lo, row hi | half << 31, word, flags}.  The fixes
-  // then issue their loads in batches instead of one round trip each.
+  // the last tile: {key row | half << 31, word, flags, 0}.  The fix then
+  // gives one entry to each lane, all loads in flight together.
   __shared__ uint4 fixq[W][QCAP];
   __shared__ float fixn[W][QCAP];   // upper bound of ||k|| of the entry's key
   int qn = 0;   // queued entries of this wave (uniform)
@@ -240,6 +297,8 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   const int half = lane >> 5;
   const int j = lane & 31;
   const int cb = wave * CW;
+  const uint32_t un = static_cast<uint32_t>(n);
+  const uint32_t uR = static_cast<uint32_t>(R);
 
   // Resident A operand: S^T rows for this wave's coordinates.  Block b, row i
   // holds coordinate cb + 32*((i >> 2) & 1) + 16*b + 4*(i >> 3) + (i & 3), so
@@ -255,13 +314,16 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   }
   const float smax = col_norm_max[wave];
 
+  // chunk c of a tile: key row c / 16, 16-byte column c % 16; the 16 chunks
+  // of a row belong to 16 consecutive threads (one DPP row)
   uint4 pf[LOADS];
   auto load_tile = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
       const int c = tid + k * NT;
-      const int64_t r = static_cast<int64_t>(tile) * KT + (c >> 4);
-      pf[k] = r < R ? reinterpret_cast<const uint4*>(keys + r * D)[c & 15] : make_uint4(0, 0, 0, 0);
+      const uint32_t r = static_cast<uint32_t>(tile) * KT + (c >> 4);
+      pf[k] = r < uR ? reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(r) * D)[c & 15]
+                     : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -269,6 +331,21 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   int buf = 0;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     uint8_t* tl = lds + buf * TILE_LDS;
+    // squared norms of the tile's keys, once per tile: each thread squares its
+    // chunks (bf16 dot2, fp32), a DPP row sum adds the 16 chunks of a key
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const uint4 v = pf[k];
+      float q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), 0.f, false);
+      q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), q, false);
+      q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(v.z), q, false);
+      q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(v.w), q, false);
+      q += dpp_f32<0x128>(q);   // row_ror:8
+      q += dpp_f32<0x124>(q);   // row_ror:4
+      q += dpp_f32<0x122>(q);   // row_ror:2
+      q += dpp_f32<0x121>(q);   // row_ror:1
+      if ((tid & 15) == 0) n2buf[buf][(tid >> 4) + k * (NT / 16)] = q;
+    }
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
       const int c = tid + k * NT;
@@ -276,31 +353,28 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     }
     __syncthreads();
     if (tile + static_cast<int>(gridDim.x) < ntiles) load_tile(tile + gridDim.x);
+    // (batch * head, position) of the tile's first key, once per tile (the
+    // host keeps the key count below 2^31)
+    const uint32_t tb = static_cast<uint32_t>(tile) * KT;
+    const uint32_t tbh = tb / un;
+    const uint32_t toff = tb - tbh * un;
 
-    // ---- projection on the matrix cores, norm from the same fragments ----
-    auto project = [&](int nb, f32x16_t& acc0, f32x16_t& acc1, float& n2) {
+    // ---- projection on the matrix cores ----
+    auto project = [&](int nb, f32x16_t& acc0, f32x16_t& acc1) {
       acc0 = f32x16_t{};
       acc1 = f32x16_t{};
-      float n2a = 0.f, n2b = 0.f, n2c = 0.f, n2d = 0.f;
       const uint8_t* krow = tl + (nb * KB + j) * LDS_ROW + 16 * half;
   #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const uint4 bv = *reinterpret_cast<const uint4*>(krow + 32 * s);
-        const bf16x8_t bf = as_bf16x8(bv);
+        const bf16x8_t bf = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32 * s));
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], bf, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], bf, acc1, 0, 0, 0);
-        n2a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.x), as_bf16x2(bv.x), n2a, false);
-        n2b = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.y), as_bf16x2(bv.y), n2b, false);
-        n2c = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.z), as_bf16x2(bv.z), n2c, false);
-        n2d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(bv.w), as_bf16x2(bv.w), n2d, false);
       }
-      n2 = (n2a + n2b) + (n2c + n2d);
-      n2 += __shfl_xor(n2, 32);
     };
 
     // ---- bits of one block: signs, certification, stores ----
-    auto process = [&](int nb, const f32x16_t& acc0, const f32x16_t& acc1, float n2) {
-
+    auto process = [&](int nb, const f32x16_t& acc0, const f32x16_t& acc1) {
+      const float n2 = n2buf[buf][nb * KB + j];
       // ---- certification threshold for this lane's key ----
       // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
       // squares plus squares lost below the fp32 normal range (with margin).
@@ -333,8 +407,22 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       }
       // keys so large that products can overflow fp32: certify every bit
       if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
-      const int64_t r = static_cast<int64_t>(tile) * KT + nb * KB + j;
-      if (r >= R) flags = 0;  // zero padding of a ragged last tile
+      const uint32_t r = tb + nb * KB + j;
+      const bool valid = r < uR;
+      if (!valid) flags = 0;  // zero padding of a ragged last tile
+      // destination row: (batch * head) = tbh + wraps, position = offset
+      uint32_t off = toff + nb * KB + j, bhl = tbh;
+      if (un > static_cast<uint32_t>(KT)) {   // at most one wrap within a tile
+        if (off >= un) {
+          off -= un;
+          ++bhl;
+        }
+      } else {
+        const uint32_t w = off / un;
+        bhl += w;
+        off -= w * un;
+      }
+      const int64_t dst = static_cast<int64_t>(bhl) * cap + pos + off;
 
       // ---- flagged words: queued for the exact fix after the last tile, or
       // (queue full) fixed here, one (key, coordinate) pair at a time ----
@@ -347,9 +435,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
             const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
                                       static_cast<uint32_t>(need >> 32),
                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(need), 0u)));
-            fixq[wave][slot] = make_uint4(static_cast<uint32_t>(r),
-                                          static_cast<uint32_t>(r >> 32) | (static_cast<uint32_t>(half) << 31),
-                                          word, flags);
+            fixq[wave][slot] = make_uint4(r | (static_cast<uint32_t>(half) << 31), word, flags, 0u);
             fixn[wave][slot] = knorm_up;
             deferred = true;
           }
@@ -384,9 +470,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       }
 
       // ---- stores ----
-      if (r < R) {
-        const int64_t bh = r / n;
-        const int64_t dst = bh * cap + pos + (r - bh * n);
+      if (valid) {
         if (!deferred) signs[dst * WPR + (cb >> 5) + half] = word;
         if (wave == 0 && half == 0) {
           float nrm = __builtin_sqrtf(n2);
@@ -402,92 +486,83 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     // products are issued before this block's bit extraction, so they run
     // while it executes.
     f32x16_t c0, c1, d0, d1;
-    float cn2, dn2;
-    project(0, c0, c1, cn2);
+    project(0, c0, c1);
   #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) {
-      if (nb + 1 < NBLK) project(nb + 1, d0, d1, dn2);
-      process(nb, c0, c1, cn2);
+      if (nb + 1 < NBLK) project(nb + 1, d0, d1);
+      process(nb, c0, c1);
       c0 = d0;
       c1 = d1;
-      cn2 = dn2;
     }
     buf ^= 1;
   }
 
-  // ---- deferred exact fixes.  Lane e holds queue entry e (QCAP <= 64).
-  // Entries go FIXB at a time; each pass decides the lowest flagged bit of
-  // every entry of the group, with all key and S^T row loads issued together
-  // and the tree sums interleaved. ----
+  // ---- deferred exact fixes: lane e takes queue entry e (QCAP <= 64) and
+  // decides its flagged bits one per pass, lowest first, from its own loads
+  // of the key row and of the sketch row; the rare sums too close to zero
+  // for the fp64 bound go, one at a time, to the exact integer accumulator ----
   if (qn > 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint4 ent = lane < qn ? fixq[wave][lane] : make_uint4(0, 0, 0, 0);
-    const float knu = lane < qn ? fixn[wave][lane] : 0.f;
-    uint32_t qword = ent.z;
-    uint32_t qflags = ent.w;
-    for (int base = 0; base < qn; base += FIXB) {
-      for (;;) {
-        uint32_t fl[FIXB];
-        uint32_t any = 0;
+    const bool act = lane < qn;
+    const uint4 ent = act ? fixq[wave][lane] : make_uint4(0, 0, 0, 0);
+    const float knu = act ? fixn[wave][lane] : 0.f;
+    const uint32_t r = ent.x & 0x7FFFFFFFu;
+    const int hf = static_cast<int>(ent.x >> 31);
+    uint32_t word = ent.y;
+    uint32_t fl = ent.z;
+    const uint16_t* krow = keys + static_cast<int64_t>(r) * D;
+    uint4 kr[D / 8];
 #pragma unroll
-        for (int i = 0; i < FIXB; ++i) {
-          fl[i] = base + i < qn ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(qflags), base + i)) : 0u;
-          any |= fl[i];
-        }
-        if (any == 0) break;
-        uint32_t kp[FIXB], sp[FIXB];
-        const uint16_t* krow[FIXB];
-        const uint16_t* srow[FIXB];
+    for (int i = 0; i < D / 8; ++i) kr[i] = act ? reinterpret_cast<const uint4*>(krow)[i] : make_uint4(0, 0, 0, 0);
+    uint32_t nz = 0;
 #pragma unroll
-        for (int i = 0; i < FIXB; ++i) {   // every slot loads (the last entry if past the end): no branches
-          const int e = min(base + i, qn - 1);
-          const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ent.x), e));
-          const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ent.y), e));
-          const int64_t r = static_cast<int64_t>(lo) | (static_cast<int64_t>(hi & 0x7FFFFFFFu) << 32);
-          const int bitp = fl[i] ? __builtin_ctz(fl[i]) : 0;
-          krow[i] = keys + r * D;
-          srow[i] = s_md + static_cast<int64_t>(cb + 32 * static_cast<int>(hi >> 31) + bitp) * D;
-          kp[i] = reinterpret_cast<const uint32_t*>(krow[i])[lane];
-          sp[i] = reinterpret_cast<const uint32_t*>(srow[i])[lane];
-        }
-        double sums[FIXB];
-#pragma unroll
-        for (int i = 0; i < FIXB; ++i) sums[i] = pair_sum(kp[i], sp[i]);   // independent: interleaved
-#pragma unroll
-        for (int i = 0; i < FIXB; ++i) {
-          if (fl[i] == 0) continue;
-          const int e = base + i;
-          // all (+/-) zero keys project to exactly 0: bit 1
-          bool bit = true;
-          if (__ballot((kp[i] & 0x7FFF7FFFu) != 0) != 0) {
-            const float kn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(knu), e));
-            bit = decide(uniform_f64(sums[i]), static_cast<double>(kn) * smax, kp[i], sp[i], krow[i], srow[i],
-                         long_scratch[wave], lane);
-          }
-          if (lane == e) {
-            const uint32_t m = qflags & (0u - qflags);   // lowest flagged bit
-            qword = bit ? (qword | m) : (qword & ~m);
-            qflags &= qflags - 1;
-          }
-        }
+    for (int i = 0; i < D / 8; ++i) nz |= (kr[i].x | kr[i].y | kr[i].z | kr[i].w) & 0x7FFF7FFFu;
+    if (nz == 0) {   // an all (+/-) zero key projects to exactly 0: bit 1
+      word |= fl;
+      fl = 0;
+    }
+    const double bnd = static_cast<double>(knu) * smax;
+    uint32_t slow = 0;   // bits the fp64 sum could not decide
+    while (__ballot(fl != 0)) {
+      if (fl) {
+        const int p = __builtin_ctz(fl);
+        const uint16_t* srow = s_md + static_cast<int64_t>(cb + 32 * hf + p) * D;
+        const int bit = serial_sign(kr, reinterpret_cast<const uint4*>(srow), bnd);
+        if (bit < 0) slow |= 1u << p;
+        else word = bit ? (word | (1u << p)) : (word & ~(1u << p));
+        fl &= fl - 1;
       }
     }
-    if (lane < qn) {
-      const int64_t r = static_cast<int64_t>(ent.x) | (static_cast<int64_t>(ent.y & 0x7FFFFFFFu) << 32);
-      const int64_t bh = r / n;
-      const int64_t dst = bh * cap + pos + (r - bh * n);
-      signs[dst * WPR + (cb >> 5) + static_cast<int>(ent.y >> 31)] = qword;
+    // exact integer sums, one (key, coordinate) at a time on lane 0
+    for (uint64_t lanes = __ballot(slow != 0); lanes; lanes &= lanes - 1) {
+      const int src = __builtin_ctzll(lanes);
+      uint32_t bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slow), src));
+      const uint16_t* kp = readlane_ptr(krow, src);
+      const int hsrc = __builtin_amdgcn_readlane(hf, src);
+      while (bits) {
+        const int p = __builtin_ctz(bits);
+        bits &= bits - 1;
+        bool b = false;
+        if (lane == 0) b = exact_sign_long(kp, s_md + static_cast<int64_t>(cb + 32 * hsrc + p) * D, long_scratch[wave]);
+        b = __builtin_amdgcn_readfirstlane(static_cast<int>(b)) != 0;
+        if (lane == src) word = b ? (word | (1u << p)) : (word & ~(1u << p));
+      }
+    }
+    if (act) {
+      const uint32_t bh = r / un;
+      const int64_t dst = static_cast<int64_t>(bh) * cap + pos + (r - bh * un);
+      signs[dst * WPR + (cb >> 5) + hf] = word;
     }
   }
 }
 
 template <int M>
-int launch_encode_m(const DeviceSketch& s, const void* keys, int64_t R, int n, uint32_t* signs,
+int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
                     float* norms, int cap, int pos, hipStream_t stream) {
   constexpr int NT = 64 * (M / CW);
-  const int ntiles = static_cast<int>((R + KT - 1) / KT);
+  const int ntiles = static_cast<int>((static_cast<int64_t>(R) + KT - 1) / KT);
   static int max_grid = 0;  // resident workgroups on this device (fixed per template)
   if (max_grid == 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -516,9 +591,10 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
                   float* norms, int cap, int pos, void* stream) {
   const int64_t R = static_cast<int64_t>(B) * H_kv * n;
   if (R == 0) return hipSuccess;
+  if (R > INT32_MAX) return hipErrorInvalidValue;   // the kernel indexes keys in 32 bits
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (s.m == 256) return launch_encode_m<256>(s, keys, R, n, signs, norms, cap, pos, st);
-  return launch_encode_m<512>(s, keys, R, n, signs, norms, cap, pos, st);
+  if (s.m == 256) return launch_encode_m<256>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
+  return launch_encode_m<512>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
 }
 
 }  // namespace qjl

@@ -149,6 +149,9 @@ QJL_API qjl_status qjl_encode_keys(const void* keys_bf16, int32_t B, int32_t H_k
                 static_cast<long long>(pos) + n, cap);
   if (static_cast<int64_t>(B) * H_kv * cap > (int64_t{1} << 40))
     return fail(QJL_EINVAL, "qjl_encode_keys: cache too large");
+  if (static_cast<int64_t>(B) * H_kv * n > INT32_MAX)
+    return fail(QJL_EINVAL, "qjl_encode_keys: B*H_kv*n=%lld keys in one call (at most 2^31 - 1)",
+                static_cast<long long>(B) * H_kv * n);
   if (n == 0) return QJL_OK;
   if (keys_bf16 == nullptr || signs == nullptr || norms == nullptr)
     return fail(QJL_EINVAL, "qjl_encode_keys: NULL pointer");
