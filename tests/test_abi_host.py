@@ -88,6 +88,9 @@ def test_encode_validation(lib):
     assert enc(lib, pos=-1) == EINVAL
     assert enc(lib, n=5, pos=4, cap=8) == EINVAL
     assert "exceeds cap" in qjl.last_error()
+    # more than 2^31 - 1 keys in one call (rejected before any pointer is used)
+    assert enc(lib, B=2, H=2, n=1 << 29, cap=1 << 29) == EINVAL
+    assert "2^31" in qjl.last_error()
     assert enc(lib, keys=None) == EINVAL
     assert enc(lib, signs=None) == EINVAL
     assert enc(lib, norms=None) == EINVAL
