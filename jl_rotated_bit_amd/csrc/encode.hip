@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -56,17 +57,6 @@ constexpr int FIXB = 16;             // (word, bit) fixes per batch of loads
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
-
-// Exact bf16 -> fp64 built from the bit fields (no fp32 step, so bf16
-// subnormals are never flushed).
-__device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
-  const uint32_t e = (bits16 >> 7) & 0xFF;
-  const uint32_t f = bits16 & 0x7F;
-  const double v = e ? __longlong_as_double((static_cast<long long>(e + 896) << 52) |
-                                            (static_cast<long long>(f) << 45))
-                     : static_cast<double>(f) * 0x1.0p-133;
-  return (bits16 & 0x8000) ? -v : v;
-}
 
 // Adds v (< 2^48) << (32 * w) into a little-endian multiword integer in LDS.
 __device__ void long_add(uint32_t* acc, int w, uint64_t v) {
@@ -115,53 +105,6 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// lane src's pointer, as a wave-uniform value
-__device__ __forceinline__ const uint16_t* readlane_ptr(const uint16_t* p, int src) {
-  const uint64_t u = reinterpret_cast<uintptr_t>(p);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), src));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), src));
-  return reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// The same pairwise tree over the 64 lanes, through DPP row rotations and
-// 16-/32-lane row swaps (VALU only, no LDS round trips): every lane ends
-// with the sum of all 64 inputs, formed with 6 levels of additions.
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const uint64_t u = __double_as_longlong(x);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), CTRL, 0xF, 0xF, true);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, 0xF, 0xF, true);
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-}
-// x + (x of the lane 16 (WIDE: 32) lanes away): with both operands equal, a
-// row swap returns [x g0, x g0, x g2, x g2] and [x g1, x g1, x g3, x g3]
-// (16-lane groups g); their sum is the butterfly step in every lane.
-template <bool WIDE>
-__device__ __forceinline__ double swap_add_f64(double x) {
-  const uint64_t u = __double_as_longlong(x);
-  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
-  uint32_t l0, l1, h0, h1;
-  if constexpr (WIDE) {
-    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    const auto c = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    l0 = a[0]; l1 = a[1]; h0 = c[0]; h1 = c[1];
-  } else {
-    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    const auto c = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    l0 = a[0]; l1 = a[1]; h0 = c[0]; h1 = c[1];
-  }
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(h0) << 32) | l0)) +
-         __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(h1) << 32) | l1));
-}
-__device__ __forceinline__ double wave_sum_f64_dpp(double x) {
-  x += dpp_f64<0x128>(x);   // row_ror:8
-  x += dpp_f64<0x124>(x);   // row_ror:4
-  x += dpp_f64<0x122>(x);   // row_ror:2
-  x += dpp_f64<0x121>(x);   // row_ror:1
-  x = swap_add_f64<false>(x);
-  return swap_add_f64<true>(x);
-}
-
 // Exact bf16 -> fp64 via fp32: a bf16 value is an fp32 value whose low 16
 // bits are zero (normal or subnormal), and fp32 -> fp64 is exact.
 __device__ __forceinline__ double bf16_lo_f64(uint32_t pair) {
@@ -169,38 +112,6 @@ __device__ __forceinline__ double bf16_lo_f64(uint32_t pair) {
 }
 __device__ __forceinline__ double bf16_hi_f64(uint32_t pair) {
   return static_cast<double>(__uint_as_float(pair & 0xFFFF0000u));
-}
-
-// lane 0's value as a wave-uniform double
-__device__ __forceinline__ double uniform_f64(double x) {
-  const uint64_t u = __double_as_longlong(x);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-}
-
-// Exact sign bit of sum_c key[c] * s[c] for one (key, coordinate): lane l
-// holds channels 2l and 2l+1 of both as bf16 pairs.  The 128 products are
-// exact in fp64; pair_sum adds them in a 7-level tree, so
-// |sum - exact| <= 7 * 2^-53 * sum|p| < 2^-50 * bnd for any bnd >= sum|p|,
-// such as ||k|| max_i ||s_i|| (Cauchy-Schwarz).  decide() takes the bit when
-// |sum| > 2^-49 * bnd and otherwise asks the exact integer accumulator.
-__device__ __forceinline__ double pair_sum(uint32_t kpair, uint32_t spair) {
-  const double p = bf16_lo_f64(kpair) * bf16_lo_f64(spair) + bf16_hi_f64(kpair) * bf16_hi_f64(spair);
-  return wave_sum_f64_dpp(p);
-}
-__device__ bool decide(double sum, double bnd, uint32_t kpair, uint32_t spair, const uint16_t* key_row,
-                       const uint16_t* s_row, uint32_t* scratch, int lane) {
-  if (!(bnd < INFINITY)) {
-    // the key norm left the fp32 range: bound from the magnitudes instead
-    const double m = __builtin_fabs(bf16_lo_f64(kpair) * bf16_lo_f64(spair)) +
-                     __builtin_fabs(bf16_hi_f64(kpair) * bf16_hi_f64(spair));
-    bnd = uniform_f64(wave_sum_f64_dpp(m)) * (1.0 + 0x1.0p-40);
-  }
-  if (__builtin_fabs(sum) > 0x1.0p-49 * bnd) return sum > 0.0;
-  bool b = false;
-  if (lane == 0) b = exact_sign_long(key_row, s_row, scratch);
-  return __builtin_amdgcn_readfirstlane(static_cast<int>(b)) != 0;
 }
 
 // Norm of a key whose fp32 sum of squares under- or overflowed: scale by a
@@ -229,44 +140,146 @@ __device__ float scaled_norm(const uint16_t* key_lds) {
   return __builtin_ldexpf(__builtin_sqrtf(s), e);
 }
 
-// Sign of sum_c key[c] * s[c] for one (key, coordinate) in one lane: kr
-// holds the key's 128 bf16 values, s_row points at the sketch row.  Every
-// product of two bf16 values is exact in fp64; four running sums of 32
-// products each and their total form a summation tree of height 34, so the
-// result is off by at most 34 * 2^-53 * sum|p| < 2^-47 * bnd for any
-// bnd >= sum|p| (such as ||k|| max_i ||s_i||, by Cauchy-Schwarz).  Returns
-// the bit (1 for a positive sum) when |sum| > 2^-46 * bnd, else -1.
-// (Each 8-product group's conversions stay next to its products; hoisted,
-// the 256 doubles would not fit in registers.)
-__device__ __forceinline__ int serial_sign(const uint4 (&kr)[D / 8], const uint4* s_row, double bnd) {
-  uint4 sv[D / 8];
+// fp64 move across a 16-lane row through DPP (each half separately)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), CTRL, 0xF, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each half row
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+// Sum over a 16-lane row: mirror, half-mirror, then quad swaps.  Every step
+// adds a lane's value to its partner's and the partner adds the same two
+// numbers, so all 16 lanes end with bit-identical totals (tree height 4).
+__device__ __forceinline__ double row_sum_f64(double x) {
+  x += dpp_f64<kRowMirror>(x);
+  x += dpp_f64<kRowHalfMirror>(x);
+  x += dpp_f64<kQuadXor2>(x);
+  x += dpp_f64<kQuadXor1>(x);
+  return x;
+}
+__device__ __forceinline__ uint32_t row_or(uint32_t x) {
+  x |= __builtin_amdgcn_update_dpp(0u, x, kRowMirror, 0xF, 0xF, true);
+  x |= __builtin_amdgcn_update_dpp(0u, x, kRowHalfMirror, 0xF, 0xF, true);
+  x |= __builtin_amdgcn_update_dpp(0u, x, kQuadXor2, 0xF, 0xF, true);
+  x |= __builtin_amdgcn_update_dpp(0u, x, kQuadXor1, 0xF, 0xF, true);
+  return x;
+}
+
+// Exact-sign evaluation of queued sign words (the words whose flagged bits
+// the fp32 projection could not certify).  Sixteen lanes serve one entry:
+// lane (group g, sub c) loads 16 bytes (channels 8c .. 8c+7) of the key row
+// and of the sketch row, so every load instruction reads four whole rows.
+// The eight products of a lane are exact in fp64 and are added in order,
+// then row_sum_f64 adds the 16 lanes: a summation tree of height 11, off by
+// at most 11 * 2^-53 * sum|p| < 2^-49 * bnd for any bnd >= sum|p| (such as
+// ||k|| max_i ||s_i||, Cauchy-Schwarz).  The bit is the sign of the sum when
+// |sum| > 2^-46 * bnd; the rare sums below that go, one at a time, to the
+// exact integer accumulator.  RU rounds of four entries have their loads in
+// flight together; flagged bits of an entry are taken one pass each, lowest
+// first.  fq/fk: the queue ({key row | half << 31, word, flags, -}, norm
+// bound); the decided words are stored to their rows.
+template <int RU>
+__device__ __forceinline__ void fix_queue(const uint4* fq, const float* fk, int qn, const uint16_t* keys,
+                                          const uint16_t* s_md, int cb, float smax, uint32_t* signs,
+                                          uint32_t un, int cap, int pos, int wpr, uint32_t* scratch,
+                                          int lane) {
+  const int g = lane >> 4, sub = lane & 15;
+  for (int base = 0; base < qn; base += 4 * RU) {
+    uint4 kc[RU], sc[RU];
+    uint32_t word[RU], fl[RU], row[RU], slow[RU];
+    int hf[RU], p[RU];
+    double bnd[RU];
 #pragma unroll
-  for (int i = 0; i < D / 8; ++i) sv[i] = s_row[i];
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  double mag = 0.0;
-  const bool need_mag = !(bnd < INFINITY);   // the key norm left the fp32 range
+    for (int t = 0; t < RU; ++t) {
+      const int e = base + 4 * t + g;
+      const bool act = e < qn;
+      const uint4 ent = act ? fq[e] : make_uint4(0, 0, 0, 0);
+      row[t] = ent.x & 0x7FFFFFFFu;
+      hf[t] = static_cast<int>(ent.x >> 31);
+      word[t] = ent.y;
+      fl[t] = ent.z;   // zero for inactive entries
+      bnd[t] = act ? static_cast<double>(fk[e]) * smax : 0.0;
+      p[t] = fl[t] ? __builtin_ctz(fl[t]) : 0;
+      slow[t] = 0;
+      kc[t] = act ? reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(row[t]) * D)[sub]
+                  : make_uint4(0, 0, 0, 0);
+      sc[t] = fl[t] ? reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(cb + 32 * hf[t] + p[t]) * D)[sub]
+                    : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-  for (int i = 0; i < D / 8; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-    // opaque to the optimizer: the caller loops over bits with kr fixed, and
-    // hoisting these conversions out of that loop would need 256 doubles
-    asm volatile("" : "+v"(kw[0]), "+v"(kw[1]), "+v"(kw[2]), "+v"(kw[3]));
-    const uint32_t sw[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
+    for (int t = 0; t < RU; ++t) {   // an all (+/-) zero key projects to exactly 0: bit 1
+      if (row_or((kc[t].x | kc[t].y | kc[t].z | kc[t].w) & 0x7FFF7FFFu) == 0) {
+        word[t] |= fl[t];
+        fl[t] = 0;
+      }
+    }
+    for (;;) {
+      uint32_t any = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const double p0 = bf16_lo_f64(kw[u]) * bf16_lo_f64(sw[u]);
-      const double p1 = bf16_hi_f64(kw[u]) * bf16_hi_f64(sw[u]);
-      acc[u] += p0;
-      acc[u] += p1;
-      if (need_mag) mag += __builtin_fabs(p0) + __builtin_fabs(p1);
+      for (int t = 0; t < RU; ++t) any |= fl[t];
+      if (__ballot(any != 0) == 0) break;
+#pragma unroll
+      for (int t = 0; t < RU; ++t) {
+        if (fl[t] == 0) continue;   // uniform over the entry's 16 lanes
+        const uint32_t kw[4] = {kc[t].x, kc[t].y, kc[t].z, kc[t].w};
+        const uint32_t sw[4] = {sc[t].x, sc[t].y, sc[t].z, sc[t].w};
+        double acc = 0.0, mag = 0.0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const double p0 = bf16_lo_f64(kw[u]) * bf16_lo_f64(sw[u]);
+          const double p1 = bf16_hi_f64(kw[u]) * bf16_hi_f64(sw[u]);
+          acc += p0;
+          acc += p1;
+          mag += __builtin_fabs(p0);
+          mag += __builtin_fabs(p1);
+        }
+        const double sum = row_sum_f64(acc);
+        double b = bnd[t];
+        if (!(b < INFINITY)) b = row_sum_f64(mag) * (1.0 + 0x1.0p-40);   // the key norm left fp32
+        const uint32_t m = 1u << p[t];
+        if (__builtin_fabs(sum) > 0x1.0p-46 * b) word[t] = sum > 0.0 ? (word[t] | m) : (word[t] & ~m);
+        else slow[t] |= m;
+        fl[t] &= fl[t] - 1;
+        if (fl[t]) {   // next flagged coordinate of this entry
+          p[t] = __builtin_ctz(fl[t]);
+          sc[t] = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(cb + 32 * hf[t] + p[t]) * D)[sub];
+        }
+      }
+    }
+    // exact integer sums, one (key, coordinate) at a time on lane 0
+#pragma unroll
+    for (int t = 0; t < RU; ++t) {
+      for (uint64_t heads = __ballot(sub == 0 && slow[t] != 0); heads; heads &= heads - 1) {
+        const int src = __builtin_ctzll(heads);
+        uint32_t bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slow[t]), src));
+        const uint32_t rsrc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(row[t]), src));
+        const int hsrc = __builtin_amdgcn_readlane(hf[t], src);
+        while (bits) {
+          const int q = __builtin_ctz(bits);
+          bits &= bits - 1;
+          bool bit = false;
+          if (lane == 0)
+            bit = exact_sign_long(keys + static_cast<int64_t>(rsrc) * D,
+                                  s_md + static_cast<int64_t>(cb + 32 * hsrc + q) * D, scratch);
+          bit = __builtin_amdgcn_readfirstlane(static_cast<int>(bit)) != 0;
+          if ((lane >> 4) == (src >> 4)) word[t] = bit ? (word[t] | (1u << q)) : (word[t] & ~(1u << q));
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < RU; ++t) {
+      if (sub == 0 && base + 4 * t + g < qn) {
+        const uint32_t bh = row[t] / un;
+        const int64_t dst = static_cast<int64_t>(bh) * cap + pos + (row[t] - bh * un);
+        signs[dst * wpr + (cb >> 5) + hf[t]] = word[t];
+      }
     }
   }
-  const double sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  // magnitude bound: sum|p| computed with relative error below 2^-46
-  if (need_mag) bnd = mag * (1.0 + 0x1.0p-40);
-  if (__builtin_fabs(sum) > 0x1.0p-46 * bnd) return sum > 0.0 ? 1 : 0;
-  return -1;
 }
 
 template <int M>
@@ -313,6 +326,18 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     for (int s = 0; s < 8; ++s) a[b][s] = as_bf16x8(row[2 * s + half]);
   }
   const float smax = col_norm_max[wave];
+  // decides and stores the queued words of this wave (uniform call): RU
+  // rounds of four entries at a time (fewer registers inside the tile loop)
+  auto flush = [&](auto ru) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    fix_queue<decltype(ru)::value>(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
+                                   long_scratch[wave], lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
   // chunk c of a tile: key row c / 16, 16-byte column c % 16; the 16 chunks
   // of a row belong to 16 consecutive threads (one DPP row)
@@ -378,33 +403,41 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       // ---- certification threshold for this lane's key ----
       // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
       // squares plus squares lost below the fp32 normal range (with margin).
-      const float knorm_up = __builtin_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f));
+      // (v_sqrt_f32 is within 1 ulp; the factor 1 + 2^-20 keeps the bound)
+      const float knorm_up =
+          __builtin_amdgcn_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f)) * (1.0f + 0x1.0p-20f);
       const float tau = __builtin_fmaf(c1 * knorm_up, smax, c2);
 
-      // ---- sign word, highest coordinate shifted in first ----
+      // ---- sign word, highest coordinate shifted in first: acc1 gives bits
+      // 16..31, acc0 bits 0..15 ----
       uint32_t sw = 0;
-      float amin = __builtin_fabsf(acc0[0]);
+      float amin1 = __builtin_fabsf(acc1[0]);
+      float amin0 = __builtin_fabsf(acc0[0]);
   #pragma unroll
       for (int r = 15; r >= 0; --r) {
         sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc1[r]), 31);
-        amin = fminf(amin, __builtin_fabsf(acc1[r]));
+        amin1 = fminf(amin1, __builtin_fabsf(acc1[r]));
       }
   #pragma unroll
       for (int r = 15; r >= 0; --r) {
         sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc0[r]), 31);
-        amin = fminf(amin, __builtin_fabsf(acc0[r]));
+        amin0 = fminf(amin0, __builtin_fabsf(acc0[r]));
       }
       uint32_t word = ~sw;
-      // ---- flag word (|acc| <= tau), only when some lane of the wave has one ----
-      uint32_t flags = 0;
-      if (__ballot(amin <= tau) != 0) {
-        uint32_t fw = 0;
+      // ---- flag bits (|acc| <= tau), each half only when some lane of the
+      // wave has one there ----
+      uint32_t fw1 = 0xFFFFu, fw0 = 0xFFFFu;   // set bit: not flagged
+      if (__ballot(amin1 <= tau) != 0) {
+        fw1 = 0;
   #pragma unroll
-        for (int r = 15; r >= 0; --r) fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
-  #pragma unroll
-        for (int r = 15; r >= 0; --r) fw = __builtin_amdgcn_alignbit(fw, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
-        flags = ~fw;
+        for (int r = 15; r >= 0; --r) fw1 = __builtin_amdgcn_alignbit(fw1, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
       }
+      if (__ballot(amin0 <= tau) != 0) {
+        fw0 = 0;
+  #pragma unroll
+        for (int r = 15; r >= 0; --r) fw0 = __builtin_amdgcn_alignbit(fw0, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
+      }
+      uint32_t flags = ~((fw1 << 16) | fw0);
       // keys so large that products can overflow fp32: certify every bit
       if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
       const uint32_t r = tb + nb * KB + j;
@@ -430,43 +463,19 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       bool deferred = false;
       if (need) {
         const int cnt = __popcll(need);
-        if (qn + cnt <= QCAP) {
-          if (flags != 0) {
-            const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                      static_cast<uint32_t>(need >> 32),
-                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(need), 0u)));
-            fixq[wave][slot] = make_uint4(r | (static_cast<uint32_t>(half) << 31), word, flags, 0u);
-            fixn[wave][slot] = knorm_up;
-            deferred = true;
-          }
-          qn += cnt;
-        } else {
-          uint64_t todo = need;
-          while (todo) {
-            const int src = __builtin_ctzll(todo);
-            todo &= todo - 1;
-            uint32_t fsrc = __shfl(flags, src);
-            const int jsrc = src & 31;
-            const int hsrc = src >> 5;
-            const uint16_t* key_lds = reinterpret_cast<const uint16_t*>(tl + (nb * KB + jsrc) * LDS_ROW);
-            const uint32_t kpair = reinterpret_cast<const uint32_t*>(key_lds)[lane];
-            if (__ballot((kpair & 0x7FFF7FFFu) != 0) == 0) {
-              // the key is all (+/-) zeros: every projection is exactly 0 -> bit 1
-              if (lane == src) word |= fsrc;
-              continue;
-            }
-            while (fsrc) {
-              const int p = __builtin_ctz(fsrc);
-              fsrc &= fsrc - 1;
-              const uint16_t* s_row = s_md + static_cast<int64_t>(cb + 32 * hsrc + p) * D;
-              const uint32_t spair = reinterpret_cast<const uint32_t*>(s_row)[lane];
-              const double bnd = static_cast<double>(__shfl(knorm_up, src)) * smax;
-              const bool bit = decide(uniform_f64(pair_sum(kpair, spair)), bnd, kpair, spair, key_lds, s_row,
-                                      long_scratch[wave], lane);
-              if (lane == src) word = bit ? (word | (1u << p)) : (word & ~(1u << p));
-            }
-          }
+        if (qn + cnt > QCAP) {   // full: decide the queued words now
+          flush(std::integral_constant<int, 1>{});
+          qn = 0;
         }
+        if (flags != 0) {
+          const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                    static_cast<uint32_t>(need >> 32),
+                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(need), 0u)));
+          fixq[wave][slot] = make_uint4(r | (static_cast<uint32_t>(half) << 31), word, flags, 0u);
+          fixn[wave][slot] = knorm_up;
+          deferred = true;
+        }
+        qn += cnt;
       }
 
       // ---- stores ----
@@ -497,65 +506,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     buf ^= 1;
   }
 
-  // ---- deferred exact fixes: lane e takes queue entry e (QCAP <= 64) and
-  // decides its flagged bits one per pass, lowest first, from its own loads
-  // of the key row and of the sketch row; the rare sums too close to zero
-  // for the fp64 bound go, one at a time, to the exact integer accumulator ----
-  if (qn > 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const bool act = lane < qn;
-    const uint4 ent = act ? fixq[wave][lane] : make_uint4(0, 0, 0, 0);
-    const float knu = act ? fixn[wave][lane] : 0.f;
-    const uint32_t r = ent.x & 0x7FFFFFFFu;
-    const int hf = static_cast<int>(ent.x >> 31);
-    uint32_t word = ent.y;
-    uint32_t fl = ent.z;
-    const uint16_t* krow = keys + static_cast<int64_t>(r) * D;
-    uint4 kr[D / 8];
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) kr[i] = act ? reinterpret_cast<const uint4*>(krow)[i] : make_uint4(0, 0, 0, 0);
-    uint32_t nz = 0;
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) nz |= (kr[i].x | kr[i].y | kr[i].z | kr[i].w) & 0x7FFF7FFFu;
-    if (nz == 0) {   // an all (+/-) zero key projects to exactly 0: bit 1
-      word |= fl;
-      fl = 0;
-    }
-    const double bnd = static_cast<double>(knu) * smax;
-    uint32_t slow = 0;   // bits the fp64 sum could not decide
-    while (__ballot(fl != 0)) {
-      if (fl) {
-        const int p = __builtin_ctz(fl);
-        const uint16_t* srow = s_md + static_cast<int64_t>(cb + 32 * hf + p) * D;
-        const int bit = serial_sign(kr, reinterpret_cast<const uint4*>(srow), bnd);
-        if (bit < 0) slow |= 1u << p;
-        else word = bit ? (word | (1u << p)) : (word & ~(1u << p));
-        fl &= fl - 1;
-      }
-    }
-    // exact integer sums, one (key, coordinate) at a time on lane 0
-    for (uint64_t lanes = __ballot(slow != 0); lanes; lanes &= lanes - 1) {
-      const int src = __builtin_ctzll(lanes);
-      uint32_t bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slow), src));
-      const uint16_t* kp = readlane_ptr(krow, src);
-      const int hsrc = __builtin_amdgcn_readlane(hf, src);
-      while (bits) {
-        const int p = __builtin_ctz(bits);
-        bits &= bits - 1;
-        bool b = false;
-        if (lane == 0) b = exact_sign_long(kp, s_md + static_cast<int64_t>(cb + 32 * hsrc + p) * D, long_scratch[wave]);
-        b = __builtin_amdgcn_readfirstlane(static_cast<int>(b)) != 0;
-        if (lane == src) word = b ? (word | (1u << p)) : (word & ~(1u << p));
-      }
-    }
-    if (act) {
-      const uint32_t bh = r / un;
-      const int64_t dst = static_cast<int64_t>(bh) * cap + pos + (r - bh * un);
-      signs[dst * WPR + (cb >> 5) + hf] = word;
-    }
-  }
+  if (qn > 0) flush(std::integral_constant<int, 4>{});
 }
 
 template <int M>
