@@ -116,17 +116,17 @@ __device__ __forceinline__ double bf16_hi_f64(uint32_t pair) {
 
 // Norm of a key whose fp32 sum of squares under- or overflowed: scale by a
 // power of two first (exact), then undo it.
-__device__ float scaled_norm(const uint16_t* key_lds) {
+__device__ float scaled_norm(const uint16_t* key) {
   uint32_t emax = 0;
   for (int c = 0; c < D; ++c) {
-    const uint32_t e = (key_lds[c] >> 7) & 0xFF;
+    const uint32_t e = (key[c] >> 7) & 0xFF;
     emax = e > emax ? e : emax;
   }
   if (emax == 0) {
     // all zeros or bf16 subnormals: scale up by 2^64 (exact)
     float s = 0.f;
     for (int c = 0; c < D; ++c) {
-      const float v = __uint_as_float(static_cast<uint32_t>(key_lds[c]) << 16) * 0x1.0p64f;
+      const float v = __uint_as_float(static_cast<uint32_t>(key[c]) << 16) * 0x1.0p64f;
       s = __builtin_fmaf(v, v, s);
     }
     return __builtin_sqrtf(s) * 0x1.0p-64f;
@@ -134,7 +134,7 @@ __device__ float scaled_norm(const uint16_t* key_lds) {
   const int e = static_cast<int>(emax) - 127;
   float s = 0.f;
   for (int c = 0; c < D; ++c) {
-    const float v = __builtin_ldexpf(__uint_as_float(static_cast<uint32_t>(key_lds[c]) << 16), -e);
+    const float v = __builtin_ldexpf(__uint_as_float(static_cast<uint32_t>(key[c]) << 16), -e);
     s = __builtin_fmaf(v, v, s);
   }
   return __builtin_ldexpf(__builtin_sqrtf(s), e);
@@ -285,7 +285,7 @@ __device__ __forceinline__ void fix_queue(const uint4* fq, const float* fk, int 
 template <int M>
 __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2))) void encode_kernel(
     const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md,
-    const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
+    const uint16_t* __restrict__ s_efrag, const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
     float* __restrict__ norms, int R, int n, int cap, int pos, int ntiles, float c1,
     float c2) {
   constexpr int W = M / CW;
@@ -317,13 +317,13 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   // holds coordinate cb + 32*((i >> 2) & 1) + 16*b + 4*(i >> 3) + (i & 3), so
   // the 32x32 result places coordinate cb + 32*half + 16*b + r in register r
   // of lane (j, half).
+  // (s_efrag holds these fragments in lane order: one 1 KB load each)
   bf16x8_t a[2][8];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int coord = cb + 32 * ((j >> 2) & 1) + 16 * b + 4 * (j >> 3) + (j & 3);
-    const uint4* row = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(coord) * D);
+    const uint4* fr = reinterpret_cast<const uint4*>(s_efrag) + (static_cast<int64_t>(wave) * 2 + b) * 8 * 64 + lane;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) a[b][s] = as_bf16x8(row[2 * s + half]);
+    for (int s = 0; s < 8; ++s) a[b][s] = as_bf16x8(fr[s * 64]);
   }
   const float smax = col_norm_max[wave];
   // decides and stores the queued words of this wave (uniform call): RU
@@ -352,12 +352,11 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     }
   };
 
-  if (blockIdx.x < ntiles) load_tile(blockIdx.x);
-  int buf = 0;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    uint8_t* tl = lds + buf * TILE_LDS;
-    // squared norms of the tile's keys, once per tile: each thread squares its
-    // chunks (bf16 dot2, fp32), a DPP row sum adds the 16 chunks of a key
+  // staged tile -> LDS tile bb, and its keys' squared norms -> n2buf[bb]:
+  // each thread squares its chunks (bf16 dot2, fp32), a DPP row sum adds the
+  // 16 chunks of a key
+  auto stage = [&](int bb) {
+    uint8_t* t = lds + bb * TILE_LDS;
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
       const uint4 v = pf[k];
@@ -369,37 +368,58 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       q += dpp_f32<0x124>(q);   // row_ror:4
       q += dpp_f32<0x122>(q);   // row_ror:2
       q += dpp_f32<0x121>(q);   // row_ror:1
-      if ((tid & 15) == 0) n2buf[buf][(tid >> 4) + k * (NT / 16)] = q;
+      if ((tid & 15) == 0) n2buf[bb][(tid >> 4) + k * (NT / 16)] = q;
     }
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
       const int c = tid + k * NT;
-      *reinterpret_cast<uint4*>(tl + (c >> 4) * LDS_ROW + (c & 15) * 16) = pf[k];
+      *reinterpret_cast<uint4*>(t + (c >> 4) * LDS_ROW + (c & 15) * 16) = pf[k];
     }
+  };
+
+  // ---- projection on the matrix cores (block nb of LDS tile bb) ----
+  auto project = [&](int bb, int nb, f32x16_t& acc0, f32x16_t& acc1) {
+    acc0 = f32x16_t{};
+    acc1 = f32x16_t{};
+    const uint8_t* krow = lds + bb * TILE_LDS + (nb * KB + j) * LDS_ROW + 16 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8_t bf = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32 * s));
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], bf, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], bf, acc1, 0, 0, 0);
+    }
+  };
+
+  // Software pipeline: the next block's matrix products (across tile
+  // boundaries too) are issued before this block's bit extraction, so they
+  // run while it executes.  Tiles alternate between two LDS buffers; the
+  // barrier that publishes tile t+1 sits inside the last block of tile t.
+  // An LDS tile is read only by project(), and its last reads (tile t-1)
+  // come before the barrier that precedes its next write (tile t+1); the
+  // norms are copied to registers right after the barrier that publishes them.
+  int buf = 0;
+  f32x16_t cur0, cur1, nxt0, nxt1;   // accumulators of this block and the next
+  float n2r[NBLK];
+  if (blockIdx.x < ntiles) {
+    load_tile(blockIdx.x);
+    stage(0);
     __syncthreads();
-    if (tile + static_cast<int>(gridDim.x) < ntiles) load_tile(tile + gridDim.x);
+    if (static_cast<int>(blockIdx.x + gridDim.x) < ntiles) load_tile(blockIdx.x + gridDim.x);
+#pragma unroll
+    for (int k = 0; k < NBLK; ++k) n2r[k] = n2buf[0][k * KB + j];
+    project(0, 0, cur0, cur1);
+  }
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const bool more = tile + static_cast<int>(gridDim.x) < ntiles;   // uniform
     // (batch * head, position) of the tile's first key, once per tile (the
     // host keeps the key count below 2^31)
     const uint32_t tb = static_cast<uint32_t>(tile) * KT;
     const uint32_t tbh = tb / un;
     const uint32_t toff = tb - tbh * un;
-
-    // ---- projection on the matrix cores ----
-    auto project = [&](int nb, f32x16_t& acc0, f32x16_t& acc1) {
-      acc0 = f32x16_t{};
-      acc1 = f32x16_t{};
-      const uint8_t* krow = tl + (nb * KB + j) * LDS_ROW + 16 * half;
-  #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8_t bf = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32 * s));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], bf, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], bf, acc1, 0, 0, 0);
-      }
-    };
+    float n2n[NBLK];
 
     // ---- bits of one block: signs, certification, stores ----
-    auto process = [&](int nb, const f32x16_t& acc0, const f32x16_t& acc1) {
-      const float n2 = n2buf[buf][nb * KB + j];
+    auto process = [&](int nb, const f32x16_t& acc0, const f32x16_t& acc1, float n2) {
       // ---- certification threshold for this lane's key ----
       // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
       // squares plus squares lost below the fp32 normal range (with margin).
@@ -484,25 +504,31 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
         if (wave == 0 && half == 0) {
           float nrm = __builtin_sqrtf(n2);
           if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) {
-            nrm = scaled_norm(reinterpret_cast<const uint16_t*>(tl + (nb * KB + j) * LDS_ROW));
+            nrm = scaled_norm(keys + static_cast<int64_t>(r) * D);
           }
           norms[dst] = nrm;
         }
       }
     };
 
-    // Software pipeline over the blocks of the tile: the next block's matrix
-    // products are issued before this block's bit extraction, so they run
-    // while it executes.
-    f32x16_t c0, c1, d0, d1;
-    project(0, c0, c1);
-  #pragma unroll
+#pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) {
-      if (nb + 1 < NBLK) project(nb + 1, d0, d1);
-      process(nb, c0, c1);
-      c0 = d0;
-      c1 = d1;
+      if (nb + 1 < NBLK) {
+        project(buf, nb + 1, nxt0, nxt1);
+      } else if (more) {   // publish the next tile, start its first block
+        stage(buf ^ 1);
+        __syncthreads();
+        if (tile + 2 * static_cast<int>(gridDim.x) < ntiles) load_tile(tile + 2 * gridDim.x);
+#pragma unroll
+        for (int k = 0; k < NBLK; ++k) n2n[k] = n2buf[buf ^ 1][k * KB + j];
+        project(buf ^ 1, 0, nxt0, nxt1);
+      }
+      process(nb, cur0, cur1, n2r[nb]);
+      cur0 = nxt0;
+      cur1 = nxt1;
     }
+#pragma unroll
+    for (int k = 0; k < NBLK; ++k) n2r[k] = n2n[k];
     buf ^= 1;
   }
 
@@ -531,7 +557,7 @@ int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint3
   const float c1 = static_cast<float>(4.0 * D * 0x1.0p-24 * (1.0 + 0x1.0p-10));
   const float c2 = 0x1.0p-110f;  // absolute floor: subnormal flushes
   hipLaunchKernelGGL(encode_kernel<M>, dim3(grid), dim3(NT), 0, stream,
-                     static_cast<const uint16_t*>(keys), s.s_md, s.col_norm_max, signs, norms, R,
+                     static_cast<const uint16_t*>(keys), s.s_md, s.s_efrag, s.col_norm_max, signs, norms, R,
                      n, cap, pos, ntiles, c1, c2);
   return hipGetLastError();
 }

@@ -40,7 +40,7 @@ bool supported_dm(int d, int m) { return d == qjl::kHeadDim && (m == 256 || m ==
 // ---- device cache of S, keyed by (device, seed, d, m) ----
 struct CacheEntry {
   qjl::DeviceSketch view;
-  void* mem = nullptr;  // one allocation holding s_dm, s_md, col_norm_max
+  void* mem = nullptr;  // one allocation holding every device copy of S
 };
 
 std::mutex g_cache_mu;
@@ -85,11 +85,23 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
         for (int e = 0; e < 8; ++e)
           s_frag[((static_cast<size_t>(blk) * (d / 16) + st) * 64 + l) * 8 + e] =
               s_md[static_cast<size_t>(32 * blk + l % 32) * d + 16 * st + 8 * (l / 32) + e];
+  std::vector<uint16_t> s_efrag(n);
+  for (int w = 0; w < m / 64; ++w)
+    for (int b = 0; b < 2; ++b)
+      for (int st = 0; st < d / 16; ++st)
+        for (int l = 0; l < 64; ++l) {
+          const int jj = l % 32, hh = l / 32;
+          const int coord = 64 * w + 32 * ((jj >> 2) & 1) + 16 * b + 4 * (jj >> 3) + (jj & 3);
+          for (int e = 0; e < 8; ++e)
+            s_efrag[(((static_cast<size_t>(w) * 2 + b) * (d / 16) + st) * 64 + l) * 8 + e] =
+                s_md[static_cast<size_t>(coord) * d + 16 * st + 8 * hh + e];
+        }
   const size_t bytes_s = n * sizeof(uint16_t);
   const size_t padded = (bytes_s + 255) / 256 * 256;
   const size_t off_md = padded;
   const size_t off_fr = off_md + padded;
-  const size_t off_cm = off_fr + padded;
+  const size_t off_ef = off_fr + padded;
+  const size_t off_cm = off_ef + padded;
   const size_t total = off_cm + cmax.size() * sizeof(float);
   void* mem = nullptr;
   e = hipMalloc(&mem, total);
@@ -98,6 +110,7 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
   e = hipMemcpy(base, s_dm.data(), bytes_s, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + off_md, s_md.data(), bytes_s, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + off_fr, s_frag.data(), bytes_s, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + off_ef, s_efrag.data(), bytes_s, hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(base + off_cm, cmax.data(), cmax.size() * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
@@ -109,6 +122,7 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
   ce.view.s_dm = reinterpret_cast<const uint16_t*>(base);
   ce.view.s_md = reinterpret_cast<const uint16_t*>(base + off_md);
   ce.view.s_frag = reinterpret_cast<const uint16_t*>(base + off_fr);
+  ce.view.s_efrag = reinterpret_cast<const uint16_t*>(base + off_ef);
   ce.view.col_norm_max = reinterpret_cast<const float*>(base + off_cm);
   for (float c : cmax) ce.view.col_norm_all = std::max(ce.view.col_norm_all, c);
   ce.view.d = d;
