@@ -814,8 +814,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (i < n_split * G) reinterpret_cast<float2*>(ml_l)[i] = mlv[k];
   }
   __syncthreads();
-  // per head: global max and normalizer, then per-split weights
-  __shared__ float gmax[G], gsum[G];
+  // per head (one wave each): global max and normalizer, then the weight of
+  // every split
   for (int g = wave; g < G; g += NW) {
     float mx = -INFINITY;
     for (int s = lane; s < n_split; s += 64) mx = fmaxf(mx, ml_l[(s * G + g) * 2]);
@@ -823,13 +823,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     float Ls = 0.f;
     for (int s = lane; s < n_split; s += 64) Ls += ml_l[(s * G + g) * 2 + 1] * exp2f(ml_l[(s * G + g) * 2] - mx);
     Ls = wave_sum(Ls);
-    if (lane == 0) {
-      gmax[g] = mx;
-      gsum[g] = Ls;
-    }
+    for (int s = lane; s < n_split; s += 64) wts[s * G + g] = exp2f(ml_l[(s * G + g) * 2] - mx) / Ls;
   }
-  __syncthreads();
-  for (int i = tid; i < n_split * G; i += NT) wts[i] = exp2f(ml_l[2 * i] - gmax[i % G]) / gsum[i % G];
   __syncthreads();
   if (tid < PAIRS * REP) {
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
