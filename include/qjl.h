@@ -90,7 +90,8 @@ QJL_API qjl_status qjl_sketch_host(uint64_t seed, int32_t d, int32_t m, uint16_t
  *   signs      device, uint32 [B][H_kv][cap][m/32], 16-byte aligned; rows
  *              [pos, pos+n) of every (b, h) are written, others untouched.
  *   norms      device, fp32 [B][H_kv][cap], 4-byte aligned; same rows.
- *              norms = fp32 of the Euclidean norm of the bf16 key.
+ *              norms = the Euclidean norm of the bf16 key in fp32 (an fp32
+ *              sum of squares and the hardware square root: a few ulps).
  *   B, H_kv >= 1; n >= 0 (n == 0 is a no-op); cap >= 1; 0 <= pos;
  *   pos + n <= cap; B * H_kv * n <= 2^31 - 1 (QJL_EINVAL beyond: the
  *   kernel indexes keys in 32 bits); d == 128; m in {256, 512}.

@@ -416,6 +416,9 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     const uint32_t tb = static_cast<uint32_t>(tile) * KT;
     const uint32_t tbh = tb / un;
     const uint32_t toff = tb - tbh * un;
+    const int64_t dst0 = static_cast<int64_t>(tbh) * cap + pos + toff;   // row tb's destination
+    const uint32_t wrap_at = un - toff;                                  // first row of the next (b, h)
+    const uint32_t wrap_add = static_cast<uint32_t>(cap) - un;
     float n2n[NBLK];
 
     // ---- bits of one block: signs, certification, stores ----
@@ -463,19 +466,17 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       const uint32_t r = tb + nb * KB + j;
       const bool valid = r < uR;
       if (!valid) flags = 0;  // zero padding of a ragged last tile
-      // destination row: (batch * head) = tbh + wraps, position = offset
-      uint32_t off = toff + nb * KB + j, bhl = tbh;
-      if (un > static_cast<uint32_t>(KT)) {   // at most one wrap within a tile
-        if (off >= un) {
-          off -= un;
-          ++bhl;
-        }
+      // destination row: the tile's first row plus this row's offset, plus
+      // cap - n past a (batch, head) boundary
+      int64_t dst;
+      if (un > static_cast<uint32_t>(KT)) {   // at most one boundary within a tile
+        const uint32_t rel = nb * KB + j;
+        dst = dst0 + (rel + (rel >= wrap_at ? wrap_add : 0u));
       } else {
-        const uint32_t w = off / un;
-        bhl += w;
-        off -= w * un;
+        const uint32_t off0 = toff + nb * KB + j;
+        const uint32_t w = off0 / un;
+        dst = static_cast<int64_t>(tbh + w) * cap + pos + (off0 - w * un);
       }
-      const int64_t dst = static_cast<int64_t>(bhl) * cap + pos + off;
 
       // ---- flagged words: queued for the exact fix after the last tile, or
       // (queue full) fixed here, one (key, coordinate) pair at a time ----
@@ -501,8 +502,10 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       // ---- stores ----
       if (valid) {
         if (!deferred) signs[dst * WPR + (cb >> 5) + half] = word;
-        if (wave == 0 && half == 0) {
-          float nrm = __builtin_sqrtf(n2);
+        // the norm of block nb's keys is stored by wave nb (spreads the work)
+        if (wave == nb && half == 0) {
+          // v_sqrt_f32: within 1 ulp of the square root
+          float nrm = __builtin_amdgcn_sqrtf(n2);
           if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) {
             nrm = scaled_norm(keys + static_cast<int64_t>(r) * D);
           }
