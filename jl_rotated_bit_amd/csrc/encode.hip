@@ -12,26 +12,34 @@
 // * The projection P^T = S^T K^T runs on the matrix cores
 //   (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  A workgroup has m/64
 //   waves; wave w owns sketch coordinates [64w, 64w+64) and keeps its slice
-//   of S^T (64 x 128 bf16, 64 VGPRs) resident for the whole kernel.
-// * Keys stream through LDS in tiles of 32 (one MFMA column block), loaded
-//   with coalesced 16-byte reads and double-buffered; the next tile's loads
-//   are in flight while the current tile is multiplied.
+//   of -S^T (64 x 128 bf16, 64 VGPRs) resident for the whole kernel.  The
+//   slice is negated so that the sign bit of an accumulator is already the
+//   stored bit (1 for a non-negative projection).
+// * Keys stream through LDS in tiles of 128 rows, loaded with coalesced
+//   16-byte buffer loads (rows past the end read as zero) and
+//   double-buffered; the next tile's loads are in flight while the current
+//   tile is multiplied.
 // * The A-operand rows are permuted so that lane (key j, half h) ends up
 //   holding coordinates 64w + 32h + 0..31 of key j in its 32 accumulators:
 //   one word of packed bits per lane, assembled with v_alignbit (one
 //   instruction per bit-lane), no cross-lane traffic.
-// * ||k||^2 comes from the same B fragments (bf16 dot2, fp32 accumulate).
+// * ||k||^2 is summed (bf16 dot2, fp32) while a tile is staged into LDS.
 // * Certification: an accumulator with |acc| <= tau, where tau bounds the
 //   accumulation error of a d-term fp32 dot product of exact bf16 products
-//   (with margin), is re-evaluated exactly: the wave sums the 128 fp64
-//   products (exact) in a tree with a rigorous error bound, and falls back to
-//   an exact integer long accumulator when even that is inconclusive.  The
-//   resulting bit is the sign of the exact real sum, with sign(0) = +1.
+//   (with margin), is re-evaluated exactly: its word is queued and, after the
+//   last tile, the wave sums the 128 fp64 products (exact) with a rigorous
+//   error bound, falling back to an exact integer long accumulator when even
+//   that is inconclusive.  The resulting bit is the sign of the exact real
+//   sum, with sign(0) = +1.  A wave whose queue fills keeps going (later
+//   words are stored as computed) and afterwards re-runs its tiles from the
+//   first one it could not queue, deciding every flagged word there; keys
+//   whose squared norm left the accurate fp32 range get their norms
+//   recomputed the same way.  Neither path adds code to the tile loop.
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
-#include <type_traits>
 
 #include "internal.h"
 
@@ -53,7 +61,6 @@ constexpr int TILE_LDS = KT * LDS_ROW;
 constexpr int CHUNKS = KT * ROW_B / 16;  // 16-byte chunks per key tile (2048)
 constexpr int ACC_WORDS = 18;        // long accumulator: 576 bits
 constexpr int QCAP = 64;             // deferred-fix queue entries per wave
-constexpr int FIXB = 16;             // (word, bit) fixes per batch of loads
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
@@ -140,7 +147,7 @@ __device__ float scaled_norm(const uint16_t* key) {
   return __builtin_ldexpf(__builtin_sqrtf(s), e);
 }
 
-// fp64 move across a 16-lane row through DPP (each half separately)
+// fp64 move within a quad of lanes through DPP (each half separately)
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = __double_as_longlong(x);
@@ -148,137 +155,145 @@ __device__ __forceinline__ double dpp_f64(double x) {
   const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, 0xF, 0xF, true);
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
-constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i
-constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each half row
-constexpr int kQuadXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kQuadXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-// Sum over a 16-lane row: mirror, half-mirror, then quad swaps.  Every step
-// adds a lane's value to its partner's and the partner adds the same two
-// numbers, so all 16 lanes end with bit-identical totals (tree height 4).
-__device__ __forceinline__ double row_sum_f64(double x) {
-  x += dpp_f64<kRowMirror>(x);
-  x += dpp_f64<kRowHalfMirror>(x);
-  x += dpp_f64<kQuadXor2>(x);
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+// Sum over a quad of lanes: each step adds a lane's value to its partner's
+// and the partner adds the same two numbers, so all four lanes end with
+// bit-identical totals.
+__device__ __forceinline__ double quad_sum_f64(double x) {
   x += dpp_f64<kQuadXor1>(x);
+  x += dpp_f64<kQuadXor2>(x);
   return x;
 }
-__device__ __forceinline__ uint32_t row_or(uint32_t x) {
-  x |= __builtin_amdgcn_update_dpp(0u, x, kRowMirror, 0xF, 0xF, true);
-  x |= __builtin_amdgcn_update_dpp(0u, x, kRowHalfMirror, 0xF, 0xF, true);
-  x |= __builtin_amdgcn_update_dpp(0u, x, kQuadXor2, 0xF, 0xF, true);
+__device__ __forceinline__ uint32_t quad_or(uint32_t x) {
   x |= __builtin_amdgcn_update_dpp(0u, x, kQuadXor1, 0xF, 0xF, true);
+  x |= __builtin_amdgcn_update_dpp(0u, x, kQuadXor2, 0xF, 0xF, true);
   return x;
 }
 
+// Buffer descriptor over [base, base + bytes): loads past the end return
+// zero.  base and bytes must be wave-uniform.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, no swizzle
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+// Destination row of global key row r: (batch, head) = r / n, position
+// pos + r % n in a cache of cap rows per (batch, head).
+__device__ __forceinline__ int64_t dest_row(uint32_t r, uint32_t un, int cap, int pos) {
+  const uint32_t bh = r / un;
+  return static_cast<int64_t>(bh) * cap + pos + (r - bh * un);
+}
+
 // Exact-sign evaluation of queued sign words (the words whose flagged bits
-// the fp32 projection could not certify).  Sixteen lanes serve one entry:
-// lane (group g, sub c) loads 16 bytes (channels 8c .. 8c+7) of the key row
-// and of the sketch row, so every load instruction reads four whole rows.
-// The eight products of a lane are exact in fp64 and are added in order,
-// then row_sum_f64 adds the 16 lanes: a summation tree of height 11, off by
-// at most 11 * 2^-53 * sum|p| < 2^-49 * bnd for any bnd >= sum|p| (such as
-// ||k|| max_i ||s_i||, Cauchy-Schwarz).  The bit is the sign of the sum when
-// |sum| > 2^-46 * bnd; the rare sums below that go, one at a time, to the
-// exact integer accumulator.  RU rounds of four entries have their loads in
-// flight together; flagged bits of an entry are taken one pass each, lowest
-// first.  fq/fk: the queue ({key row | half << 31, word, flags, -}, norm
-// bound); the decided words are stored to their rows.
-template <int RU>
+// the fp32 projection could not certify).  Four lanes serve one entry: lane
+// (group g, sub c) loads 16-byte chunks c, 4 + c, 8 + c, 12 + c (32
+// channels) of the key row and of the sketch row of the entry's lowest
+// flagged coordinate, so one pass decides one flagged bit of sixteen entries
+// and each load instruction reads 64 contiguous bytes per quad.  The 32
+// products of a lane are exact in fp64 and accumulated by fma (one rounding
+// each), then quad_sum_f64 adds the four lanes: at most 34 roundings, each
+// within 2^-53 of sum|p|, so the error is below 2^-47 * bnd for any
+// bnd >= sum|p| (such as ||k|| max_i ||s_i||, Cauchy-Schwarz).  The bit is
+// the sign of the sum when |sum| > 2^-46 * bnd; the rare sums below that
+// go, one at a time, to the exact integer accumulator.  fq/fk: the queue
+// ({key row | half << 31, word, flags, -}, norm bound); the decided words
+// are stored to their rows.
 __device__ __forceinline__ void fix_queue(const uint4* fq, const float* fk, int qn, const uint16_t* keys,
                                           const uint16_t* s_md, int cb, float smax, uint32_t* signs,
                                           uint32_t un, int cap, int pos, int wpr, uint32_t* scratch,
                                           int lane) {
-  const int g = lane >> 4, sub = lane & 15;
-  for (int base = 0; base < qn; base += 4 * RU) {
-    uint4 kc[RU], sc[RU];
-    uint32_t word[RU], fl[RU], row[RU], slow[RU];
-    int hf[RU], p[RU];
-    double bnd[RU];
+  const int g = lane >> 2, sub = lane & 3;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  for (int base = 0; base < qn; base += 16) {
+    const int e = base + g;
+    const bool act = e < qn;
+    const uint4 ent = act ? fq[e] : zero;
+    const uint32_t row = ent.x & 0x7FFFFFFFu;
+    const int hf = static_cast<int>(ent.x >> 31);
+    uint32_t word = ent.y, fl = ent.z, slow = 0;   // fl is zero for inactive entries
+    const double bnd = act ? static_cast<double>(fk[e]) * smax : 0.0;
+    int p = fl ? __builtin_ctz(fl) : 0;
+    // unconditional 16-byte loads (an inactive entry reads key row 0 and
+    // sketch row cb, both in bounds, and decides nothing)
+    const uint4* krow = reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(row) * D);
+    uint4 kc[4], sc[4];
 #pragma unroll
-    for (int t = 0; t < RU; ++t) {
-      const int e = base + 4 * t + g;
-      const bool act = e < qn;
-      const uint4 ent = act ? fq[e] : make_uint4(0, 0, 0, 0);
-      row[t] = ent.x & 0x7FFFFFFFu;
-      hf[t] = static_cast<int>(ent.x >> 31);
-      word[t] = ent.y;
-      fl[t] = ent.z;   // zero for inactive entries
-      bnd[t] = act ? static_cast<double>(fk[e]) * smax : 0.0;
-      p[t] = fl[t] ? __builtin_ctz(fl[t]) : 0;
-      slow[t] = 0;
-      kc[t] = act ? reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(row[t]) * D)[sub]
-                  : make_uint4(0, 0, 0, 0);
-      sc[t] = fl[t] ? reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(cb + 32 * hf[t] + p[t]) * D)[sub]
-                    : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < 4; ++u) kc[u] = krow[4 * u + sub];
+    auto load_s = [&]() {
+      const uint4* srow = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(cb + 32 * hf + p) * D);
 #pragma unroll
-    for (int t = 0; t < RU; ++t) {   // an all (+/-) zero key projects to exactly 0: bit 1
-      if (row_or((kc[t].x | kc[t].y | kc[t].z | kc[t].w) & 0x7FFF7FFFu) == 0) {
-        word[t] |= fl[t];
-        fl[t] = 0;
-      }
+      for (int u = 0; u < 4; ++u) sc[u] = srow[4 * u + sub];
+    };
+    load_s();
+    // an all (+/-) zero key projects to exactly 0: bit 1
+    uint32_t nz = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) nz |= kc[u].x | kc[u].y | kc[u].z | kc[u].w;
+    if (quad_or(nz & 0x7FFF7FFFu) == 0) {
+      word |= fl;
+      fl = 0;
     }
     for (;;) {
-      uint32_t any = 0;
-#pragma unroll
-      for (int t = 0; t < RU; ++t) any |= fl[t];
-      if (__ballot(any != 0) == 0) break;
-#pragma unroll
-      for (int t = 0; t < RU; ++t) {
-        if (fl[t] == 0) continue;   // uniform over the entry's 16 lanes
-        const uint32_t kw[4] = {kc[t].x, kc[t].y, kc[t].z, kc[t].w};
-        const uint32_t sw[4] = {sc[t].x, sc[t].y, sc[t].z, sc[t].w};
-        double acc = 0.0, mag = 0.0;
+      if (__ballot(fl != 0) == 0) break;
+      if (fl != 0) {   // uniform over the entry's four lanes
+        double acc = 0.0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const double p0 = bf16_lo_f64(kw[u]) * bf16_lo_f64(sw[u]);
-          const double p1 = bf16_hi_f64(kw[u]) * bf16_hi_f64(sw[u]);
-          acc += p0;
-          acc += p1;
-          mag += __builtin_fabs(p0);
-          mag += __builtin_fabs(p1);
+          const uint32_t kw[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+          const uint32_t sw[4] = {sc[u].x, sc[u].y, sc[u].z, sc[u].w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            acc = __builtin_fma(bf16_lo_f64(kw[t]), bf16_lo_f64(sw[t]), acc);
+            acc = __builtin_fma(bf16_hi_f64(kw[t]), bf16_hi_f64(sw[t]), acc);
+          }
         }
-        const double sum = row_sum_f64(acc);
-        double b = bnd[t];
-        if (!(b < INFINITY)) b = row_sum_f64(mag) * (1.0 + 0x1.0p-40);   // the key norm left fp32
-        const uint32_t m = 1u << p[t];
-        if (__builtin_fabs(sum) > 0x1.0p-46 * b) word[t] = sum > 0.0 ? (word[t] | m) : (word[t] & ~m);
-        else slow[t] |= m;
-        fl[t] &= fl[t] - 1;
-        if (fl[t]) {   // next flagged coordinate of this entry
-          p[t] = __builtin_ctz(fl[t]);
-          sc[t] = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(cb + 32 * hf[t] + p[t]) * D)[sub];
+        const double sum = quad_sum_f64(acc);
+        double b = bnd;
+        if (!(b < INFINITY)) {   // the key norm left fp32: bound by sum|p| itself
+          double mag = 0.0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t kw[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+            const uint32_t sw[4] = {sc[u].x, sc[u].y, sc[u].z, sc[u].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              mag += __builtin_fabs(bf16_lo_f64(kw[t]) * bf16_lo_f64(sw[t]));
+              mag += __builtin_fabs(bf16_hi_f64(kw[t]) * bf16_hi_f64(sw[t]));
+            }
+          }
+          b = quad_sum_f64(mag) * (1.0 + 0x1.0p-40);
+        }
+        const uint32_t mbit = 1u << p;
+        if (__builtin_fabs(sum) > 0x1.0p-46 * b) word = sum > 0.0 ? (word | mbit) : (word & ~mbit);
+        else slow |= mbit;
+        fl &= fl - 1;
+        if (fl) {   // next flagged coordinate of this entry
+          p = __builtin_ctz(fl);
+          load_s();
         }
       }
     }
     // exact integer sums, one (key, coordinate) at a time on lane 0
-#pragma unroll
-    for (int t = 0; t < RU; ++t) {
-      for (uint64_t heads = __ballot(sub == 0 && slow[t] != 0); heads; heads &= heads - 1) {
-        const int src = __builtin_ctzll(heads);
-        uint32_t bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slow[t]), src));
-        const uint32_t rsrc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(row[t]), src));
-        const int hsrc = __builtin_amdgcn_readlane(hf[t], src);
-        while (bits) {
-          const int q = __builtin_ctz(bits);
-          bits &= bits - 1;
-          bool bit = false;
-          if (lane == 0)
-            bit = exact_sign_long(keys + static_cast<int64_t>(rsrc) * D,
-                                  s_md + static_cast<int64_t>(cb + 32 * hsrc + q) * D, scratch);
-          bit = __builtin_amdgcn_readfirstlane(static_cast<int>(bit)) != 0;
-          if ((lane >> 4) == (src >> 4)) word[t] = bit ? (word[t] | (1u << q)) : (word[t] & ~(1u << q));
-        }
+    for (uint64_t heads = __ballot(sub == 0 && slow != 0); heads; heads &= heads - 1) {
+      const int src = __builtin_ctzll(heads);
+      uint32_t bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slow), src));
+      const uint32_t rsrc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(row), src));
+      const int hsrc = __builtin_amdgcn_readlane(hf, src);
+      while (bits) {
+        const int q = __builtin_ctz(bits);
+        bits &= bits - 1;
+        bool bit = false;
+        if (lane == 0)
+          bit = exact_sign_long(keys + static_cast<int64_t>(rsrc) * D,
+                                s_md + static_cast<int64_t>(cb + 32 * hsrc + q) * D, scratch);
+        bit = __builtin_amdgcn_readfirstlane(static_cast<int>(bit)) != 0;
+        if ((lane >> 2) == (src >> 2)) word = bit ? (word | (1u << q)) : (word & ~(1u << q));
       }
     }
-#pragma unroll
-    for (int t = 0; t < RU; ++t) {
-      if (sub == 0 && base + 4 * t + g < qn) {
-        const uint32_t bh = row[t] / un;
-        const int64_t dst = static_cast<int64_t>(bh) * cap + pos + (row[t] - bh * un);
-        signs[dst * wpr + (cb >> 5) + hf[t]] = word[t];
-      }
-    }
+    if (sub == 0 && act) signs[dest_row(row, un, cap, pos) * wpr + (cb >> 5) + hf] = word;
   }
 }
 
@@ -286,8 +301,7 @@ template <int M>
 __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2))) void encode_kernel(
     const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md,
     const uint16_t* __restrict__ s_efrag, const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
-    float* __restrict__ norms, int R, int n, int cap, int pos, int ntiles, float c1,
-    float c2) {
+    float* __restrict__ norms, int R, int n, int cap, int pos, int ntiles, float c1, float c2) {
   constexpr int W = M / CW;
   constexpr int NT = 64 * W;
   constexpr int LOADS = CHUNKS / NT;  // 16-byte loads per thread per tile
@@ -296,27 +310,30 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TILE_LDS];
   __shared__ float n2buf[2][KT];   // squared key norms of the tile
+  __shared__ float n2sink[W][64];  // written by lanes that own no norm (no branch)
   __shared__ uint32_t long_scratch[W][2 * ACC_WORDS];
   // Sign words with bits to certify, queued per wave for an exact fix after
-  // the last tile: {key row | half << 31, word, flags, 0}.  The fix then
-  // gives one entry to each lane, all loads in flight together.
+  // the last tile: {key row | half << 31, word, flags, 0}.
   __shared__ uint4 fixq[W][QCAP];
   __shared__ float fixn[W][QCAP];   // upper bound of ||k|| of the entry's key
-  int qn = 0;   // queued entries of this wave (uniform)
+  int qn = 0;              // queued entries of this wave (uniform)
+  int ovf = INT_MAX;       // first tile with a flagged word the queue had no room for (uniform)
+  bool odd_norm = false;   // some key of this wave's norm blocks left the accurate range (uniform)
 
+  if (static_cast<int>(blockIdx.x) >= ntiles) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int j = lane & 31;
   const int cb = wave * CW;
   const uint32_t un = static_cast<uint32_t>(n);
   const uint32_t uR = static_cast<uint32_t>(R);
 
-  // Resident A operand: S^T rows for this wave's coordinates.  Block b, row i
-  // holds coordinate cb + 32*((i >> 2) & 1) + 16*b + 4*(i >> 3) + (i & 3), so
-  // the 32x32 result places coordinate cb + 32*half + 16*b + r in register r
-  // of lane (j, half).
+  // Resident A operand: -S^T rows for this wave's coordinates.  Block b, row
+  // i holds coordinate cb + 32*((i >> 2) & 1) + 16*b + 4*(i >> 3) + (i & 3),
+  // so the 32x32 result places coordinate cb + 32*half + 16*b + r in
+  // register r of lane (j, half).
   // (s_efrag holds these fragments in lane order: one 1 KB load each)
   bf16x8_t a[2][8];
 #pragma unroll
@@ -326,39 +343,33 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     for (int s = 0; s < 8; ++s) a[b][s] = as_bf16x8(fr[s * 64]);
   }
   const float smax = col_norm_max[wave];
-  // decides and stores the queued words of this wave (uniform call): RU
-  // rounds of four entries at a time (fewer registers inside the tile loop)
-  auto flush = [&](auto ru) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    fix_queue<decltype(ru)::value>(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
-                                   long_scratch[wave], lane);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
+  const float c1s = c1 * smax;   // tau = c1s * ||k||_up + c2
 
-  // chunk c of a tile: key row c / 16, 16-byte column c % 16; the 16 chunks
-  // of a row belong to 16 consecutive threads (one DPP row)
+  // chunk c of a tile: key row c / 16, 16-byte column c % 16 (byte offset
+  // 16 c); the 16 chunks of a row belong to 16 consecutive threads (one DPP
+  // row).  Rows past the end of the keys read as zero.
   uint4 pf[LOADS];
-  auto load_tile = [&](int tile) {
+  constexpr int LPB = LOADS / NBLK;   // chunks staged (and reloaded) per block
+  static_assert(LOADS % NBLK == 0, "chunks must split evenly over the blocks");
+  // (a tile past the end gets an empty descriptor: its loads return zeros
+  // and touch no memory, so every load in the loop is unconditional and the
+  // compiler's wait counts stay exact)
+  auto load_part = [&](int tile, int part) {
+    const uint32_t tb = static_cast<uint32_t>(tile) * KT;
+    const uint32_t rows = tb < uR ? min(uR - tb, static_cast<uint32_t>(KT)) : 0u;
+    const rsrc_t rs = make_rsrc(keys + static_cast<int64_t>(tb) * D, static_cast<int>(rows) * ROW_B);
 #pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      const int c = tid + k * NT;
-      const uint32_t r = static_cast<uint32_t>(tile) * KT + (c >> 4);
-      pf[k] = r < uR ? reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(r) * D)[c & 15]
-                     : make_uint4(0, 0, 0, 0);
-    }
+    for (int k = part * LPB; k < (part + 1) * LPB; ++k)
+      pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + k * NT) * 16, 0, 0));
   };
 
-  // staged tile -> LDS tile bb, and its keys' squared norms -> n2buf[bb]:
-  // each thread squares its chunks (bf16 dot2, fp32), a DPP row sum adds the
-  // 16 chunks of a key
-  auto stage = [&](int bb) {
+  // staged chunks -> LDS tile bb, and their keys' squared norms ->
+  // n2buf[bb]: each thread squares its chunks (bf16 dot2, fp32), a DPP row
+  // sum adds the 16 chunks of a key
+  auto stage_part = [&](int bb, int part) {
     uint8_t* t = lds + bb * TILE_LDS;
 #pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
+    for (int k = part * LPB; k < (part + 1) * LPB; ++k) {
       const uint4 v = pf[k];
       float q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), 0.f, false);
       q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), q, false);
@@ -368,12 +379,9 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       q += dpp_f32<0x124>(q);   // row_ror:4
       q += dpp_f32<0x122>(q);   // row_ror:2
       q += dpp_f32<0x121>(q);   // row_ror:1
-      if ((tid & 15) == 0) n2buf[bb][(tid >> 4) + k * (NT / 16)] = q;
-    }
-#pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
+      *((tid & 15) == 0 ? &n2buf[bb][(tid >> 4) + k * (NT / 16)] : &n2sink[wave][lane]) = q;
       const int c = tid + k * NT;
-      *reinterpret_cast<uint4*>(t + (c >> 4) * LDS_ROW + (c & 15) * 16) = pf[k];
+      *reinterpret_cast<uint4*>(t + (c >> 4) * LDS_ROW + (c & 15) * 16) = v;
     }
   };
 
@@ -390,141 +398,183 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     }
   };
 
+  // certification threshold of a key from its fp32 squared norm:
+  // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119) covers the fp32 rounding of 128
+  // exact squares and squares lost below the fp32 normal range (with
+  // margin); v_sqrt_f32 is within 1 ulp, which the factor 1 + 2^-20 keeps.
+  auto norm_bound = [&](float n2) {
+    return __builtin_amdgcn_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f)) * (1.0f + 0x1.0p-20f);
+  };
+  // sign word of a lane, highest coordinate shifted in first (acc1 gives
+  // bits 16..31, acc0 bits 0..15); with -S the sign bit is the stored bit
+  auto sign_word = [](const f32x16_t& acc0, const f32x16_t& acc1) {
+    uint32_t sw = 0;
+#pragma unroll
+    for (int r = 15; r >= 0; --r) sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc1[r]), 31);
+#pragma unroll
+    for (int r = 15; r >= 0; --r) sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc0[r]), 31);
+    return sw;
+  };
+
   // Software pipeline: the next block's matrix products (across tile
   // boundaries too) are issued before this block's bit extraction, so they
-  // run while it executes.  Tiles alternate between two LDS buffers; the
-  // barrier that publishes tile t+1 sits inside the last block of tile t.
-  // An LDS tile is read only by project(), and its last reads (tile t-1)
-  // come before the barrier that precedes its next write (tile t+1); the
-  // norms are copied to registers right after the barrier that publishes them.
+  // run while it executes.  Tiles alternate between two LDS buffers: while
+  // tile t is multiplied, block nb stages a quarter of tile t+1 (loaded
+  // during tile t-1) into the other buffer and reloads those registers with
+  // the same quarter of tile t+2; the barrier in block 3 publishes tile t+1.
+  // That buffer's previous tile (t-1) was last read before the barrier that
+  // published tile t, and so were its norms.
   int buf = 0;
   f32x16_t cur0, cur1, nxt0, nxt1;   // accumulators of this block and the next
   float n2r[NBLK];
-  if (blockIdx.x < ntiles) {
-    load_tile(blockIdx.x);
-    stage(0);
-    __syncthreads();
-    if (static_cast<int>(blockIdx.x + gridDim.x) < ntiles) load_tile(blockIdx.x + gridDim.x);
 #pragma unroll
-    for (int k = 0; k < NBLK; ++k) n2r[k] = n2buf[0][k * KB + j];
-    project(0, 0, cur0, cur1);
-  }
+  for (int p = 0; p < NBLK; ++p) load_part(blockIdx.x, p);
+#pragma unroll
+  for (int p = 0; p < NBLK; ++p) stage_part(0, p);
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NBLK; ++p) load_part(blockIdx.x + gridDim.x, p);
+#pragma unroll
+  for (int k = 0; k < NBLK; ++k) n2r[k] = n2buf[0][k * KB + j];
+  project(0, 0, cur0, cur1);
+  // Every value loaded before the loop is consumed here, so no wait for
+  // them lands inside the loop (where it would also wait for the prefetched
+  // tile and the stores).
+  asm volatile("" ::"s"(c1s));
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const bool more = tile + static_cast<int>(gridDim.x) < ntiles;   // uniform
-    // (batch * head, position) of the tile's first key, once per tile (the
-    // host keeps the key count below 2^31)
+    // per-tile geometry (uniform; the host keeps the key count below 2^31)
     const uint32_t tb = static_cast<uint32_t>(tile) * KT;
+    const uint32_t rows = min(uR - tb, static_cast<uint32_t>(KT));
     const uint32_t tbh = tb / un;
     const uint32_t toff = tb - tbh * un;
+    const bool straddle = toff + rows > un;   // rows of more than one (batch, head)
     const int64_t dst0 = static_cast<int64_t>(tbh) * cap + pos + toff;   // row tb's destination
-    const uint32_t wrap_at = un - toff;                                  // first row of the next (b, h)
-    const uint32_t wrap_add = static_cast<uint32_t>(cap) - un;
+    uint32_t* const sg_tile = signs + dst0 * WPR + (cb >> 5);
+    float* const nm_tile = norms + dst0;
     float n2n[NBLK];
+    // Words of blocks 0..2 wait in registers and are stored right after the
+    // barrier in block 3: no store then sits between the prefetched tile's
+    // loads and the wait for them (the memory counter retires in order).
+    uint32_t wbuf[NBLK - 1];
+    uint32_t okbits = 0;   // bit nb: store block nb's word; bit NBLK: store nbuf
+    float nbuf = 0.f;      // norm of this lane's key in block `wave`
+    // destination row of tile row rel when the tile straddles a (batch, head)
+    // boundary: the tile's first row plus rel, plus cap - n past each boundary
+    auto dst_straddle = [&](uint32_t rel) -> int64_t {
+      if (un > static_cast<uint32_t>(KT))   // at most one boundary within a tile
+        return dst0 + (rel + (rel >= un - toff ? static_cast<uint32_t>(cap) - un : 0u));
+      return dest_row(tb + rel, un, cap, pos);
+    };
+    auto store_word = [&](uint32_t rel, uint32_t word) {
+      if (!straddle) sg_tile[rel * WPR + half] = word;
+      else signs[dst_straddle(rel) * WPR + (cb >> 5) + half] = word;
+    };
+    auto store_norm = [&](uint32_t rel, float nrm) {
+      if (!straddle) nm_tile[rel] = nrm;
+      else norms[dst_straddle(rel)] = nrm;
+    };
+    auto flush_stores = [&]() {
+#pragma unroll
+      for (int nb = 0; nb < NBLK - 1; ++nb)
+        if (okbits & (1u << nb)) store_word(nb * KB + j, wbuf[nb]);
+      if (okbits & (1u << NBLK)) store_norm(wave * KB + j, nbuf);
+    };
 
     // ---- bits of one block: signs, certification, stores ----
     auto process = [&](int nb, const f32x16_t& acc0, const f32x16_t& acc1, float n2) {
-      // ---- certification threshold for this lane's key ----
-      // ||k|| <= sqrt(n2 (1 + 2^-14) + 2^-119): fp32 rounding of 128 exact
-      // squares plus squares lost below the fp32 normal range (with margin).
-      // (v_sqrt_f32 is within 1 ulp; the factor 1 + 2^-20 keeps the bound)
-      const float knorm_up =
-          __builtin_amdgcn_sqrtf(__builtin_fmaf(n2, 1.0f + 0x1.0p-14f, 0x1.0p-118f)) * (1.0f + 0x1.0p-20f);
-      const float tau = __builtin_fmaf(c1 * knorm_up, smax, c2);
-
-      // ---- sign word, highest coordinate shifted in first: acc1 gives bits
-      // 16..31, acc0 bits 0..15 ----
-      uint32_t sw = 0;
+      const float knorm_up = norm_bound(n2);
+      const float tau = __builtin_fmaf(c1s, knorm_up, c2);
+      const uint32_t word = sign_word(acc0, acc1);
       float amin1 = __builtin_fabsf(acc1[0]);
       float amin0 = __builtin_fabsf(acc0[0]);
-  #pragma unroll
-      for (int r = 15; r >= 0; --r) {
-        sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc1[r]), 31);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
         amin1 = fminf(amin1, __builtin_fabsf(acc1[r]));
-      }
-  #pragma unroll
-      for (int r = 15; r >= 0; --r) {
-        sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(acc0[r]), 31);
         amin0 = fminf(amin0, __builtin_fabsf(acc0[r]));
       }
-      uint32_t word = ~sw;
       // ---- flag bits (|acc| <= tau), each half only when some lane of the
       // wave has one there ----
       uint32_t fw1 = 0xFFFFu, fw0 = 0xFFFFu;   // set bit: not flagged
       if (__ballot(amin1 <= tau) != 0) {
         fw1 = 0;
-  #pragma unroll
+#pragma unroll
         for (int r = 15; r >= 0; --r) fw1 = __builtin_amdgcn_alignbit(fw1, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
       }
       if (__ballot(amin0 <= tau) != 0) {
         fw0 = 0;
-  #pragma unroll
+#pragma unroll
         for (int r = 15; r >= 0; --r) fw0 = __builtin_amdgcn_alignbit(fw0, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
       }
       uint32_t flags = ~((fw1 << 16) | fw0);
       // keys so large that products can overflow fp32: certify every bit
       if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
-      const uint32_t r = tb + nb * KB + j;
-      const bool valid = r < uR;
-      if (!valid) flags = 0;  // zero padding of a ragged last tile
-      // destination row: the tile's first row plus this row's offset, plus
-      // cap - n past a (batch, head) boundary
-      int64_t dst;
-      if (un > static_cast<uint32_t>(KT)) {   // at most one boundary within a tile
-        const uint32_t rel = nb * KB + j;
-        dst = dst0 + (rel + (rel >= wrap_at ? wrap_add : 0u));
-      } else {
-        const uint32_t off0 = toff + nb * KB + j;
-        const uint32_t w = off0 / un;
-        dst = static_cast<int64_t>(tbh + w) * cap + pos + (off0 - w * un);
-      }
+      const uint32_t rel = nb * KB + j;   // row within the tile
+      const bool valid = rel < rows;
+      if (!valid) flags = 0;              // zero padding of a ragged last tile
 
-      // ---- flagged words: queued for the exact fix after the last tile, or
-      // (queue full) fixed here, one (key, coordinate) pair at a time ----
+      // ---- flagged words: queued for the exact fix after the last tile;
+      // with the queue full they are stored as computed and the tile is
+      // re-run afterwards ----
       const uint64_t need = __ballot(flags != 0);
       bool deferred = false;
       if (need) {
         const int cnt = __popcll(need);
-        if (qn + cnt > QCAP) {   // full: decide the queued words now
-          flush(std::integral_constant<int, 1>{});
-          qn = 0;
-        }
         if (flags != 0) {
           const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
                                     static_cast<uint32_t>(need >> 32),
                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(need), 0u)));
-          fixq[wave][slot] = make_uint4(r | (static_cast<uint32_t>(half) << 31), word, flags, 0u);
-          fixn[wave][slot] = knorm_up;
-          deferred = true;
+          if (slot < QCAP) {
+            fixq[wave][slot] = make_uint4((tb + rel) | (static_cast<uint32_t>(half) << 31), word, flags, 0u);
+            fixn[wave][slot] = knorm_up;
+            deferred = true;
+          }
         }
-        qn += cnt;
+        if (qn + cnt > QCAP) {
+          if (ovf == INT_MAX) ovf = tile;
+          qn = QCAP;
+        } else {
+          qn += cnt;
+        }
       }
 
-      // ---- stores ----
-      if (valid) {
-        if (!deferred) signs[dst * WPR + (cb >> 5) + half] = word;
-        // the norm of block nb's keys is stored by wave nb (spreads the work)
-        if (wave == nb && half == 0) {
-          // v_sqrt_f32: within 1 ulp of the square root
-          float nrm = __builtin_amdgcn_sqrtf(n2);
-          if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) {
-            nrm = scaled_norm(keys + static_cast<int64_t>(r) * D);
-          }
-          norms[dst] = nrm;
+      // ---- stores; the norms of block nb's keys are stored by wave nb ----
+      const bool norm_lane = wave == nb && half == 0;
+      // v_sqrt_f32: within 1 ulp of the square root where n2 is accurate;
+      // keys outside that range are redone after the tile loop
+      const float nrm = __builtin_amdgcn_sqrtf(n2);
+      if (wave == nb) {
+        if (__ballot(half == 0 && valid && !(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) != 0) odd_norm = true;
+      }
+      if (nb < NBLK - 1) {
+        wbuf[nb] = word;
+        if (valid && !deferred) okbits |= 1u << nb;
+        if (norm_lane && valid) {
+          nbuf = nrm;
+          okbits |= 1u << NBLK;
         }
+      } else if (valid) {
+        if (!deferred) store_word(rel, word);
+        if (norm_lane) store_norm(rel, nrm);
       }
     };
 
+    const bool more = tile + static_cast<int>(gridDim.x) < ntiles;   // uniform
 #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) {
-      if (nb + 1 < NBLK) {
-        project(buf, nb + 1, nxt0, nxt1);
-      } else if (more) {   // publish the next tile, start its first block
-        stage(buf ^ 1);
-        __syncthreads();
-        if (tile + 2 * static_cast<int>(gridDim.x) < ntiles) load_tile(tile + 2 * gridDim.x);
+      if (nb + 1 < NBLK) project(buf, nb + 1, nxt0, nxt1);
+      // (after the last tile this stages zeros into the idle buffer, unread)
+      stage_part(buf ^ 1, nb);
+      load_part(tile + 2 * gridDim.x, nb);
+      if (nb + 1 == NBLK) {
+        if (more) {   // publish the next tile, start its first block
+          __syncthreads();
+          flush_stores();
 #pragma unroll
-        for (int k = 0; k < NBLK; ++k) n2n[k] = n2buf[buf ^ 1][k * KB + j];
-        project(buf ^ 1, 0, nxt0, nxt1);
+          for (int k = 0; k < NBLK; ++k) n2n[k] = n2buf[buf ^ 1][k * KB + j];
+          project(buf ^ 1, 0, nxt0, nxt1);
+        } else {
+          flush_stores();
+        }
       }
       process(nb, cur0, cur1, n2r[nb]);
       cur0 = nxt0;
@@ -535,7 +585,105 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     buf ^= 1;
   }
 
-  if (qn > 0) flush(std::integral_constant<int, 4>{});
+  // ---- after the tile loop: queued words, overflowed tiles, odd norms ----
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (qn > 0) fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
+                        long_scratch[wave], lane);
+  if (ovf != INT_MAX) {
+    // Re-run of this wave's tiles from the first one whose flagged words did
+    // not all fit: the same products from B fragments read straight from
+    // memory, every word stored again (certified as computed, or queued and
+    // decided exactly batch by batch).
+    qn = 0;
+    for (int tile = ovf; tile < ntiles; tile += gridDim.x) {
+      const uint32_t tb = static_cast<uint32_t>(tile) * KT;
+      const uint32_t rows = min(uR - tb, static_cast<uint32_t>(KT));
+      for (int nb = 0; nb < NBLK; ++nb) {
+        const uint32_t rel = nb * KB + j;
+        const bool valid = rel < rows;
+        // rows past the end read row tb (in bounds) and are never stored
+        const uint4* krow = reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(valid ? tb + rel : tb) * D);
+        float n2 = 0.f;
+        f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint4 v = krow[2 * s + half];
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), n2, false);
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), n2, false);
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(v.z), n2, false);
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(v.w), n2, false);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], as_bf16x8(v), acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], as_bf16x8(v), acc1, 0, 0, 0);
+        }
+        n2 += __shfl_xor(n2, 32);   // the other half of the key's channels
+        const float knorm_up = norm_bound(n2);
+        const float tau = __builtin_fmaf(c1s, knorm_up, c2);
+        const uint32_t word = sign_word(acc0, acc1);
+        uint32_t nf = 0;   // set bit: |acc| > tau (certified)
+#pragma unroll
+        for (int r = 15; r >= 0; --r) nf = __builtin_amdgcn_alignbit(nf, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
+#pragma unroll
+        for (int r = 15; r >= 0; --r) nf = __builtin_amdgcn_alignbit(nf, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
+        uint32_t fl = ~nf;
+        if (!(n2 < 0x1.0p100f)) fl = 0xFFFFFFFFu;
+        if (!valid) fl = 0;
+        if (valid && fl == 0) signs[dest_row(tb + rel, un, cap, pos) * WPR + (cb >> 5) + half] = word;
+        const uint64_t need = __ballot(fl != 0);
+        if (need) {
+          if (fl != 0) {
+            const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                      static_cast<uint32_t>(need >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(need), 0u)));
+            fixq[wave][slot] = make_uint4((tb + rel) | (static_cast<uint32_t>(half) << 31), word, fl, 0u);
+            fixn[wave][slot] = knorm_up;
+          }
+          qn += __popcll(need);
+          if (qn > QCAP - 64) {   // no room for another block's words: decide these now
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
+                      long_scratch[wave], lane);
+            qn = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (qn > 0) fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
+                          long_scratch[wave], lane);
+  }
+  if (odd_norm) {
+    // norms of this wave's blocks (nb == wave), one lane per key, with the
+    // scaled evaluation where the fp32 sum of squares is inaccurate
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+      const uint32_t tb = static_cast<uint32_t>(tile) * KT;
+      const uint32_t rows = min(uR - tb, static_cast<uint32_t>(KT));
+      const uint32_t rel = wave * KB + j;
+      if (half == 0 && rel < rows) {
+        const uint16_t* key = keys + static_cast<int64_t>(tb + rel) * D;
+        const uint4* kr = reinterpret_cast<const uint4*>(key);
+        float n2 = 0.f;
+        for (int c = 0; c < 16; ++c) {
+          const uint4 v = kr[c];
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), n2, false);
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), n2, false);
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(v.z), n2, false);
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(v.w), n2, false);
+        }
+        float nrm = __builtin_amdgcn_sqrtf(n2);
+        if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) nrm = scaled_norm(key);
+        norms[dest_row(tb + rel, un, cap, pos)] = nrm;
+      }
+    }
+  }
 }
 
 template <int M>

@@ -20,10 +20,10 @@ struct DeviceSketch {
   // [m/32 blocks][8 k-steps][64 lanes][8 bf16], lane l holding
   // S^T[32*block + l%32][16*kstep + 8*(l/32) .. +7] (decode: S^T q)
   const uint16_t* s_frag = nullptr;
-  // S^T in the lane order of the encode's resident A operand
-  // (v_mfma_f32_32x32x16_bf16): [m/64 waves][2 blocks][8 k-steps][64 lanes][8
-  // bf16], lane (j, h) of (wave w, block b, k-step s) holding
-  // S^T[64w + 32((j >> 2) & 1) + 16b + 4(j >> 3) + (j & 3)][16s + 8h .. +7]
+  // -S^T (sign bits flipped) in the lane order of the encode's resident A
+  // operand (v_mfma_f32_32x32x16_bf16): [m/64 waves][2 blocks][8 k-steps][64
+  // lanes][8 bf16], lane (j, h) of (wave w, block b, k-step s) holding
+  // -S^T[64w + 32((j >> 2) & 1) + 16b + 4(j >> 3) + (j & 3)][16s + 8h .. +7]
   // (j = lane % 32, h = lane / 32), so each (w, b, s) is one contiguous 1 KB load.
   const uint16_t* s_efrag = nullptr;
   const float* col_norm_max = nullptr;  // [m/64] max_{i in group} ||S[:, i]||_2, rounded up

@@ -94,7 +94,7 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
           const int coord = 64 * w + 32 * ((jj >> 2) & 1) + 16 * b + 4 * (jj >> 3) + (jj & 3);
           for (int e = 0; e < 8; ++e)
             s_efrag[(((static_cast<size_t>(w) * 2 + b) * (d / 16) + st) * 64 + l) * 8 + e] =
-                s_md[static_cast<size_t>(coord) * d + 16 * st + 8 * hh + e];
+                static_cast<uint16_t>(s_md[static_cast<size_t>(coord) * d + 16 * st + 8 * hh + e] ^ 0x8000u);
         }
   const size_t bytes_s = n * sizeof(uint16_t);
   const size_t padded = (bytes_s + 255) / 256 * 256;
