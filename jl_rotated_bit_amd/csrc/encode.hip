@@ -349,8 +349,17 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   // 16 c); the 16 chunks of a row belong to 16 consecutive threads (one DPP
   // row).  Rows past the end of the keys read as zero.
   uint4 pf[LOADS];
+  // Part p of a tile is block p (rows 32p .. 32p+31, 512 chunks of 16
+  // bytes).  A thread holds CPT chunks of one row: L = 16 / CPT consecutive
+  // lanes cover a row, lane i its chunks i, i + L, ...  Each group of L lanes
+  // reads whole 128-byte lines, and a key's squared norm needs a sum over L
+  // lanes only.
   constexpr int LPB = LOADS / NBLK;   // chunks staged (and reloaded) per block
-  static_assert(LOADS % NBLK == 0, "chunks must split evenly over the blocks");
+  constexpr int CPT = LPB;            // chunks per thread per row
+  constexpr int L = 16 / CPT;         // lanes per row
+  static_assert(LOADS % NBLK == 0 && (L == 8 || L == 16), "unsupported chunk split");
+  const int prow = tid / L;           // row within the block
+  const int pcol = tid % L;           // first chunk
   // (a tile past the end gets an empty descriptor: its loads return zeros
   // and touch no memory, so every load in the loop is unconditional and the
   // compiler's wait counts stay exact)
@@ -359,30 +368,32 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     const uint32_t rows = tb < uR ? min(uR - tb, static_cast<uint32_t>(KT)) : 0u;
     const rsrc_t rs = make_rsrc(keys + static_cast<int64_t>(tb) * D, static_cast<int>(rows) * ROW_B);
 #pragma unroll
-    for (int k = part * LPB; k < (part + 1) * LPB; ++k)
-      pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + k * NT) * 16, 0, 0));
+    for (int i = 0; i < CPT; ++i)
+      pf[part * CPT + i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (part * KB + prow) * ROW_B + (pcol + L * i) * 16, 0, 0));
   };
 
   // staged chunks -> LDS tile bb, and their keys' squared norms ->
-  // n2buf[bb]: each thread squares its chunks (bf16 dot2, fp32), a DPP row
-  // sum adds the 16 chunks of a key
+  // n2buf[bb]: each thread squares its chunks (bf16 dot2, fp32), then a DPP
+  // all-reduce over the row's L lanes (pairs xor 1, xor 2, then the mirror
+  // within 8 lanes, then within 16)
   auto stage_part = [&](int bb, int part) {
-    uint8_t* t = lds + bb * TILE_LDS;
+    uint8_t* t = lds + bb * TILE_LDS + (part * KB + prow) * LDS_ROW;
+    float q = 0.f;
 #pragma unroll
-    for (int k = part * LPB; k < (part + 1) * LPB; ++k) {
-      const uint4 v = pf[k];
-      float q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), 0.f, false);
+    for (int i = 0; i < CPT; ++i) {
+      const uint4 v = pf[part * CPT + i];
+      q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), q, false);
       q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), q, false);
       q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(v.z), q, false);
       q = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(v.w), q, false);
-      q += dpp_f32<0x128>(q);   // row_ror:8
-      q += dpp_f32<0x124>(q);   // row_ror:4
-      q += dpp_f32<0x122>(q);   // row_ror:2
-      q += dpp_f32<0x121>(q);   // row_ror:1
-      *((tid & 15) == 0 ? &n2buf[bb][(tid >> 4) + k * (NT / 16)] : &n2sink[wave][lane]) = q;
-      const int c = tid + k * NT;
-      *reinterpret_cast<uint4*>(t + (c >> 4) * LDS_ROW + (c & 15) * 16) = v;
+      *reinterpret_cast<uint4*>(t + (pcol + L * i) * 16) = v;
     }
+    q += dpp_f32<0xB1>(q);    // quad_perm [1, 0, 3, 2]
+    q += dpp_f32<0x4E>(q);    // quad_perm [2, 3, 0, 1]
+    q += dpp_f32<0x141>(q);   // row_half_mirror
+    if constexpr (L == 16) q += dpp_f32<0x140>(q);   // row_mirror
+    *(pcol == 0 ? &n2buf[bb][part * KB + prow] : &n2sink[wave][lane]) = q;
   };
 
   // ---- projection on the matrix cores (block nb of LDS tile bb) ----
@@ -492,39 +503,25 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
         amin1 = fminf(amin1, __builtin_fabsf(acc1[r]));
         amin0 = fminf(amin0, __builtin_fabsf(acc0[r]));
       }
-      // ---- flag bits (|acc| <= tau), each half only when some lane of the
-      // wave has one there ----
-      uint32_t fw1 = 0xFFFFu, fw0 = 0xFFFFu;   // set bit: not flagged
-      if (__ballot(amin1 <= tau) != 0) {
-        fw1 = 0;
-#pragma unroll
-        for (int r = 15; r >= 0; --r) fw1 = __builtin_amdgcn_alignbit(fw1, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
-      }
-      if (__ballot(amin0 <= tau) != 0) {
-        fw0 = 0;
-#pragma unroll
-        for (int r = 15; r >= 0; --r) fw0 = __builtin_amdgcn_alignbit(fw0, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
-      }
-      uint32_t flags = ~((fw1 << 16) | fw0);
-      // keys so large that products can overflow fp32: certify every bit
-      if (!(n2 < 0x1.0p100f)) flags = 0xFFFFFFFFu;
+      // ---- a word with some |acc| <= tau (or a key whose fp32 norm left
+      // the range the bound is proved for) is queued for the exact fix after
+      // the last tile, which finds its flagged bits; with the queue full it
+      // is stored as computed and the tile is re-run afterwards ----
       const uint32_t rel = nb * KB + j;   // row within the tile
-      const bool valid = rel < rows;
-      if (!valid) flags = 0;              // zero padding of a ragged last tile
-
-      // ---- flagged words: queued for the exact fix after the last tile;
-      // with the queue full they are stored as computed and the tile is
-      // re-run afterwards ----
-      const uint64_t need = __ballot(flags != 0);
+      const bool valid = rel < rows;      // (zero padding of a ragged last tile)
+      const bool huge = !(n2 < 0x1.0p100f);
+      const uint64_t need = __ballot(valid && (fminf(amin1, amin0) <= tau || huge));
       bool deferred = false;
       if (need) {
         const int cnt = __popcll(need);
-        if (flags != 0) {
+        if ((need >> lane) & 1) {
           const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
                                     static_cast<uint32_t>(need >> 32),
                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(need), 0u)));
           if (slot < QCAP) {
-            fixq[wave][slot] = make_uint4((tb + rel) | (static_cast<uint32_t>(half) << 31), word, flags, 0u);
+            // flags: all bits for a huge key, else found after the loop
+            fixq[wave][slot] = make_uint4((tb + rel) | (static_cast<uint32_t>(half) << 31), word,
+                                          huge ? 0xFFFFFFFFu : 0u, 0u);
             fixn[wave][slot] = knorm_up;
             deferred = true;
           }
@@ -589,8 +586,38 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (qn > 0) fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
-                        long_scratch[wave], lane);
+  if (qn > 0) {
+    // Flagged bits of the queued words: the queued keys are multiplied again
+    // (entry e in column e % 32), and the word and its flags are taken from
+    // these products, so nothing depends on the loop's column order.
+    for (int e0 = 0; e0 < qn; e0 += 32) {
+      const int e = e0 + j;
+      const bool act = e < qn;
+      const uint4 ent = fixq[wave][act ? e : 0];
+      const uint4* krow = reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(ent.x & 0x7FFFFFFFu) * D);
+      f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8_t v = as_bf16x8(krow[2 * s + half]);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], v, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], v, acc1, 0, 0, 0);
+      }
+      if (act && static_cast<int>(ent.x >> 31) == half) {
+        const float tau = __builtin_fmaf(c1s, fixn[wave][e], c2);
+        uint32_t nf = 0;   // set bit: |acc| > tau (certified)
+#pragma unroll
+        for (int r = 15; r >= 0; --r) nf = __builtin_amdgcn_alignbit(nf, __float_as_uint(tau - __builtin_fabsf(acc1[r])), 31);
+#pragma unroll
+        for (int r = 15; r >= 0; --r) nf = __builtin_amdgcn_alignbit(nf, __float_as_uint(tau - __builtin_fabsf(acc0[r])), 31);
+        fixq[wave][e].y = sign_word(acc0, acc1);
+        fixq[wave][e].z |= ~nf;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR, long_scratch[wave], lane);
+  }
   if (ovf != INT_MAX) {
     // Re-run of this wave's tiles from the first one whose flagged words did
     // not all fit: the same products from B fragments read straight from
