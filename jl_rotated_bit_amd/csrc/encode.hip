@@ -330,25 +330,11 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   const uint32_t un = static_cast<uint32_t>(n);
   const uint32_t uR = static_cast<uint32_t>(R);
 
-  // Resident A operand: -S^T rows for this wave's coordinates.  Block b, row
-  // i holds coordinate cb + 32*((i >> 2) & 1) + 16*b + 4*(i >> 3) + (i & 3),
-  // so the 32x32 result places coordinate cb + 32*half + 16*b + r in
-  // register r of lane (j, half).
-  // (s_efrag holds these fragments in lane order: one 1 KB load each)
-  bf16x8_t a[2][8];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const uint4* fr = reinterpret_cast<const uint4*>(s_efrag) + (static_cast<int64_t>(wave) * 2 + b) * 8 * 64 + lane;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) a[b][s] = as_bf16x8(fr[s * 64]);
-  }
+  bf16x8_t a[2][8];   // loaded after the first tile's requests (see below)
   const float smax = col_norm_max[wave];
   const float c1s = c1 * smax;   // tau = c1s * ||k||_up + c2
 
-  // chunk c of a tile: key row c / 16, 16-byte column c % 16 (byte offset
-  // 16 c); the 16 chunks of a row belong to 16 consecutive threads (one DPP
-  // row).  Rows past the end of the keys read as zero.
-  uint4 pf[LOADS];
+  uint4 pf[LOADS];   // 16-byte key chunks in flight (rows past the end read as zero)
   // Part p of a tile is block p (rows 32p .. 32p+31, 512 chunks of 16
   // bytes).  A thread holds CPT chunks of one row: L = 16 / CPT consecutive
   // lanes cover a row, lane i its chunks i, i + L, ...  Each group of L lanes
@@ -440,6 +426,19 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   float n2r[NBLK];
 #pragma unroll
   for (int p = 0; p < NBLK; ++p) load_part(blockIdx.x, p);
+  // (the first tile's memory requests go out before the L2-resident
+  // sketch fragments)
+  // Resident A operand: -S^T rows for this wave's coordinates.  Block b, row
+  // i holds coordinate cb + 32*((i >> 2) & 1) + 16*b + 4*(i >> 3) + (i & 3),
+  // so the 32x32 result places coordinate cb + 32*half + 16*b + r in
+  // register r of lane (j, half).
+  // (s_efrag holds these fragments in lane order: one 1 KB load each)
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint4* fr = reinterpret_cast<const uint4*>(s_efrag) + (static_cast<int64_t>(wave) * 2 + b) * 8 * 64 + lane;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) a[b][s] = as_bf16x8(fr[s * 64]);
+  }
 #pragma unroll
   for (int p = 0; p < NBLK; ++p) stage_part(0, p);
   __syncthreads();
