@@ -494,7 +494,24 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     auto process = [&](int nb, const f32x16_t& acc0, const f32x16_t& acc1, float n2) {
       const float knorm_up = norm_bound(n2);
       const float tau = __builtin_fmaf(c1s, knorm_up, c2);
-      const uint32_t word = sign_word(acc0, acc1);
+      uint32_t word = sign_word(acc0, acc1);
+      // An all-(+/-)zero key projects to exactly 0, every bit 1: found through
+      // n2 == 0 and a look at its row in LDS (rare), so padding rows never
+      // reach the exact fix.
+      bool zero_key = false;
+      if (__ballot(n2 == 0.f) != 0) {
+        const uint4* zr = reinterpret_cast<const uint4*>(lds + buf * TILE_LDS + (nb * KB + j) * LDS_ROW + 128 * half);
+        uint32_t o = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint4 v = zr[c];
+          o |= v.x | v.y | v.z | v.w;
+        }
+        o &= 0x7FFF7FFFu;
+        o |= __shfl_xor(o, 32);   // the other half of the row
+        zero_key = n2 == 0.f && o == 0;
+        if (zero_key) word = 0xFFFFFFFFu;
+      }
       float amin1 = __builtin_fabsf(acc1[0]);
       float amin0 = __builtin_fabsf(acc0[0]);
 #pragma unroll
@@ -509,7 +526,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       const uint32_t rel = nb * KB + j;   // row within the tile
       const bool valid = rel < rows;      // (zero padding of a ragged last tile)
       const bool huge = !(n2 < 0x1.0p100f);
-      const uint64_t need = __ballot(valid && (fminf(amin1, amin0) <= tau || huge));
+      const uint64_t need = __ballot(valid && !zero_key && (fminf(amin1, amin0) <= tau || huge));
       bool deferred = false;
       if (need) {
         const int cnt = __popcll(need);
@@ -539,7 +556,8 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       // keys outside that range are redone after the tile loop
       const float nrm = __builtin_amdgcn_sqrtf(n2);
       if (wave == nb) {
-        if (__ballot(half == 0 && valid && !(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) != 0) odd_norm = true;
+        if (__ballot(half == 0 && valid && !zero_key && !(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) != 0)
+          odd_norm = true;
       }
       if (nb < NBLK - 1) {
         wbuf[nb] = word;

@@ -134,6 +134,22 @@ def test_certification_queue_fills_and_overflows(gpu_lib, m):
     check_encode(gpu_lib, K.reshape(1, 1, n, 128), m, label="queue overflow")
 
 
+@pytest.mark.parametrize("m", [256, 512])
+def test_zero_padding_rows(gpu_lib, m):
+    """All-(+/-)zero rows (padding) mixed with ordinary keys, in runs and
+    one by one: every bit of a zero row is 1 and its norm is 0, and the
+    ordinary rows around them are unaffected."""
+    rng = np.random.default_rng(300 + m)
+    B, H, n = 1, 1, 1500
+    K = wl.gaussian_keys(rng, B * H * n).reshape(B, H, n, 128)
+    K[:, :, ::3] = 0                  # every third row
+    K[0, 0, 300:900] = 0              # a long run, spanning several 128-row tiles
+    K[0, 0, 7] = 0x8000               # -0.0 everywhere
+    got_w, got_n = check_encode(gpu_lib, K, m, label="zero padding")
+    assert np.all(got_w[0, 0, 300:900] == 0xFFFFFFFF) and np.all(got_n[0, 0, 300:900] == 0)
+    assert np.all(got_w[0, 0, 7] == 0xFFFFFFFF)
+
+
 def test_matches_exact_rationals_on_cancellations(gpu_lib):
     """Brute force with Fractions on rows built to cancel exactly or almost."""
     S = oracle.sketch(SEED, 128, 256)
