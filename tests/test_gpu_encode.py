@@ -185,6 +185,20 @@ def test_mha16k_keys_sampled(gpu_lib):
     check_encode(gpu_lib, w.keys, w.m, sample_rows=rows, label="mha16k keys (sampled rows)")
 
 
+def test_large_ragged_uneven_split(gpu_lib):
+    """Enough tiles that the first workgroup of each CU takes a larger share,
+    with a tile count that is no multiple of the grid and a per-head row
+    count that is no multiple of the 128-row tile (tiles cross heads);
+    every row of the first and last tiles plus a sample in between."""
+    rng = np.random.default_rng(11)
+    B, H, n = 1, 8, 32768 + 77
+    keys = wl.gaussian_keys(rng, B * H * n).reshape(B, H, n, 128)
+    R = B * H * n
+    rows = np.unique(np.concatenate([np.arange(0, 4096), np.arange(R - 4096, R),
+                                     np.random.default_rng(12).choice(R, 30_000, replace=False)]))
+    check_encode(gpu_lib, keys, 256, cap=n + 5, pos=3, sample_rows=rows, label="large ragged")
+
+
 def test_other_seed(gpu_lib):
     rng = np.random.default_rng(3)
     keys = wl.gaussian_keys(rng, 4000).reshape(1, 4, 1000, 128)
