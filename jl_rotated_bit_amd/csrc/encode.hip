@@ -40,6 +40,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -460,7 +461,9 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   // them lands inside the loop (where it would also wait for the prefetched
   // tile and the stores).
   asm volatile("" ::"s"(c1s));
-  for (int tile = t_first; tile < t_end; tile += t_step) {
+  // One tile; the last one (LAST) stages and prefetches nothing.
+  auto tile_step = [&](int tile, auto last_c) {
+    constexpr bool LAST = decltype(last_c)::value;
     // per-tile geometry (uniform; the host keeps the key count below 2^31)
     const uint32_t tb = static_cast<uint32_t>(tile) * KT;
     const uint32_t rows = min(uR - tb, static_cast<uint32_t>(KT));
@@ -581,15 +584,16 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       }
     };
 
-    const bool more = tile + t_step < t_end;   // uniform
+    constexpr bool more = !LAST;
 #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) {
       if (nb + 1 < NBLK) project(buf, nb + 1, nxt0, nxt1);
-      // (after the last tile this stages zeros into the idle buffer, unread)
-      stage_part(buf ^ 1, nb);
-      load_part(tile + 2 * t_step, nb);
+      if constexpr (more) {
+        stage_part(buf ^ 1, nb);
+        load_part(tile + 2 * t_step, nb);   // (past the range: an empty descriptor)
+      }
       if (nb + 1 == NBLK) {
-        if (more) {   // publish the next tile, start its first block
+        if constexpr (more) {   // publish the next tile, start its first block
           __syncthreads();
           flush_stores();
 #pragma unroll
@@ -603,10 +607,32 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       cur0 = nxt0;
       cur1 = nxt1;
     }
+    if constexpr (more) {
 #pragma unroll
-    for (int k = 0; k < NBLK; ++k) n2r[k] = n2n[k];
-    buf ^= 1;
+      for (int k = 0; k < NBLK; ++k) n2r[k] = n2n[k];
+      buf ^= 1;
+    }
+  };
+  int tile = t_first;
+  for (; tile + t_step < t_end; tile += t_step) tile_step(tile, std::false_type{});
+  // The last tile needs no staging, so its registers carry the re-
+  // multiplication's first 32 keys (queued so far): their loads run while
+  // the tile is multiplied.  Keys queued during the last tile are read from
+  // its LDS buffer afterwards.
+  const int qn_pre = qn;
+  const uint32_t tb_last = static_cast<uint32_t>(tile) * KT;
+  uint4 fb[8];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // queue entries of other lanes
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  {
+    const uint4 ent = fixq[wave][j < qn_pre ? j : 0];
+    const uint32_t row = j < qn_pre ? (ent.x & 0x7FFFFFFFu) : 0u;   // row 0: in bounds, unused
+    const uint4* krow = reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(row) * D);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) fb[s] = krow[2 * s + half];
   }
+  tile_step(tile, std::true_type{});
 
   // ---- after the tile loop: queued words, overflowed tiles, odd norms ----
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -620,13 +646,27 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       const int e = e0 + j;
       const bool act = e < qn;
       const uint4 ent = fixq[wave][act ? e : 0];
-      const uint4* krow = reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(ent.x & 0x7FFFFFFFu) * D);
+      const uint32_t row = ent.x & 0x7FFFFFFFu;
       f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
+      if (e0 == 0) {   // prefetched keys, or the last tile's rows in LDS
+        const bool in_lds = e >= qn_pre;
+        const uint32_t rel = in_lds && act ? row - tb_last : 0u;
+        const uint8_t* lrow = lds + buf * TILE_LDS + rel * LDS_ROW + 16 * half;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8_t v = as_bf16x8(krow[2 * s + half]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], v, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], v, acc1, 0, 0, 0);
+        for (int s = 0; s < 8; ++s) {
+          const uint4 l = *reinterpret_cast<const uint4*>(lrow + 32 * s);
+          const bf16x8_t v = as_bf16x8(in_lds ? l : fb[s]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], v, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], v, acc1, 0, 0, 0);
+        }
+      } else {
+        const uint4* krow = reinterpret_cast<const uint4*>(keys + static_cast<int64_t>(row) * D);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8_t v = as_bf16x8(krow[2 * s + half]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], v, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], v, acc1, 0, 0, 0);
+        }
       }
       if (act && static_cast<int>(ent.x >> 31) == half) {
         const float tau = __builtin_fmaf(c1s, fixn[wave][e], c2);
