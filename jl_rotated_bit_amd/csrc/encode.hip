@@ -298,7 +298,9 @@ __device__ __forceinline__ void fix_queue(const uint4* fq, const float* fk, int 
   }
 }
 
-template <int M>
+// ALIGNED: n is a multiple of the 128-key tile, so every tile is full and
+// lies within one (batch, head).
+template <int M, bool ALIGNED>
 __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2))) void encode_kernel(
     const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md,
     const uint16_t* __restrict__ s_efrag, const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   // compiler's wait counts stay exact)
   auto load_part = [&](int tile, int part) {
     const uint32_t tb = static_cast<uint32_t>(tile) * KT;
-    const uint32_t rows = tile < t_end ? min(uR - tb, static_cast<uint32_t>(KT)) : 0u;
+    const uint32_t rows = tile < t_end ? (ALIGNED ? static_cast<uint32_t>(KT) : min(uR - tb, static_cast<uint32_t>(KT))) : 0u;
     const rsrc_t rs = make_rsrc(keys + static_cast<int64_t>(tb) * D, static_cast<int>(rows) * ROW_B);
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
@@ -466,10 +468,10 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     constexpr bool LAST = decltype(last_c)::value;
     // per-tile geometry (uniform; the host keeps the key count below 2^31)
     const uint32_t tb = static_cast<uint32_t>(tile) * KT;
-    const uint32_t rows = min(uR - tb, static_cast<uint32_t>(KT));
+    const uint32_t rows = ALIGNED ? static_cast<uint32_t>(KT) : min(uR - tb, static_cast<uint32_t>(KT));
     const uint32_t tbh = tb / un;
     const uint32_t toff = tb - tbh * un;
-    const bool straddle = toff + rows > un;   // rows of more than one (batch, head)
+    const bool straddle = !ALIGNED && toff + rows > un;   // rows of more than one (batch, head)
     const int64_t dst0 = static_cast<int64_t>(tbh) * cap + pos + toff;   // row tb's destination
     uint32_t* const sg_tile = signs + dst0 * WPR + (cb >> 5);
     float* const nm_tile = norms + dst0;
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
       // the last tile, which finds its flagged bits; with the queue full it
       // is stored as computed and the tile is re-run afterwards ----
       const uint32_t rel = nb * KB + j;   // row within the tile
-      const bool valid = rel < rows;      // (zero padding of a ragged last tile)
+      const bool valid = ALIGNED || rel < rows;   // (zero padding of a ragged last tile)
       const bool huge = !(n2 < 0x1.0p100f);
       const uint64_t need = __ballot(valid && !zero_key && (fminf(amin1, amin0) <= tau || huge));
       bool deferred = false;
@@ -779,8 +781,8 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
-template <int M>
-int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
+template <int M, bool ALIGNED>
+int launch_encode_mt(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
                     float* norms, int cap, int pos, hipStream_t stream) {
   constexpr int NT = 64 * (M / CW);
   const int ntiles = static_cast<int>((static_cast<int64_t>(R) + KT - 1) / KT);
@@ -791,7 +793,7 @@ int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint3
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidDevice;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_kernel<M>, NT, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_kernel<M, ALIGNED>, NT, 0) !=
         hipSuccess)
       return hipErrorInvalidDeviceFunction;
     wg_per_cu = per_cu > 0 ? per_cu : 1;
@@ -815,10 +817,17 @@ int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint3
   // over round-to-nearest (covers truncating or blocked accumulation).
   const float c1 = static_cast<float>(4.0 * D * 0x1.0p-24 * (1.0 + 0x1.0p-10));
   const float c2 = 0x1.0p-110f;  // absolute floor: subnormal flushes
-  hipLaunchKernelGGL(encode_kernel<M>, dim3(grid), dim3(NT), 0, stream,
+  hipLaunchKernelGGL((encode_kernel<M, ALIGNED>), dim3(grid), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(keys), s.s_md, s.s_efrag, s.col_norm_max, signs, norms, R,
                      n, cap, pos, ntiles, ga, ta, c1, c2);
   return hipGetLastError();
+}
+
+template <int M>
+int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
+                    float* norms, int cap, int pos, hipStream_t stream) {
+  if (n % KT == 0) return launch_encode_mt<M, true>(s, keys, R, n, signs, norms, cap, pos, stream);
+  return launch_encode_mt<M, false>(s, keys, R, n, signs, norms, cap, pos, stream);
 }
 
 }  // namespace
