@@ -61,7 +61,7 @@ constexpr int LDS_ROW = ROW_B + 16;  // padded LDS row: spreads lanes over banks
 constexpr int TILE_LDS = KT * LDS_ROW;
 constexpr int CHUNKS = KT * ROW_B / 16;  // 16-byte chunks per key tile (2048)
 constexpr int ACC_WORDS = 18;        // long accumulator: 576 bits
-constexpr int QCAP = 64;             // deferred-fix queue entries per wave
+constexpr int QCAP = 112;            // deferred-fix queue entries per wave
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
@@ -205,7 +205,7 @@ __device__ __forceinline__ int64_t dest_row(uint32_t r, uint32_t un, int cap, in
 __device__ __forceinline__ void fix_queue(const uint4* fq, const float* fk, int qn, const uint16_t* keys,
                                           const uint16_t* s_md, int cb, float smax, uint32_t* signs,
                                           uint32_t un, int cap, int pos, int wpr, uint32_t* scratch,
-                                          int lane) {
+                                          int lane, uint32_t r0) {
   const int g = lane >> 2, sub = lane & 3;
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   for (int base = 0; base < qn; base += 16) {
@@ -294,7 +294,7 @@ __device__ __forceinline__ void fix_queue(const uint4* fq, const float* fk, int 
         if ((lane >> 2) == (src >> 2)) word = bit ? (word | (1u << q)) : (word & ~(1u << q));
       }
     }
-    if (sub == 0 && act) signs[dest_row(row, un, cap, pos) * wpr + (cb >> 5) + hf] = word;
+    if (sub == 0 && act) signs[dest_row(r0 + row, un, cap, pos) * wpr + (cb >> 5) + hf] = word;
   }
 }
 
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md,
     const uint16_t* __restrict__ s_efrag, const float* __restrict__ col_norm_max, uint32_t* __restrict__ signs,
     float* __restrict__ norms, int R, int n, int cap, int pos, int ntiles, int ga, int ta, float c1,
-    float c2) {
+    float c2, int r0_) {
   constexpr int W = M / CW;
   constexpr int NT = 64 * W;
   constexpr int LOADS = CHUNKS / NT;  // 16-byte loads per thread per tile
@@ -341,6 +341,9 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
   const int cb = wave * CW;
   const uint32_t un = static_cast<uint32_t>(n);
   const uint32_t uR = static_cast<uint32_t>(R);
+  // keys and rows are local to this launch; r0 is the global row of local
+  // row 0 (destination rows are computed from global rows)
+  const uint32_t r0 = static_cast<uint32_t>(r0_);
 
   bf16x8_t a[2][8];   // loaded after the first tile's requests (see below)
   const float smax = col_norm_max[wave];
@@ -469,8 +472,8 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     // per-tile geometry (uniform; the host keeps the key count below 2^31)
     const uint32_t tb = static_cast<uint32_t>(tile) * KT;
     const uint32_t rows = ALIGNED ? static_cast<uint32_t>(KT) : min(uR - tb, static_cast<uint32_t>(KT));
-    const uint32_t tbh = tb / un;
-    const uint32_t toff = tb - tbh * un;
+    const uint32_t tbh = (r0 + tb) / un;
+    const uint32_t toff = r0 + tb - tbh * un;
     const bool straddle = !ALIGNED && toff + rows > un;   // rows of more than one (batch, head)
     const int64_t dst0 = static_cast<int64_t>(tbh) * cap + pos + toff;   // row tb's destination
     uint32_t* const sg_tile = signs + dst0 * WPR + (cb >> 5);
@@ -487,7 +490,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     auto dst_straddle = [&](uint32_t rel) -> int64_t {
       if (un > static_cast<uint32_t>(KT))   // at most one boundary within a tile
         return dst0 + (rel + (rel >= un - toff ? static_cast<uint32_t>(cap) - un : 0u));
-      return dest_row(tb + rel, un, cap, pos);
+      return dest_row(r0 + tb + rel, un, cap, pos);
     };
     auto store_word = [&](uint32_t rel, uint32_t word) {
       if (!straddle) sg_tile[rel * WPR + half] = word;
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR, long_scratch[wave], lane);
+    fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR, long_scratch[wave], lane, r0);
   }
   if (ovf != INT_MAX) {
     // Re-run of this wave's tiles from the first one whose flagged words did
@@ -724,7 +727,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
         uint32_t fl = ~nf;
         if (!(n2 < 0x1.0p100f)) fl = 0xFFFFFFFFu;
         if (!valid) fl = 0;
-        if (valid && fl == 0) signs[dest_row(tb + rel, un, cap, pos) * WPR + (cb >> 5) + half] = word;
+        if (valid && fl == 0) signs[dest_row(r0 + tb + rel, un, cap, pos) * WPR + (cb >> 5) + half] = word;
         const uint64_t need = __ballot(fl != 0);
         if (need) {
           if (fl != 0) {
@@ -740,7 +743,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
-                      long_scratch[wave], lane);
+                      long_scratch[wave], lane, r0);
             qn = 0;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (qn > 0) fix_queue(fixq[wave], fixn[wave], qn, keys, s_md, cb, smax, signs, un, cap, pos, WPR,
-                          long_scratch[wave], lane);
+                          long_scratch[wave], lane, r0);
   }
   if (odd_norm) {
     // norms of this wave's blocks (nb == wave), one lane per key, with the
@@ -775,18 +778,18 @@ __global__ __launch_bounds__(64 * (M / CW)) __attribute__((amdgpu_waves_per_eu(2
         }
         float nrm = __builtin_amdgcn_sqrtf(n2);
         if (!(n2 >= 0x1.0p-100f && n2 <= 0x1.0p100f)) nrm = scaled_norm(key);
-        norms[dest_row(tb + rel, un, cap, pos)] = nrm;
+        norms[dest_row(r0 + tb + rel, un, cap, pos)] = nrm;
       }
     }
   }
 }
 
+// Resident workgroups of encode_kernel<M, ALIGNED> per CU and on the device
+// (fixed per template and device model; queried once).
 template <int M, bool ALIGNED>
-int launch_encode_mt(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
-                    float* norms, int cap, int pos, hipStream_t stream) {
+int encode_occupancy(int* max_grid_out, int* wg_per_cu_out) {
   constexpr int NT = 64 * (M / CW);
-  const int ntiles = static_cast<int>((static_cast<int64_t>(R) + KT - 1) / KT);
-  static int max_grid = 0;  // resident workgroups on this device (fixed per template)
+  static int max_grid = 0;
   static int wg_per_cu = 0;
   if (max_grid == 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -799,6 +802,17 @@ int launch_encode_mt(const DeviceSketch& s, const void* keys, int R, int n, uint
     wg_per_cu = per_cu > 0 ? per_cu : 1;
     max_grid = cus * wg_per_cu;
   }
+  *max_grid_out = max_grid;
+  *wg_per_cu_out = wg_per_cu;
+  return hipSuccess;
+}
+
+// One launch over local rows [0, R) of keys, whose global row 0 is r0.
+template <int M, bool ALIGNED>
+int launch_encode_mt(const void* keys, int R, int r0, const DeviceSketch& s, int n, uint32_t* signs,
+                     float* norms, int cap, int pos, int max_grid, int wg_per_cu, hipStream_t stream) {
+  constexpr int NT = 64 * (M / CW);
+  const int ntiles = static_cast<int>((static_cast<int64_t>(R) + KT - 1) / KT);
   const int grid = ntiles < max_grid ? ntiles : max_grid;
   // Two workgroups per CU: the one dispatched first (index below grid/2)
   // keeps the older waves, which win instruction issue; its first tile
@@ -819,15 +833,40 @@ int launch_encode_mt(const DeviceSketch& s, const void* keys, int R, int n, uint
   const float c2 = 0x1.0p-110f;  // absolute floor: subnormal flushes
   hipLaunchKernelGGL((encode_kernel<M, ALIGNED>), dim3(grid), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(keys), s.s_md, s.s_efrag, s.col_norm_max, signs, norms, R,
-                     n, cap, pos, ntiles, ga, ta, c1, c2);
+                     n, cap, pos, ntiles, ga, ta, c1, c2, r0);
   return hipGetLastError();
+}
+
+// Keys are encoded in launches of at most kMaxTilesPerWg tiles per
+// workgroup: a wave then queues ~43 words on average (one in ~100 words
+// needs the exact fix), far below its QCAP-entry queue, whose overflow
+// path (re-running the wave's tiles) is slow.  At m = 256 one launch
+// covers 2^20 keys.
+constexpr int kMaxTilesPerWg = 16;
+
+template <int M, bool ALIGNED>
+int launch_encode_chunks(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
+                         float* norms, int cap, int pos, hipStream_t stream) {
+  int max_grid = 0, wg_per_cu = 0;
+  const int e = encode_occupancy<M, ALIGNED>(&max_grid, &wg_per_cu);
+  if (e != hipSuccess) return e;
+  const int64_t chunk = static_cast<int64_t>(kMaxTilesPerWg) * max_grid * KT;   // a multiple of KT
+  for (int64_t r0 = 0; r0 < R; r0 += chunk) {
+    const int rows = static_cast<int>(R - r0 < chunk ? R - r0 : chunk);
+    const int err = launch_encode_mt<M, ALIGNED>(static_cast<const uint16_t*>(keys) + r0 * D, rows,
+                                                 static_cast<int>(r0), s, n, signs, norms, cap, pos,
+                                                 max_grid, wg_per_cu, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 template <int M>
 int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
                     float* norms, int cap, int pos, hipStream_t stream) {
-  if (n % KT == 0) return launch_encode_mt<M, true>(s, keys, R, n, signs, norms, cap, pos, stream);
-  return launch_encode_mt<M, false>(s, keys, R, n, signs, norms, cap, pos, stream);
+  // (chunks start at multiples of the tile, so alignment carries over)
+  if (n % KT == 0) return launch_encode_chunks<M, true>(s, keys, R, n, signs, norms, cap, pos, stream);
+  return launch_encode_chunks<M, false>(s, keys, R, n, signs, norms, cap, pos, stream);
 }
 
 }  // namespace

@@ -199,6 +199,21 @@ def test_large_ragged_uneven_split(gpu_lib):
     check_encode(gpu_lib, keys, 256, cap=n + 5, pos=3, sample_rows=rows, label="large ragged")
 
 
+@pytest.mark.parametrize("m,H,n", [(256, 33, 32768 + 5), (512, 9, 65536 + 3)])
+def test_across_launch_chunks(gpu_lib, m, H, n):
+    """More keys than one launch takes (2^20 at m = 256, 2^19 at m = 512),
+    with a per-head row count that is no multiple of the tile: rows around
+    each launch boundary, the first and last rows, and a sample."""
+    rng = np.random.default_rng(13 + m)
+    keys = wl.gaussian_keys(rng, H * n).reshape(1, H, n, 128)
+    R = H * n
+    chunk = 1 << 20 if m == 256 else 1 << 19
+    around = [np.arange(max(0, c - 3000), min(R, c + 3000)) for c in range(chunk, R, chunk)]
+    rows = np.unique(np.concatenate([np.arange(0, 2000), np.arange(R - 2000, R), *around,
+                                     np.random.default_rng(14).choice(R, 20_000, replace=False)]))
+    check_encode(gpu_lib, keys, m, sample_rows=rows, label="across launch chunks")
+
+
 def test_other_seed(gpu_lib):
     rng = np.random.default_rng(3)
     keys = wl.gaussian_keys(rng, 4000).reshape(1, 4, 1000, 128)
