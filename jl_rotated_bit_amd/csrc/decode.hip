@@ -420,9 +420,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[bb][st]),
                                                       __builtin_bit_cast(bf16x8_t, qfrag[(st * 2 + half) * 32 + col]),
                                                       acc, 0, 0, 0);
+      // limb p of coordinate 32 blk + 8 a4 + 4 half + i goes to byte
+      // 32 blk + 16 half + 4 i + a4 of its row (the order in which the score
+      // loop spreads a sign word: byte b of register q takes bit 8 b + q)
+      uint32_t pk[3][4] = {};
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        uint32_t pk[3] = {0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * a4 + i;
@@ -439,16 +442,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           const int q1 = (Q - c0) >> 8;
           const int c1 = ((q1 + 128) & 255) - 128;
           const int c2 = (q1 - c1) >> 8;
-          pk[0] |= (static_cast<uint32_t>(c2) & 255u) << (8 * i);
-          pk[1] |= (static_cast<uint32_t>(c1) & 255u) << (8 * i);
-          pk[2] |= (static_cast<uint32_t>(c0) & 255u) << (8 * i);
+          pk[0][i] |= (static_cast<uint32_t>(c2) & 255u) << (8 * a4);
+          pk[1][i] |= (static_cast<uint32_t>(c1) & 255u) << (8 * a4);
+          pk[2][i] |= (static_cast<uint32_t>(c0) & 255u) << (8 * a4);
         }
-        if (col < G) {
-          const int coord = 32 * blk + 8 * a4 + 4 * half;
+      }
+      if (col < G) {
 #pragma unroll
-          for (int p = 0; p < 3; ++p)
-            *reinterpret_cast<uint32_t*>(limbs + (p * G + col) * L::LROW + coord) = pk[p];
-        }
+        for (int p = 0; p < 3; ++p)
+          *reinterpret_cast<uint4*>(limbs + (p * G + col) * L::LROW + 32 * blk + 16 * half) =
+              make_uint4(pk[p][0], pk[p][1], pk[p][2], pk[p][3]);
       }
     }
     if (col < G) atomicAdd(&sumq[col], qsum);
@@ -521,11 +524,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w = sw[j][ks >> 1];
+        // register qd, byte b: bit 8 b + 4 (ks % 2) + qd of the word (the
+        // limbs were stored in this order)
         i32x4_t bits;
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          bits[qd] = static_cast<int>((__builtin_amdgcn_ubfe(w, 16 * (ks & 1) + 4 * qd, 4) * 0x00204081u) &
-                                      0x01010101u);
+        for (int qd = 0; qd < 4; ++qd) bits[qd] = static_cast<int>((w >> (4 * (ks & 1) + qd)) & 0x01010101u);
 #pragma unroll
         for (int cb = 0; cb < NSQ; ++cb)
           sacc[cb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lop[cb], bits, sacc[cb][j], 0, 0, 0);
