@@ -120,15 +120,16 @@ def test_adversarial_keys(gpu_lib, m):
 @pytest.mark.parametrize("m", [256, 512])
 def test_certification_queue_fills_and_overflows(gpu_lib, m):
     """Keys scaled by 2^60 have every bit re-derived exactly (their fp32
-    squared norm leaves the range the error bound is proved for).  The mix
-    fills a wave's queue of deferred fixes part way in one block and
-    overflows it in the next, so both the deferred batches and the
-    immediate fallback decide bits."""
+    squared norm leaves the range the error bound is proved for), and each
+    such key queues one word per wave and half.  Blocks 0 and 1 queue 96
+    words per wave and block 2 pushes past the 112-entry queue, so the
+    queued words are decided after the loop and the rest of the tile by
+    the re-run path."""
     rng = np.random.default_rng(90 + m)
     n = 300
     scale = np.ones(n)
-    scale[:16] = 2.0 ** 60            # block 0: 16 keys -> 32 queued words
-    scale[32:64] = 2.0 ** 60          # block 1: 64 more words -> overflow
+    scale[:16] = 2.0 ** 60            # block 0: 16 keys -> 32 queued words per wave
+    scale[32:64] = 2.0 ** 60          # block 1: 64 more words
     scale[64::3] = 2.0 ** 60
     K = oracle.float64_to_bf16_bits(oracle.bf16_bits_to_float64(wl.gaussian_keys(rng, n)) * scale[:, None])
     check_encode(gpu_lib, K.reshape(1, 1, n, 128), m, label="queue overflow")
