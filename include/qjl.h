@@ -95,8 +95,9 @@ QJL_API qjl_status qjl_sketch_host(uint64_t seed, int32_t d, int32_t m, uint16_t
  *   B, H_kv >= 1; n >= 0 (n == 0 is a no-op); cap >= 1; 0 <= pos;
  *   pos + n <= cap; B * H_kv * n <= 2^31 - 1 (QJL_EINVAL beyond: the
  *   kernel indexes keys in 32 bits); d == 128; m in {256, 512}.
- * The work is enqueued on `stream` (one kernel launch per 2^20 keys at
- * m = 256, per 2^19 at m = 512, on a 256-CU device) and the call returns.
+ * The work is enqueued on `stream` and the call returns.  On a 256-CU
+ * device one kernel launch takes up to 9 * 2^17 keys at m = 256 (9 * 2^16 at
+ * m = 512); larger key sets are divided evenly among the fewest launches.
  * The caller owns all buffers.  Returns QJL_OK, QJL_EINVAL, QJL_EUNSUPPORTED,
  * QJL_ENOMEM (first use of this S on this device) or QJL_EHIP. */
 QJL_API qjl_status qjl_encode_keys(const void *keys_bf16, int32_t B, int32_t H_kv, int32_t n,

@@ -837,11 +837,14 @@ int launch_encode_mt(const void* keys, int R, int r0, const DeviceSketch& s, int
   return hipGetLastError();
 }
 
-// Keys are encoded in launches of at most kMaxTilesPerWg tiles per
-// workgroup: a wave then queues ~43 words on average (one in ~100 words
-// needs the exact fix), far below its QCAP-entry queue, whose overflow
-// path (re-running the wave's tiles) is slow.  At m = 256 one launch
-// covers 2^20 keys.
+// Keys are encoded in launches of about kMaxTilesPerWg tiles per workgroup:
+// a wave then queues ~43 words on average (one in ~100 words needs the exact
+// fix), far below its QCAP-entry queue, whose overflow path (re-running the
+// wave's tiles) is slow.  A launch may take up to 1/8 more, so that a small
+// remainder (65537 tokens per head, say) does not need a launch of its own,
+// which would cost a whole prologue and end phase for a few keys; larger key
+// sets are divided evenly, in whole tiles, among the fewest launches.  At
+// m = 256 on 256 compute units one launch covers up to 9 * 2^17 keys.
 constexpr int kMaxTilesPerWg = 16;
 
 template <int M, bool ALIGNED>
@@ -850,7 +853,10 @@ int launch_encode_chunks(const DeviceSketch& s, const void* keys, int R, int n, 
   int max_grid = 0, wg_per_cu = 0;
   const int e = encode_occupancy<M, ALIGNED>(&max_grid, &wg_per_cu);
   if (e != hipSuccess) return e;
-  const int64_t chunk = static_cast<int64_t>(kMaxTilesPerWg) * max_grid * KT;   // a multiple of KT
+  const int64_t tiles = (static_cast<int64_t>(R) + KT - 1) / KT;
+  const int64_t cap_tiles = static_cast<int64_t>(kMaxTilesPerWg) * max_grid * 9 / 8;
+  const int64_t launches = (tiles + cap_tiles - 1) / cap_tiles;
+  const int64_t chunk = (tiles + launches - 1) / launches * KT;   // a multiple of KT
   for (int64_t r0 = 0; r0 < R; r0 += chunk) {
     const int rows = static_cast<int>(R - r0 < chunk ? R - r0 : chunk);
     const int err = launch_encode_mt<M, ALIGNED>(static_cast<const uint16_t*>(keys) + r0 * D, rows,

@@ -200,19 +200,40 @@ def test_large_ragged_uneven_split(gpu_lib):
     check_encode(gpu_lib, keys, 256, cap=n + 5, pos=3, sample_rows=rows, label="large ragged")
 
 
-@pytest.mark.parametrize("m,H,n", [(256, 33, 32768 + 5), (512, 9, 65536 + 3)])
+def launch_starts(R, m, cus=256):
+    """First rows of the encode launches after the first one on a device
+    with ``cus`` compute units: about 16 tiles of 128 keys per workgroup (two
+    workgroups per unit at m = 256, one at m = 512), up to 1/8 more before a
+    second launch is taken, and the tiles divided evenly among launches."""
+    tiles = -(-R // 128)
+    cap_tiles = 16 * cus * (2 if m == 256 else 1) * 9 // 8
+    launches = -(-tiles // cap_tiles)
+    chunk = -(-tiles // launches) * 128
+    return list(range(chunk, R, chunk))
+
+
+@pytest.mark.parametrize("m,H,n", [(256, 37, 32768 + 5), (512, 9, 65536 + 3), (512, 8, 65536 + 1)])
 def test_across_launch_chunks(gpu_lib, m, H, n):
-    """More keys than one launch takes (2^20 at m = 256, 2^19 at m = 512),
-    with a per-head row count that is no multiple of the tile: rows around
-    each launch boundary, the first and last rows, and a sample."""
-    rng = np.random.default_rng(13 + m)
+    """Key sets around the size one launch takes, with a per-head row count
+    that is no multiple of the tile: two launches at m = 256 (1.2 M keys) and
+    at m = 512 (590 K keys), and one launch in which a workgroup takes a
+    seventeenth tile (65537 tokens of 8 heads at m = 512).  Rows around each
+    launch boundary, the first and last rows, and a sample."""
+    rng = np.random.default_rng(13 + m + H)
     keys = wl.gaussian_keys(rng, H * n).reshape(1, H, n, 128)
     R = H * n
-    chunk = 1 << 20 if m == 256 else 1 << 19
-    around = [np.arange(max(0, c - 3000), min(R, c + 3000)) for c in range(chunk, R, chunk)]
+    around = [np.arange(max(0, c - 3000), min(R, c + 3000)) for c in launch_starts(R, m)]
     rows = np.unique(np.concatenate([np.arange(0, 2000), np.arange(R - 2000, R), *around,
                                      np.random.default_rng(14).choice(R, 20_000, replace=False)]))
     check_encode(gpu_lib, keys, m, sample_rows=rows, label="across launch chunks")
+
+
+def test_launch_starts_rule():
+    """The launch-boundary rule the chunk test aims at (host arithmetic)."""
+    assert launch_starts(8 * 65537, 512) == []
+    assert launch_starts(9 * 65539, 512) == [2305 * 128]
+    assert launch_starts(37 * 32773, 256) == [4737 * 128]
+    assert launch_starts(40 * 8 * 16384, 256) == [k * 8192 * 128 for k in range(1, 5)]
 
 
 def test_other_seed(gpu_lib):
