@@ -161,7 +161,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the QJL path has no multi-GPU mode in this build.", file=sys.stderr)
+              "the QJL path runs on one GPU (no sharding or collectives).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
