@@ -85,6 +85,10 @@ __device__ __forceinline__ uint2 ld8(const void* p) {
 // bytes must be wave-uniform.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, no swizzle
+// Cache policy of the token-tile loads: non-temporal (each byte of the cache
+// is read once per call).  A plain read stream over 1.5 GB measured 6.0 TB/s
+// with the default policy and 6.8 TB/s with this one.
+constexpr int kStream = 2;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
   // readfirstlane keeps the (uniform) size in a scalar register; a vector
   // register there would make the compiler loop over lanes around each load
@@ -277,18 +281,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int j = 0; j < 4; ++j) {
       const int off = so_lane + 16 * j * WPR * 4;
       if constexpr (CW == 2) {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kStream);
         s[j][0] = v.x;
         s[j][1] = v.y;
       } else {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStream);
         s[j][0] = v.x;
         s[j][1] = v.y;
         s[j][2] = v.z;
         s[j][3] = v.w;
       }
     }
-    n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, 0, 0));
+    n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, 0, kStream));
   };
   // value chunk c of a tile: token t0 + 4c + lane/16, channels 8*(lane%16) .. +7
   const int vo_lane = grp * D * 2 + l16 * 16;
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const rsrc_t rv = make_rsrc(v_base + static_cast<int64_t>(t0_) * D, tile_rows(t0_) * D * 2);
 #pragma unroll
     for (int u = 0; u < VCH / 2; ++u) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_lane + 4 * (c_begin + u) * D * 2, 0, 0);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rv, vo_lane + 4 * (c_begin + u) * D * 2, 0, kStream);
       vc[c_begin + u] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
