@@ -252,6 +252,25 @@ def main():
     b2b_enc_ms = back_to_back("encode", args.steps)
     log(f"[bench] back to back: decode {b2b_dec_ms * 1e3:.2f} us, encode {b2b_enc_ms * 1e3:.2f} us")
 
+    # A decode step that first appends one token: the newest key of every
+    # (batch, kv head) is encoded into row N - 1 of the caches, then the
+    # decode runs over all N tokens.  (Writing the new value row is the
+    # caller's copy and is not timed.)
+    new_keys = [s["keys"][:, :, N - 1:N].contiguous() for s in sets]
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        s = sets[i % n_sets]
+        qjl.encode_keys(new_keys[i % n_sets], s["signs"], s["norms"], N - 1, SEED, m)
+        qjl.decode_attention(s["q"], s["signs"], s["norms"], s["values"], N, SEED, m,
+                             out=s["out"], workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    append_ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] append step (encode of {B * Hkv} keys + decode): {append_ms * 1e3:.2f} us")
+
     if args.copy_calibration:
         a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
@@ -291,6 +310,8 @@ def main():
         "decode_us_in_step": round(float(dec_ms.mean()) * 1e3, 3),
         "decode_us_in_step_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
                                       round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
+        "append_step_us": round(append_ms * 1e3, 3),
+        "append_step_frac_of_hbm_peak": round(dbytes / (append_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "encode_keys_per_s": round(n_keys / enc_s, 1),
         "encode_us": round(enc_s * 1e6, 3),
         "encode_us_in_step": round(float(enc_ms.mean()) * 1e3, 3),

@@ -38,6 +38,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <type_traits>
@@ -867,6 +868,92 @@ int launch_encode_chunks(const DeviceSketch& s, const void* keys, int R, int n, 
   return hipSuccess;
 }
 
+// ---- small key sets: one thread per (key, sketch coordinate) ----
+// For a handful of keys (a decode step appends one per kv head) the tile
+// kernel's fixed costs (a workgroup's resident S^T operand, a whole tile, the
+// deferred-fix phase) dominate.  Here a 256-thread workgroup takes one key
+// and 256 coordinates; a thread forms its projection in fp64 from the key row
+// (staged once in LDS as fp64) and its S^T row.  Every bf16 x bf16 product is
+// exact in fp64, so their sum, with at most 128 roundings in any order, is within
+// 128 * 2^-53 * sum|k_j s_ij| <= 2^-46 ||k|| max_i ||s_i|| of the exact value:
+// a projection beyond twice that decides its sign, and the rest (none in
+// practice) go to the exact integer evaluation, one lane at a time.
+// All-zero keys take all-ones words.  The norm is fp32 of the fp64 square
+// root of the fp64 sum of squares.
+template <int M>
+__global__ __launch_bounds__(256) void encode_small_kernel(
+    const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md, float cnmax,
+    uint32_t* __restrict__ signs, float* __restrict__ norms, int n, int cap, int pos) {
+  constexpr int WPR = M / 32;
+  constexpr int BPK = M / 256;             // workgroups per key
+  __shared__ double kf[D];
+  __shared__ double ksq_part[2];
+  __shared__ uint32_t long_scratch[4][2 * ACC_WORDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t r = blockIdx.x / BPK;                        // key
+  const int i = static_cast<int>(blockIdx.x % BPK) * 256 + tid;   // coordinate
+  const uint16_t* krow = keys + static_cast<int64_t>(r) * D;
+  if (tid < D) {
+    const double v = static_cast<double>(__uint_as_float(static_cast<uint32_t>(krow[tid]) << 16));
+    kf[tid] = v;
+    // squares of bf16 values are exact in fp64; two waves reduce 64 each
+    double q = v * v;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
+    if (lane == 0) ksq_part[wave] = q;
+  }
+  // this thread's S^T row (256 bytes), requested while the key is staged
+  const uint4* srow = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(i) * D);
+  uint4 sv[D / 8];
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) sv[c] = srow[c];
+  __syncthreads();
+  const double ksq = ksq_part[0] + ksq_part[1];
+  // four independent chains (any order of the 128 roundings keeps the bound)
+  double part[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const uint32_t w[4] = {sv[c].x, sv[c].y, sv[c].z, sv[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      part[e] = __builtin_fma(kf[8 * c + 2 * e], bf16_lo_f64(w[e]), part[e]);
+      part[e] = __builtin_fma(kf[8 * c + 2 * e + 1], bf16_hi_f64(w[e]), part[e]);
+    }
+  }
+  const double acc = (part[0] + part[1]) + (part[2] + part[3]);
+  const double knorm = __builtin_sqrt(ksq);
+  const double thr = 0x1.0p-45 * knorm * static_cast<double>(cnmax);
+  bool bit = acc >= 0.0;
+  const bool decided = ksq == 0.0 || __builtin_fabs(acc) > thr;
+  if (ksq == 0.0) bit = true;   // all-(+/-)zero key: every projection is exactly 0
+  uint64_t open = __ballot(!decided);
+  while (open != 0) {   // wave-uniform
+    const int l = __builtin_ctzll(open);
+    if (lane == l) bit = exact_sign_long(krow, s_md + static_cast<int64_t>(i) * D, long_scratch[wave]);
+    open &= open - 1;
+  }
+  const uint64_t mask = __ballot(bit);
+  const int64_t row = dest_row(r, static_cast<uint32_t>(n), cap, pos);
+  if (lane == 0) {
+    // coordinates i0 .. i0 + 63 of this wave: words i0/32 and i0/32 + 1
+    const int w0 = (static_cast<int>(blockIdx.x % BPK) * 256 + wave * 64) / 32;
+    *reinterpret_cast<uint2*>(signs + row * WPR + w0) =
+        make_uint2(static_cast<uint32_t>(mask), static_cast<uint32_t>(mask >> 32));
+    if (blockIdx.x % BPK == 0 && wave == 0) norms[row] = static_cast<float>(knorm);
+  }
+}
+
+template <int M>
+int launch_encode_small(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
+                        float* norms, int cap, int pos, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(R) * (M / 256);
+  hipLaunchKernelGGL(encode_small_kernel<M>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(keys), s.s_md, s.col_norm_all, signs, norms, n, cap, pos);
+  return hipGetLastError();
+}
+
 template <int M>
 int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
                     float* norms, int cap, int pos, hipStream_t stream) {
@@ -877,14 +964,26 @@ int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint3
 
 }  // namespace
 
+// Key sets of at most this many keys go to the small-set kernel.
+std::atomic<int> encode_small_max{kEncodeSmallMaxDefault};
+
 int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int n, uint32_t* signs,
                   float* norms, int cap, int pos, void* stream) {
   const int64_t R = static_cast<int64_t>(B) * H_kv * n;
   if (R == 0) return hipSuccess;
   if (R > INT32_MAX) return hipErrorInvalidValue;   // the kernel indexes keys in 32 bits
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (R <= encode_small_max.load(std::memory_order_relaxed)) {
+    if (s.m == 256) return launch_encode_small<256>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
+    return launch_encode_small<512>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
+  }
   if (s.m == 256) return launch_encode_m<256>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
   return launch_encode_m<512>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
+}
+
+int set_encode_small_max(int keys) {
+  if (keys < 0) return encode_small_max.load(std::memory_order_relaxed);
+  return encode_small_max.exchange(keys, std::memory_order_relaxed);
 }
 
 }  // namespace qjl

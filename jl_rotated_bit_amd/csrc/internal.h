@@ -53,6 +53,12 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
 int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int n, uint32_t* signs,
                   float* norms, int cap, int pos, void* stream);
 
+// Encode calls with at most this many keys (B * H_kv * n) use the small-set
+// kernel; set_encode_small_max changes the limit (negative: query only) and
+// returns the previous one.
+constexpr int kEncodeSmallMaxDefault = 256;
+int set_encode_small_max(int keys);
+
 int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,
                   const uint32_t* signs, const float* norms, const void* values, int B, int H_q,
                   int H_kv, int N, int cap, float scale, float* out, void* workspace,

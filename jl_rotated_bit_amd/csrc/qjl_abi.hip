@@ -180,6 +180,8 @@ QJL_API qjl_status qjl_encode_keys(const void* keys_bf16, int32_t B, int32_t H_k
   return QJL_OK;
 }
 
+QJL_API int32_t qjl_set_encode_small_max(int32_t keys) { return qjl::set_encode_small_max(keys); }
+
 QJL_API int32_t qjl_decode_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t N, int32_t d,
                                       int32_t m) {
   qjl::DecodePlan p;

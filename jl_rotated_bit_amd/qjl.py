@@ -69,6 +69,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                              c_vp, c_sz, c_vp]
         lib.qjl_release_cache.restype = c_int
         lib.qjl_release_cache.argtypes = []
+        lib.qjl_set_encode_small_max.restype = c_int
+        lib.qjl_set_encode_small_max.argtypes = [c_int]
         v = lib.qjl_abi_version()
         if v != ABI_VERSION:
             raise RuntimeError(f"libqjl ABI version {v}, binding expects {ABI_VERSION}")
@@ -166,6 +168,12 @@ def decode_attention(q, signs, norms, values, N: int, seed: int, m: int, scale: 
         seed & (2 ** 64 - 1), 0.0 if scale is None else float(scale), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return out
+
+
+def set_encode_small_max(keys: int) -> int:
+    """Largest encode call (in keys) that runs the small-set kernel; returns
+    the previous limit (a negative ``keys`` only queries it)."""
+    return load().qjl_set_encode_small_max(keys)
 
 
 def release_cache():

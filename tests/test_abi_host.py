@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for name in names:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", qjl.LIB_PATH], capture_output=True,
@@ -42,6 +42,21 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) <= exported
     # nothing else with the qjl_ prefix leaks out
     assert {n for n in exported if n.startswith("qjl_")} == set(names)
+
+
+def test_encode_small_max_knob(lib):
+    """The small-set encode limit: default 256, set and query without a GPU."""
+    lib.qjl_set_encode_small_max.restype = ctypes.c_int32
+    lib.qjl_set_encode_small_max.argtypes = [ctypes.c_int32]
+    start = lib.qjl_set_encode_small_max(-1)
+    try:
+        assert start == 256
+        assert lib.qjl_set_encode_small_max(0) == 256
+        assert lib.qjl_set_encode_small_max(-5) == 0
+        assert lib.qjl_set_encode_small_max(100000) == 0
+        assert lib.qjl_set_encode_small_max(-1) == 100000
+    finally:
+        lib.qjl_set_encode_small_max(start)
 
 
 def test_library_targets_gfx950_only():

@@ -48,7 +48,16 @@ def check_encode(qjl, keys, m, seed=SEED, cap=None, pos=0, sample_rows=None, lab
     return got_w, got_n
 
 
-def test_small_workload_keys(gpu_lib):
+@pytest.fixture(params=["tile", "small"])
+def enc_path(request, gpu_lib):
+    """Runs a test through one encode kernel: the tile kernel (limit 0) or
+    the small-set kernel (no limit), whatever the size."""
+    prev = gpu_lib.set_encode_small_max(0 if request.param == "tile" else 2 ** 31 - 1)
+    yield request.param
+    gpu_lib.set_encode_small_max(prev)
+
+
+def test_small_workload_keys(gpu_lib, enc_path):
     w = wl.small()
     check_encode(gpu_lib, w.keys, w.m, label="small")
 
@@ -57,7 +66,7 @@ def test_small_workload_keys(gpu_lib):
 @pytest.mark.parametrize("B,H,n,cap,pos", [(1, 1, 1, 1, 0), (1, 1, 1, 9, 7), (2, 3, 31, 40, 5),
                                             (1, 2, 33, 33, 0), (3, 1, 95, 200, 100),
                                             (1, 1, 1000, 1003, 3)])
-def test_ragged_shapes_and_offsets(gpu_lib, m, B, H, n, cap, pos):
+def test_ragged_shapes_and_offsets(gpu_lib, enc_path, m, B, H, n, cap, pos):
     rng = np.random.default_rng(B * 1000 + H * 100 + n + m)
     keys = wl.gaussian_keys(rng, B * H * n).reshape(B, H, n, 128)
     check_encode(gpu_lib, keys, m, cap=cap, pos=pos, label="ragged")
@@ -109,7 +118,7 @@ def adversarial_keys(S, rng):
 
 
 @pytest.mark.parametrize("m", [256, 512])
-def test_adversarial_keys(gpu_lib, m):
+def test_adversarial_keys(gpu_lib, enc_path, m):
     S = oracle.sketch(SEED, 128, m)
     K = adversarial_keys(S, np.random.default_rng(m))
     got_w, _ = check_encode(gpu_lib, K.reshape(1, 1, -1, 128), m, label="adversarial")
@@ -118,7 +127,7 @@ def test_adversarial_keys(gpu_lib, m):
 
 
 @pytest.mark.parametrize("m", [256, 512])
-def test_certification_queue_fills_and_overflows(gpu_lib, m):
+def test_certification_queue_fills_and_overflows(gpu_lib, enc_path, m):
     """Keys scaled by 2^60 have every bit re-derived exactly (their fp32
     squared norm leaves the range the error bound is proved for), and each
     such key queues one word per wave and half.  Blocks 0 and 1 queue 96
@@ -136,7 +145,7 @@ def test_certification_queue_fills_and_overflows(gpu_lib, m):
 
 
 @pytest.mark.parametrize("m", [256, 512])
-def test_zero_padding_rows(gpu_lib, m):
+def test_zero_padding_rows(gpu_lib, enc_path, m):
     """All-(+/-)zero rows (padding) mixed with ordinary keys, in runs and
     one by one: every bit of a zero row is 1 and its norm is 0, and the
     ordinary rows around them are unaffected."""
@@ -151,7 +160,7 @@ def test_zero_padding_rows(gpu_lib, m):
     assert np.all(got_w[0, 0, 7] == 0xFFFFFFFF)
 
 
-def test_matches_exact_rationals_on_cancellations(gpu_lib):
+def test_matches_exact_rationals_on_cancellations(gpu_lib, enc_path):
     """Brute force with Fractions on rows built to cancel exactly or almost."""
     S = oracle.sketch(SEED, 128, 256)
     rng = np.random.default_rng(77)
@@ -236,8 +245,21 @@ def test_launch_starts_rule():
     assert launch_starts(40 * 8 * 16384, 256) == [k * 8192 * 128 for k in range(1, 5)]
 
 
-def test_other_seed(gpu_lib):
+def test_other_seed(gpu_lib, enc_path):
     rng = np.random.default_rng(3)
     keys = wl.gaussian_keys(rng, 4000).reshape(1, 4, 1000, 128)
     check_encode(gpu_lib, keys, 256, seed=2 ** 64 - 3, label="seed 2^64-3")
     check_encode(gpu_lib, keys, 512, seed=0, label="seed 0")
+
+
+@pytest.mark.parametrize("m", [256, 512])
+def test_default_limit_both_sides(gpu_lib, m):
+    """With the default limit (256 keys), calls of 256 keys run the small-set
+    kernel and calls of 257 the tile kernel; both match the oracle, and the
+    one-token append of a decode step (one key per kv head) is exact."""
+    assert gpu_lib.set_encode_small_max(-1) == 256
+    rng = np.random.default_rng(600 + m)
+    for B, H, n in [(1, 2, 128), (1, 1, 257), (2, 8, 1)]:
+        keys = wl.gaussian_keys(rng, B * H * n).reshape(B, H, n, 128)
+        check_encode(gpu_lib, keys, m, cap=n + 9, pos=9, label=f"default limit {B * H * n} keys")
+
