@@ -10,7 +10,8 @@ Names and semantics follow the C entry points:
 * ``sketch_host(seed, d, m)``                 -> qjl_sketch_host
 * ``encode_keys(keys, signs, norms, pos, seed, m)``        -> qjl_encode_keys
 * ``decode_attention(q, signs, norms, values, N, seed, m, scale)`` -> qjl_decode_attention
-* ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache``
+* ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache`` /
+  ``set_encode_small_max``
 """
 
 from __future__ import annotations
