@@ -110,7 +110,8 @@ QJL_API qjl_status qjl_encode_keys(const void *keys_bf16, int32_t B, int32_t H_k
  * covers a decode step that appends one token per (batch, kv head) for up to
  * 256 such pairs.  (Each workgroup of the small-set kernel reads all of S, so
  * its cost grows with the key count; it runs after a decode has displaced S
- * from the caches.)  0 sends
+ * from the caches.)  Calls above 2^23 keys (2^22 at m = 512) always run the
+ * tile kernel.  0 sends
  * every call to the tile kernel.  A negative `keys` changes nothing.  Returns
  * the previous limit.  Process-wide; takes effect for calls made after it
  * returns.  (For tuning and for testing either kernel on any size.) */

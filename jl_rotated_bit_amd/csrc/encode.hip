@@ -973,7 +973,9 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
   if (R == 0) return hipSuccess;
   if (R > INT32_MAX) return hipErrorInvalidValue;   // the kernel indexes keys in 32 bits
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (R <= encode_small_max.load(std::memory_order_relaxed)) {
+  // (the small-set grid, R * m / 256 workgroups of 256 threads, stays below
+  // 2^31 threads whatever the limit is set to)
+  if (R <= encode_small_max.load(std::memory_order_relaxed) && R * (s.m / 256) <= (int64_t{1} << 23)) {
     if (s.m == 256) return launch_encode_small<256>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
     return launch_encode_small<512>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
   }
