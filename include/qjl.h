@@ -105,12 +105,11 @@ QJL_API qjl_status qjl_encode_keys(const void *keys_bf16, int32_t B, int32_t H_k
                                    float *norms, int32_t cap, int32_t pos, void *stream);
 
 /* Encode calls with at most `keys` keys (B * H_kv * n) run a small-set kernel
- * (one thread per key and sketch coordinate, fp64 projections with the same
- * exact-sign guarantee); larger calls run the tile kernel.  The default, 256,
+ * (four lanes per key and sketch coordinate, fp64 projections with the same
+ * exact-sign guarantee); larger calls run the tile kernel.  The default, 512,
  * covers a decode step that appends one token per (batch, kv head) for up to
- * 256 such pairs.  (Each workgroup of the small-set kernel reads all of S, so
- * its cost grows with the key count; it runs after a decode has displaced S
- * from the caches.)  Calls above 2^23 keys (2^22 at m = 512) always run the
+ * 512 such pairs; alone, the two kernels take equal time near 800 keys at
+ * m = 256 and 550 at m = 512.  Calls above 2^21 keys (2^20 at m = 512) always run the
  * tile kernel.  0 sends
  * every call to the tile kernel.  A negative `keys` changes nothing.  Returns
  * the previous limit.  Process-wide; takes effect for calls made after it

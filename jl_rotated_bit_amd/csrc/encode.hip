@@ -868,32 +868,36 @@ int launch_encode_chunks(const DeviceSketch& s, const void* keys, int R, int n, 
   return hipSuccess;
 }
 
-// ---- small key sets: one thread per (key, sketch coordinate) ----
+// ---- small key sets: four lanes per (key, sketch coordinate) ----
 // For a handful of keys (a decode step appends one per kv head) the tile
 // kernel's fixed costs (a workgroup's resident S^T operand, a whole tile, the
 // deferred-fix phase) dominate.  Here a 256-thread workgroup takes one key
-// and 256 coordinates; a thread forms its projection in fp64 from the key row
-// (staged once in LDS as fp64) and its S^T row.  Every bf16 x bf16 product is
-// exact in fp64, so their sum, with at most 128 roundings in any order, is within
-// 128 * 2^-53 * sum|k_j s_ij| <= 2^-46 ||k|| max_i ||s_i|| of the exact value:
-// a projection beyond twice that decides its sign, and the rest (none in
-// practice) go to the exact integer evaluation, one lane at a time.
-// All-zero keys take all-ones words.  The norm is fp32 of the fp64 square
-// root of the fp64 sum of squares.
+// and 64 coordinates; the four lanes of a quad share a coordinate, each
+// multiplying 32 of the 128 channels (16-byte chunks sub, sub + 4, sub + 8,
+// sub + 12 of the key row, staged once in LDS as fp64, and of the S^T row)
+// in fp64, and a quad sum joins them (the same value in all four lanes).
+// Every bf16 x bf16 product is exact in fp64 and a sum takes at most 34
+// roundings on any path, so it lies within 2^-47 ||k|| max_i ||s_i|| of the
+// exact value: a projection beyond 2^-45 ||k|| max_i ||s_i|| decides its
+// sign, and the rest (none in practice) go to the exact integer evaluation,
+// one at a time.  All-zero keys take all-ones words.  The norm is fp32 of the
+// fp64 square root of the fp64 sum of squares.
 template <int M>
 __global__ __launch_bounds__(256) void encode_small_kernel(
     const uint16_t* __restrict__ keys, const uint16_t* __restrict__ s_md, float cnmax,
     uint32_t* __restrict__ signs, float* __restrict__ norms, int n, int cap, int pos) {
   constexpr int WPR = M / 32;
-  constexpr int BPK = M / 256;             // workgroups per key
+  constexpr int BPK = M / 64;              // workgroups per key
   __shared__ double kf[D];
   __shared__ double ksq_part[2];
   __shared__ uint32_t long_scratch[4][2 * ACC_WORDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const uint32_t r = blockIdx.x / BPK;                        // key
-  const int i = static_cast<int>(blockIdx.x % BPK) * 256 + tid;   // coordinate
+  const int sub = lane & 3;
+  const uint32_t r = blockIdx.x / BPK;                                  // key
+  const int cbase = static_cast<int>(blockIdx.x % BPK) * 64;            // first coordinate
+  const int i = cbase + (tid >> 2);                                     // this quad's coordinate
   const uint16_t* krow = keys + static_cast<int64_t>(r) * D;
   if (tid < D) {
     const double v = static_cast<double>(__uint_as_float(static_cast<uint32_t>(krow[tid]) << 16));
@@ -904,51 +908,55 @@ __global__ __launch_bounds__(256) void encode_small_kernel(
     for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
     if (lane == 0) ksq_part[wave] = q;
   }
-  // this thread's S^T row (256 bytes), requested while the key is staged
+  // chunks sub, sub + 4, sub + 8, sub + 12 of the S^T row, requested while
+  // the key is staged
   const uint4* srow = reinterpret_cast<const uint4*>(s_md + static_cast<int64_t>(i) * D);
-  uint4 sv[D / 8];
+  uint4 sv[4];
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) sv[c] = srow[c];
+  for (int u = 0; u < 4; ++u) sv[u] = srow[4 * u + sub];
   __syncthreads();
   const double ksq = ksq_part[0] + ksq_part[1];
-  // four independent chains (any order of the 128 roundings keeps the bound)
-  double part[4] = {0.0, 0.0, 0.0, 0.0};
+  double part[2] = {0.0, 0.0};
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const uint32_t w[4] = {sv[c].x, sv[c].y, sv[c].z, sv[c].w};
+  for (int u = 0; u < 4; ++u) {
+    const int c0 = 8 * (4 * u + sub);
+    const uint32_t w[4] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      part[e] = __builtin_fma(kf[8 * c + 2 * e], bf16_lo_f64(w[e]), part[e]);
-      part[e] = __builtin_fma(kf[8 * c + 2 * e + 1], bf16_hi_f64(w[e]), part[e]);
+      part[e & 1] = __builtin_fma(kf[c0 + 2 * e], bf16_lo_f64(w[e]), part[e & 1]);
+      part[e & 1] = __builtin_fma(kf[c0 + 2 * e + 1], bf16_hi_f64(w[e]), part[e & 1]);
     }
   }
-  const double acc = (part[0] + part[1]) + (part[2] + part[3]);
+  const double acc = quad_sum_f64(part[0] + part[1]);
   const double knorm = __builtin_sqrt(ksq);
   const double thr = 0x1.0p-45 * knorm * static_cast<double>(cnmax);
   bool bit = acc >= 0.0;
   const bool decided = ksq == 0.0 || __builtin_fabs(acc) > thr;
   if (ksq == 0.0) bit = true;   // all-(+/-)zero key: every projection is exactly 0
-  uint64_t open = __ballot(!decided);
+  uint64_t open = __ballot(!decided && sub == 0);
   while (open != 0) {   // wave-uniform
     const int l = __builtin_ctzll(open);
     if (lane == l) bit = exact_sign_long(krow, s_md + static_cast<int64_t>(i) * D, long_scratch[wave]);
     open &= open - 1;
   }
-  const uint64_t mask = __ballot(bit);
+  // lane 4q (q = 0..15) holds the bit of coordinate cbase + 16 wave + q
+  const uint64_t mask = __ballot(bit && sub == 0);
+  uint32_t half = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) half |= static_cast<uint32_t>((mask >> (4 * q)) & 1u) << q;
   const int64_t row = dest_row(r, static_cast<uint32_t>(n), cap, pos);
   if (lane == 0) {
-    // coordinates i0 .. i0 + 63 of this wave: words i0/32 and i0/32 + 1
-    const int w0 = (static_cast<int>(blockIdx.x % BPK) * 256 + wave * 64) / 32;
-    *reinterpret_cast<uint2*>(signs + row * WPR + w0) =
-        make_uint2(static_cast<uint32_t>(mask), static_cast<uint32_t>(mask >> 32));
-    if (blockIdx.x % BPK == 0 && wave == 0) norms[row] = static_cast<float>(knorm);
+    // coordinates cbase + 16 wave .. +15: half (wave & 1) of word (cbase + 16 wave) / 32
+    const int c = cbase + 16 * wave;
+    reinterpret_cast<uint16_t*>(signs + row * WPR + c / 32)[(c / 16) & 1] = static_cast<uint16_t>(half);
+    if (cbase == 0 && wave == 0) norms[row] = static_cast<float>(knorm);
   }
 }
 
 template <int M>
 int launch_encode_small(const DeviceSketch& s, const void* keys, int R, int n, uint32_t* signs,
                         float* norms, int cap, int pos, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(R) * (M / 256);
+  const int64_t blocks = static_cast<int64_t>(R) * (M / 64);
   hipLaunchKernelGGL(encode_small_kernel<M>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(keys), s.s_md, s.col_norm_all, signs, norms, n, cap, pos);
   return hipGetLastError();
@@ -973,9 +981,9 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
   if (R == 0) return hipSuccess;
   if (R > INT32_MAX) return hipErrorInvalidValue;   // the kernel indexes keys in 32 bits
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // (the small-set grid, R * m / 256 workgroups of 256 threads, stays below
+  // (the small-set grid, R * m / 64 workgroups of 256 threads, stays below
   // 2^31 threads whatever the limit is set to)
-  if (R <= encode_small_max.load(std::memory_order_relaxed) && R * (s.m / 256) <= (int64_t{1} << 23)) {
+  if (R <= encode_small_max.load(std::memory_order_relaxed) && R * (s.m / 64) <= (int64_t{1} << 23)) {
     if (s.m == 256) return launch_encode_small<256>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
     return launch_encode_small<512>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
   }

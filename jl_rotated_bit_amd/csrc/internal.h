@@ -56,7 +56,7 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
 // Encode calls with at most this many keys (B * H_kv * n) use the small-set
 // kernel; set_encode_small_max changes the limit (negative: query only) and
 // returns the previous one.
-constexpr int kEncodeSmallMaxDefault = 256;
+constexpr int kEncodeSmallMaxDefault = 512;
 int set_encode_small_max(int keys);
 
 int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,

@@ -45,13 +45,13 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_encode_small_max_knob(lib):
-    """The small-set encode limit: default 256, set and query without a GPU."""
+    """The small-set encode limit: default 512, set and query without a GPU."""
     lib.qjl_set_encode_small_max.restype = ctypes.c_int32
     lib.qjl_set_encode_small_max.argtypes = [ctypes.c_int32]
     start = lib.qjl_set_encode_small_max(-1)
     try:
-        assert start == 256
-        assert lib.qjl_set_encode_small_max(0) == 256
+        assert start == 512
+        assert lib.qjl_set_encode_small_max(0) == 512
         assert lib.qjl_set_encode_small_max(-5) == 0
         assert lib.qjl_set_encode_small_max(100000) == 0
         assert lib.qjl_set_encode_small_max(-1) == 100000

@@ -254,12 +254,12 @@ def test_other_seed(gpu_lib, enc_path):
 
 @pytest.mark.parametrize("m", [256, 512])
 def test_default_limit_both_sides(gpu_lib, m):
-    """With the default limit (256 keys), calls of 256 keys run the small-set
-    kernel and calls of 257 the tile kernel; both match the oracle, and the
+    """With the default limit (512 keys), calls of 512 keys run the small-set
+    kernel and calls of 513 the tile kernel; both match the oracle, and the
     one-token append of a decode step (one key per kv head) is exact."""
-    assert gpu_lib.set_encode_small_max(-1) == 256
+    assert gpu_lib.set_encode_small_max(-1) == 512
     rng = np.random.default_rng(600 + m)
-    for B, H, n in [(1, 2, 128), (1, 1, 257), (2, 8, 1)]:
+    for B, H, n in [(1, 4, 128), (1, 1, 513), (2, 8, 1)]:
         keys = wl.gaussian_keys(rng, B * H * n).reshape(B, H, n, 128)
         check_encode(gpu_lib, keys, m, cap=n + 9, pos=9, label=f"default limit {B * H * n} keys")
 
