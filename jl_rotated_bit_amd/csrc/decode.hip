@@ -309,10 +309,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- prologue ----
   // q (straight into the split entries) and the S^T fragments are requested
-  // first; the first tile is requested once q is split, so that q does not
-  // queue behind the whole chip's tile traffic.  Memory counters drain in
-  // order, so S^T q waits for the fragments only and leaves the tile loads
-  // in flight.
+  // first; the first tile is requested once q is split (or, in the S^T q
+  // waves of eight-wave workgroups at m = 256, once S^T q is done), so that q
+  // does not queue behind the whole chip's tile traffic.
   // S^T q runs on the first SQW waves only: with eight waves, the younger
   // four would reach it only after their (lower-priority) tile requests,
   // holding up the whole workgroup.
@@ -384,11 +383,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (c < G) qss[c * 16 + (e >> 5)] = ss;   // e >> 5 = 2 st + hf
   }
   __syncthreads();
-  load_signs(t0, sw, nv);
-  load_values(t0, std::integral_constant<int, 0>{});
-  // with m = 512 the S^T fragments fill half the registers: the second half
-  // of the first tile's values is requested after S^T q
-  if constexpr (M == 256) load_values(t0, std::integral_constant<int, 1>{});
+  // The first tile.  With eight waves at m = 256 the S^T q waves request
+  // theirs after S^T q, so that a tile request held up by the chip-wide
+  // start-up traffic does not hold up S^T q (and with it every wave's first
+  // tile), while the other four waves keep the memory busy (measured: 32K
+  // 20.65 -> 20.1 us; at m = 512, and with four waves, requesting before S^T q
+  // measured faster).  With m = 512 the S^T fragments fill half the
+  // registers: the second half of the first tile's values is requested
+  // after S^T q in every wave.
+  constexpr bool kLateTile = M == 256 && NW > SQW;
+  auto first_tile = [&]() {
+    load_signs(t0, sw, nv);
+    load_values(t0, std::integral_constant<int, 0>{});
+    if constexpr (M == 256) load_values(t0, std::integral_constant<int, 1>{});
+  };
+  if (!kLateTile || wave >= SQW) first_tile();
 
   // quantization step 2^E of head h: 2^(E + 21) exceeds ||q_h|| max_i ||s_i||
   // (with margin for the rounding of S^T q and of the norm itself)
@@ -459,6 +468,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     if (col < G) atomicAdd(&sumq[col], qsum);
+    if constexpr (kLateTile) first_tile();
   }
   if constexpr (M != 256) load_values(t0, std::integral_constant<int, 1>{});
   __syncthreads();
