@@ -8,7 +8,11 @@
 // because that section's formulas are written for unit vectors, which the
 // random-rotation section reaches by scaling.
 //
-// Kernel design (one launch per call):
+// Two kernels: a tile kernel for key sets of any size (one launch, or
+// several for sets beyond about 16 tiles per workgroup), and a small-set
+// kernel for calls of a few hundred keys at most (see encode_small_kernel).
+//
+// Tile kernel design:
 // * The projection P^T = S^T K^T runs on the matrix cores
 //   (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  A workgroup has m/64
 //   waves; wave w owns sketch coordinates [64w, 64w+64) and keeps its slice
