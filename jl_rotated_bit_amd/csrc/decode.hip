@@ -19,19 +19,22 @@
 //   the G heads runs on the matrix cores (fp32 accumulation).  Each head's
 //   S^T q is then written as integers Q_i = round(Sq_i / 2^E) with |Q_i| <=
 //   2^21, where 2^(E+21) bounds ||s_i|| ||q|| (Cauchy-Schwarz), as three signed
-//   byte limbs (Q = a 2^16 + b 2^8 + c) in LDS.  The first token tile's loads
-//   are in flight during the whole prologue.
+//   byte limbs (Q = a 2^16 + b 2^8 + c) in LDS.  The first token tile is
+//   requested once q is split (in the S^T q waves of eight-wave workgroups at
+//   m = 256, once S^T q is done), so its loads are in flight meanwhile.
 // * Scores on the int8 matrix cores: per 16-token block, A = the tokens' sign
 //   bits spread to 0/1 bytes (rows = tokens), B = the limbs (columns = limb x
-//   head), so sum_i b_ti Q_i is exact in int32.  Limb columns are combined with
-//   shifts and row rotations (DPP), and est = (2 sum_i b_ti Q_i - sum_i Q_i)
-//   2^E.  Each lane then holds the scores of 16 tokens for one head.
+//   head), so sum_i b_ti Q_i is exact in int32.  Limb rows are weighted by
+//   shifts and summed with 16- and 32-lane row swaps, a reduce-scatter that
+//   leaves lane t with token t for all G heads, and est = (2 sum_i b_ti Q_i -
+//   sum_i Q_i) 2^E.
 // * Online softmax per head in registers; the probabilities, split into bf16
 //   hi + lo parts, are already laid out as the A operand (rows = part x head,
 //   k = tokens) of v_mfma_f32_16x16x32_bf16.  The value rows (16-byte loads,
 //   16 lanes per row) go to a wave-private padded LDS tile and are read back
 //   transposed (ds_read_b64_tr_b16) as its B operand.  The next tile's loads
-//   are issued before the current tile is used.
+//   are issued before the current tile is used; token tiles are read with
+//   the non-temporal cache policy (each byte is read once per call).
 // * Epilogue: waves merge in LDS; the workgroup stores its partial
 //   (max, sum, acc) per head with coherent stores; the last workgroup of a
 //   (batch, kv head) to arrive (atomic counter) merges all splits by
