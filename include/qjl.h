@@ -30,8 +30,9 @@
  *   H_q % H_kv == 0 with G = H_q / H_kv in {1, 2, 4, 8}.  Other values return
  *   QJL_EUNSUPPORTED.
  * - Device pointers are HIP device memory of the current device.  `stream`
- *   is a hipStream_t (NULL = the default stream).  Calls enqueue one kernel
- *   on `stream` and return without waiting; errors inside a kernel surface at
+ *   is a hipStream_t (NULL = the default stream).  Calls enqueue their
+ *   kernel launches (one, or a few for large encode calls) on `stream` and
+ *   return without waiting; errors inside a kernel surface at
  *   the caller's next synchronization.  The first call for a given
  *   (device, seed, d, m) uploads S to the device synchronously and keeps it
  *   until qjl_release_cache() or process exit.
