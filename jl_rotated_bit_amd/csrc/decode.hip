@@ -959,15 +959,18 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
   if (H_q % H_kv) return false;
   const int64_t streams = static_cast<int64_t>(B) * H_kv;
   // Eight-wave workgroups (one per compute unit) when the context must be
-  // split and that still fills the chip: half the S^T fragment traffic per
-  // compute unit and half the partials to merge.  Otherwise four waves.
+  // split into at least 64 workgroups: half the S^T fragment traffic per
+  // compute unit and half the partials to merge (and half the arrivals on
+  // each counter, which serialize when every workgroup has a single tile:
+  // 8K tokens of 8 kv heads took 15.2 us with 256 four-wave workgroups and
+  // 13.8 us with 128 eight-wave ones).  Otherwise four waves.
   // At m = 512 each workgroup also reads twice the S^T fragments: slightly
   // fewer, longer splits (240 rather than 256 workgroups) measured faster.
   const int64_t target8 = m == 512 ? 240 : 256;
   int64_t n_split = 0, tps = 0;
   split_plan(streams, N, 8, target8, &n_split, &tps);
   int waves = 8;
-  if (!(n_split > 1 && streams * n_split >= target8 - 32)) {
+  if (!(n_split > 1 && streams * n_split >= 64)) {
     waves = 4;
     split_plan(streams, N, 4, target8, &n_split, &tps);
   }
