@@ -934,14 +934,19 @@ int launch_decode_m(int G, const DeviceSketch& s, const DecodePlan& plan, const 
 }  // namespace
 
 namespace {
-// Context splits for workgroups of nw waves: about 2048 / nw workgroups
-// (every compute unit busy), at least one full step (nw x 64 tokens) per
-// split, splits only for few streams.
+// Context splits for workgroups of nw waves: at most about 2048 / nw
+// workgroups (every compute unit busy, none left for a second round: with 40
+// streams, 7 splits made 280 eight-wave workgroups for 256 compute units and
+// took 48.2 us at 16K, 6 splits 35.3 us), at least one full step (nw x 64
+// tokens) per split, splits only for few streams.  With four waves a stream
+// count just above the target still gets two splits (320 streams at 16K:
+// 237 us with two, 265 us with one).
 // target: workgroups wanted at eight waves each (twice as many at four)
 void split_plan(int64_t streams, int N, int nw, int64_t target8, int64_t* n_split, int64_t* tps) {
   const int64_t target = target8 * 8 / nw;
   const int min_tokens = nw * TILE;
-  int64_t want = (target + streams - 1) / streams;
+  int64_t want = target / streams;
+  if (nw == 4 && want < 2) want = (target + streams - 1) / streams;
   if (streams > kMaxCounters) want = 1;   // splits (and counters) only for few streams
   const int64_t most = (N + min_tokens - 1) / min_tokens;
   if (want > most) want = most;
