@@ -146,6 +146,19 @@ def test_eight_wave_workgroups(gpu_lib, m, G):
     check_decode(gpu_lib, q, words, norms, values, N, m, label=f"eight waves G={G}")
 
 
+def test_many_heads_one_round(gpu_lib):
+    """40 kv heads at batch 1 (MHA): the split count is rounded down (6
+    eight-wave splits, 240 workgroups), and every output row matches."""
+    rng = np.random.default_rng(700)
+    B, Hkv, G, d, N, cap, m = 1, 40, 1, 128, 5000, 5003, 256
+    assert gpu_lib.decode_num_splits(B, Hkv * G, Hkv, N, d, m) == 6
+    keys = wl.gaussian_keys(rng, B * Hkv * cap, scale=2.0).reshape(B, Hkv, cap, d)
+    values = wl.gaussian_keys(rng, B * Hkv * cap).reshape(B, Hkv, cap, d)
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    words, norms = oracle_cache(keys, m)
+    check_decode(gpu_lib, q, words, norms, values, N, m, label="40 heads, 6 splits")
+
+
 def test_unused_cache_rows_are_not_read(gpu_lib):
     rng = np.random.default_rng(8)
     B, Hkv, G, cap, N, m = 1, 2, 4, 3000, 2049, 256
