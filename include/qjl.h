@@ -105,18 +105,6 @@ QJL_API qjl_status qjl_encode_keys(const void *keys_bf16, int32_t B, int32_t H_k
                                    int32_t d, int32_t m, uint64_t seed, uint32_t *signs,
                                    float *norms, int32_t cap, int32_t pos, void *stream);
 
-/* Encode calls with at most `keys` keys (B * H_kv * n) run a small-set kernel
- * (four lanes per key and sketch coordinate, fp64 projections with the same
- * exact-sign guarantee); larger calls run the tile kernel.  The default, 512,
- * covers a decode step that appends one token per (batch, kv head) for up to
- * 512 such pairs; alone, the two kernels take equal time near 800 keys at
- * m = 256 and 550 at m = 512.  Calls above 2^21 keys (2^20 at m = 512) always run the
- * tile kernel.  0 sends
- * every call to the tile kernel.  A negative `keys` changes nothing.  Returns
- * the previous limit.  Process-wide; takes effect for calls made after it
- * returns.  (For tuning and for testing either kernel on any size.) */
-QJL_API int32_t qjl_set_encode_small_max(int32_t keys);
-
 /* Number of context splits a decode call with these sizes uses (>= 1); 0 on
  * invalid sizes.  Pure host code. */
 QJL_API int32_t qjl_decode_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t N,

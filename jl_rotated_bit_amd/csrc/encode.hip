@@ -42,7 +42,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <type_traits>
@@ -976,8 +975,9 @@ int launch_encode_m(const DeviceSketch& s, const void* keys, int R, int n, uint3
 
 }  // namespace
 
-// Key sets of at most this many keys go to the small-set kernel.
-std::atomic<int> encode_small_max{kEncodeSmallMaxDefault};
+// Key sets of at most this many keys go to the small-set kernel.  The limit
+// is per thread (a test hook may move it for its own calls only).
+thread_local int encode_small_max = kEncodeSmallMaxDefault;
 
 int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int n, uint32_t* signs,
                   float* norms, int cap, int pos, void* stream) {
@@ -987,7 +987,7 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // (the small-set grid, R * m / 64 workgroups of 256 threads, stays below
   // 2^31 threads whatever the limit is set to)
-  if (R <= encode_small_max.load(std::memory_order_relaxed) && R * (s.m / 64) <= (int64_t{1} << 23)) {
+  if (R <= encode_small_max && R * (s.m / 64) <= (int64_t{1} << 23)) {
     if (s.m == 256) return launch_encode_small<256>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
     return launch_encode_small<512>(s, keys, static_cast<int>(R), n, signs, norms, cap, pos, st);
   }
@@ -996,8 +996,9 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
 }
 
 int set_encode_small_max(int keys) {
-  if (keys < 0) return encode_small_max.load(std::memory_order_relaxed);
-  return encode_small_max.exchange(keys, std::memory_order_relaxed);
+  const int prev = encode_small_max;
+  if (keys >= 0) encode_small_max = keys;
+  return prev;
 }
 
 }  // namespace qjl

@@ -54,8 +54,8 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
                   float* norms, int cap, int pos, void* stream);
 
 // Encode calls with at most this many keys (B * H_kv * n) use the small-set
-// kernel; set_encode_small_max changes the limit (negative: query only) and
-// returns the previous one.
+// kernel; set_encode_small_max changes the calling thread's limit (negative:
+// query only) and returns the previous one.
 constexpr int kEncodeSmallMaxDefault = 512;
 int set_encode_small_max(int keys);
 

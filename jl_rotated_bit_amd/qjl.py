@@ -10,8 +10,9 @@ Names and semantics follow the C entry points:
 * ``sketch_host(seed, d, m)``                 -> qjl_sketch_host
 * ``encode_keys(keys, signs, norms, pos, seed, m)``        -> qjl_encode_keys
 * ``decode_attention(q, signs, norms, values, N, seed, m, scale)`` -> qjl_decode_attention
-* ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache`` /
-  ``set_encode_small_max``
+* ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache``
+* ``testing_set_encode_small_max`` -> qjl_testing_set_encode_small_max (a
+  per-thread test hook, not part of the public header)
 """
 
 from __future__ import annotations
@@ -24,7 +25,7 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqjl.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {0: "QJL_OK", 1: "QJL_EINVAL", 2: "QJL_EUNSUPPORTED", 3: "QJL_EWORKSPACE",
           4: "QJL_EHIP", 5: "QJL_ENOMEM"}
@@ -70,8 +71,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                              c_vp, c_sz, c_vp]
         lib.qjl_release_cache.restype = c_int
         lib.qjl_release_cache.argtypes = []
-        lib.qjl_set_encode_small_max.restype = c_int
-        lib.qjl_set_encode_small_max.argtypes = [c_int]
+        lib.qjl_testing_set_encode_small_max.restype = c_int
+        lib.qjl_testing_set_encode_small_max.argtypes = [c_int]
         v = lib.qjl_abi_version()
         if v != ABI_VERSION:
             raise RuntimeError(f"libqjl ABI version {v}, binding expects {ABI_VERSION}")
@@ -95,11 +96,13 @@ def sketch_host(seed: int, d: int, m: int) -> np.ndarray:
     return out
 
 
-def _stream_handle(stream):
+def _resolve_stream(stream):
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream_handle(stream):
+    return _resolve_stream(stream).cuda_stream
 
 
 def _ptr(t):
@@ -132,24 +135,35 @@ def decode_workspace_bytes(B, H_q, H_kv, N, d, m) -> int:
     return load().qjl_decode_workspace_bytes(B, H_q, H_kv, N, d, m)
 
 
-def workspace_for(nbytes: int, device):
-    """A zero-filled workspace of at least nbytes, cached per device.
+def workspace_for(nbytes: int, device, stream=None):
+    """A zero-filled workspace of at least nbytes, cached per (device, stream).
 
-    Calls on one stream may share it (each call returns its counters to zero);
-    callers running decode on several streams at once pass their own.
+    It is allocated and zero-filled on ``stream`` (default: the current
+    stream), so it is ready for the kernels queued there, and the caching
+    allocator keeps its memory for that stream.  Calls on one stream share
+    it (each call returns its counters to zero); calls on other streams get
+    their own.
     """
     import torch
-    key = (str(device),)
+    s = _resolve_stream(stream)
+    key = (str(device), s.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
 
 def decode_attention(q, signs, norms, values, N: int, seed: int, m: int, scale: float | None = None,
                      out=None, workspace=None, stream=None):
-    """One QJL decode step; returns out fp32 [B][H_q][d]."""
+    """One QJL decode step; returns out fp32 [B][H_q][d].
+
+    Runs on ``stream`` (default: the current stream).  The inputs must be
+    ready on that stream (the caller orders other streams' writes before
+    it); ``out`` and the cached workspace, when this function makes them,
+    are allocated on that stream.
+    """
     import torch
     B, H_q, d = q.shape
     _, H_kv, cap, _ = values.shape
@@ -159,22 +173,25 @@ def decode_attention(q, signs, norms, values, N: int, seed: int, m: int, scale: 
         raise ValueError("values must be contiguous 16-bit (bf16 bits) [B][H_kv][cap][d]")
     if tuple(signs.shape) != (B, H_kv, cap, m // 32) or tuple(norms.shape) != (B, H_kv, cap):
         raise ValueError("signs/norms shapes do not match values")
+    s = _resolve_stream(stream)
     if out is None:
-        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+        with torch.cuda.stream(s):
+            out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
     need = decode_workspace_bytes(B, H_q, H_kv, N, d, m)
     if workspace is None:
-        workspace = workspace_for(need, q.device)
+        workspace = workspace_for(need, q.device, s)
     _check(load().qjl_decode_attention(
         _ptr(q), _ptr(signs), _ptr(norms), _ptr(values), B, H_q, H_kv, N, cap, d, m,
         seed & (2 ** 64 - 1), 0.0 if scale is None else float(scale), _ptr(out),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+        _ptr(workspace), workspace.numel() * workspace.element_size(), s.cuda_stream))
     return out
 
 
-def set_encode_small_max(keys: int) -> int:
-    """Largest encode call (in keys) that runs the small-set kernel; returns
-    the previous limit (a negative ``keys`` only queries it)."""
-    return load().qjl_set_encode_small_max(keys)
+def testing_set_encode_small_max(keys: int) -> int:
+    """Test hook (csrc/qjl_testing.h): the largest encode call, in keys, that
+    the calling thread sends to the small-set kernel; returns the thread's
+    previous limit (a negative ``keys`` only queries it)."""
+    return load().qjl_testing_set_encode_small_max(keys)
 
 
 def release_cache():

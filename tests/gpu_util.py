@@ -52,3 +52,47 @@ def row_rel_l2(got, ref):
     num = np.linalg.norm(g - r, axis=1)
     den = np.maximum(np.linalg.norm(r, axis=1), 1e-300)
     return float((num / den).max())
+
+
+def oracle_encode(keys_flat, S, chunk=16384):
+    """oracle.encode over [R][d] keys, in chunks spread over host threads.
+
+    The oracle itself is unchanged: each chunk is one oracle.encode call, and
+    the chunks are joined in order.  numpy releases the interpreter lock in
+    its array loops, so threads run the chunks in parallel (one BLAS thread
+    each, so the threads do not oversubscribe the cores).
+    """
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    keys_flat = np.ascontiguousarray(keys_flat)
+    R = keys_flat.shape[0]
+    if R <= chunk:
+        return oracle.encode(keys_flat, S)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    starts = list(range(0, R, chunk))
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(lambda c: oracle.encode(keys_flat[c:c + chunk], S), starts))
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+
+
+_WL_CACHE = {}
+
+
+def cached_workload(name):
+    """The named workload, drawn once per test session (several GPU tests
+    share the large ones), with the oracle's encode of its keys."""
+    import oracle
+    from jl_rotated_bit_amd import workloads as wl
+
+    if name not in _WL_CACHE:
+        _WL_CACHE.clear()
+        w = wl.WORKLOADS[name]()
+        d = w.keys.shape[-1]
+        words, norms = oracle_encode(w.keys.reshape(-1, d), oracle.sketch(w.seed, d, w.m))
+        B, H, n = w.keys.shape[:3]
+        _WL_CACHE[name] = (w, words.reshape(B, H, n, w.m // 32), norms.reshape(B, H, n))
+    return _WL_CACHE[name]

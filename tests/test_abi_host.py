@@ -17,6 +17,7 @@ from jl_rotated_bit_amd import qjl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qjl.h")
+TESTING_HEADER = os.path.join(ROOT, "jl_rotated_bit_amd", "csrc", "qjl_testing.h")
 
 EINVAL, EUNSUP, EWS = 1, 2, 3
 
@@ -26,37 +27,48 @@ def lib():
     return qjl.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return re.findall(r"QJL_API\s+[\w\s\*]+?\b(qjl_\w+)\s*\(", text)
 
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
-    for name in names:
+    testing = declared_functions(TESTING_HEADER)
+    assert testing == ["qjl_testing_set_encode_small_max"]
+    for name in names + testing:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", qjl.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     assert set(names) <= exported
-    # nothing else with the qjl_ prefix leaks out
-    assert {n for n in exported if n.startswith("qjl_")} == set(names)
+    # nothing else with the qjl_ prefix leaks out: the public header's calls
+    # and the test hooks of the internal header
+    assert {n for n in exported if n.startswith("qjl_")} == set(names) | set(testing)
+    # the public header holds no process-wide routing switch
+    assert not any("small_max" in n for n in names)
 
 
-def test_encode_small_max_knob(lib):
-    """The small-set encode limit: default 512, set and query without a GPU."""
-    lib.qjl_set_encode_small_max.restype = ctypes.c_int32
-    lib.qjl_set_encode_small_max.argtypes = [ctypes.c_int32]
-    start = lib.qjl_set_encode_small_max(-1)
+def test_encode_small_max_hook_is_per_thread(lib):
+    """The small-set encode limit (test hook): default 512, set and queried
+    without a GPU, and a change on one thread leaves other threads at the
+    default."""
+    import threading
+    f = lib.qjl_testing_set_encode_small_max
+    start = f(-1)
     try:
         assert start == 512
-        assert lib.qjl_set_encode_small_max(0) == 512
-        assert lib.qjl_set_encode_small_max(-5) == 0
-        assert lib.qjl_set_encode_small_max(100000) == 0
-        assert lib.qjl_set_encode_small_max(-1) == 100000
+        assert f(0) == 512
+        assert f(-5) == 0
+        assert f(100000) == 0
+        seen = []
+        t = threading.Thread(target=lambda: seen.append(f(-1)))
+        t.start()
+        t.join()
+        assert seen == [512]
+        assert f(-1) == 100000
     finally:
-        lib.qjl_set_encode_small_max(start)
+        f(start)
 
 
 def test_library_targets_gfx950_only():

@@ -14,7 +14,8 @@ import pytest
 import oracle
 from jl_rotated_bit_amd import workloads as wl
 
-from .gpu_util import dev_f32, dev_u16, dev_u32, gpu_encode, host_u32, row_rel_l2, say
+from .gpu_util import (cached_workload, dev_f32, dev_u16, dev_u32, gpu_encode, host_u32,
+                       oracle_encode, row_rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +26,7 @@ TIGHT_TOL = 1e-4
 
 def oracle_cache(keys, m, seed=SEED):
     B, H, n, d = keys.shape
-    words, norms = oracle.encode(keys.reshape(-1, d), oracle.sketch(seed, d, m))
+    words, norms = oracle_encode(keys.reshape(-1, d), oracle.sketch(seed, d, m))
     return words.reshape(B, H, n, m // 32), norms.reshape(B, H, n)
 
 
@@ -74,16 +75,18 @@ def test_gqa32k_full(gpu_lib):
 
 
 def test_mha16k_full(gpu_lib):
-    w = wl.mha16k()
-    # the encode of 5.2M keys is covered (sampled) in the encode tests; here the
-    # cache comes from the GPU encode, checked bit-exact on a sample of rows
+    """The whole 40-head, batch-8, 16K workload: the GPU encode of all
+    5 242 880 keys equals the oracle's cache (every word, every norm within
+    1e-5), then the decode runs on the oracle's own cache, so the two halves
+    are checked independently."""
+    w, ref_w, ref_n = cached_workload("mha16k")
+    say("mha16k encode, all rows")
     signs, norms = gpu_encode(gpu_lib, w.keys, w.m, SEED)
-    words = host_u32(signs)
-    rows = np.random.default_rng(1).choice(w.B * w.H_kv * w.N, 4096, replace=False)
-    flat_w = words.reshape(-1, w.m // 32)
-    ref_w, _ = oracle.encode(w.keys.reshape(-1, 128)[rows], oracle.sketch(SEED, 128, w.m))
-    assert np.array_equal(flat_w[rows], ref_w)
-    check_decode(gpu_lib, w.q, words, norms.cpu().numpy(), w.values, w.N, w.m, label="mha16k")
+    assert np.array_equal(host_u32(signs), ref_w)
+    got_n = norms.cpu().numpy()
+    assert np.all(np.abs(got_n.astype(np.float64) - ref_n) <= 1e-5 * ref_n)
+    del signs, norms
+    check_decode(gpu_lib, w.q, ref_w, ref_n, w.values, w.N, w.m, label="mha16k")
 
 
 def test_long64k_append_steps(gpu_lib):
@@ -240,3 +243,32 @@ def test_workspace_reuse_across_calls(gpu_lib):
         ref = oracle.decode(q, words, norms, values, N, S)
         assert row_rel_l2(outs[i], ref) <= TIGHT_TOL
         assert np.array_equal(outs[i], outs[i + len(cases)])
+
+
+def test_side_stream_with_fresh_workspace(gpu_lib):
+    """A decode on a stream other than the current one, with the workspace
+    and output made by the binding: they are allocated and zero-filled on
+    that stream, so the result equals the oracle's and the default-stream
+    result, bit for bit."""
+    import torch
+    rng = np.random.default_rng(12)
+    B, Hkv, G, N, m = 1, 8, 4, 20000, 256
+    keys = wl.gaussian_keys(rng, B * Hkv * N).reshape(B, Hkv, N, 128)
+    values = wl.gaussian_keys(rng, B * Hkv * N).reshape(B, Hkv, N, 128)
+    q = rng.standard_normal((B, Hkv * G, 128)).astype(np.float32)
+    words, norms = oracle_cache(keys, m)
+    say("decode on a side stream", "splits", gpu_lib.decode_num_splits(B, Hkv * G, Hkv, N, 128, m))
+    qd, wd, nd, vd = dev_f32(q), dev_u32(words), dev_f32(norms), dev_u16(values)
+    ref_dev = gpu_lib.decode_attention(qd, wd, nd, vd, N, SEED, m)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        gpu_lib._workspaces.clear()          # a fresh workspace for every call
+        outs.append(gpu_lib.decode_attention(qd, wd, nd, vd, N, SEED, m, stream=side))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, words, norms, values, N, oracle.sketch(SEED, 128, m))
+    for o in outs:
+        assert row_rel_l2(o.cpu().numpy(), ref) <= TIGHT_TOL
+        assert torch.equal(o, ref_dev)

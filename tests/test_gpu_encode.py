@@ -11,7 +11,7 @@ import pytest
 import oracle
 from jl_rotated_bit_amd import workloads as wl
 
-from .gpu_util import SENTINEL, gpu_encode, host_u32, say
+from .gpu_util import SENTINEL, cached_workload, gpu_encode, host_u32, oracle_encode, say
 
 pytestmark = pytest.mark.gpu
 
@@ -19,17 +19,22 @@ SEED = 42
 NORM_RTOL = 1e-5
 
 
-def check_encode(qjl, keys, m, seed=SEED, cap=None, pos=0, sample_rows=None, label=""):
+def check_encode(qjl, keys, m, seed=SEED, cap=None, pos=0, label="", ref=None):
+    """GPU encode of every key against the oracle: all sign words bit for
+    bit, all norms within NORM_RTOL, rows outside [pos, pos + n) untouched.
+    ``ref`` = (words [R][m/32], norms [R]) when the oracle's encode of these
+    keys is already at hand."""
     B, H, n, d = keys.shape
     cap = n + pos if cap is None else cap
     say("encode", label, (B, H, n, d), "m", m, "cap", cap, "pos", pos)
     signs, norms = gpu_encode(qjl, keys, m, seed, cap=cap, pos=pos)
     got_w = host_u32(signs)
     got_n = norms.cpu().numpy()
-    S = oracle.sketch(seed, d, m)
     flat = keys.reshape(-1, d)
-    rows = np.arange(flat.shape[0]) if sample_rows is None else sample_rows
-    ref_w, ref_n = oracle.encode(flat[rows], S)
+    rows = np.arange(flat.shape[0])
+    if ref is None:
+        ref = oracle_encode(flat, oracle.sketch(seed, d, m))
+    ref_w, ref_n = ref
     bh, t = rows // n, rows % n
     gw = got_w[bh // H, bh % H, pos + t]
     gn = got_n[bh // H, bh % H, pos + t]
@@ -39,12 +44,11 @@ def check_encode(qjl, keys, m, seed=SEED, cap=None, pos=0, sample_rows=None, lab
     zero = ref_n == 0
     assert np.all(gn[zero] == 0)
     assert rel[~zero].max(initial=0.0) <= NORM_RTOL
-    if sample_rows is None:
-        # rows outside [pos, pos + n) are untouched
-        mask = np.ones(cap, bool)
-        mask[pos:pos + n] = False
-        assert np.all(got_w[:, :, mask] == np.uint32(SENTINEL))
-        assert np.all(np.isnan(got_n[:, :, mask]))
+    # rows outside [pos, pos + n) are untouched
+    mask = np.ones(cap, bool)
+    mask[pos:pos + n] = False
+    assert np.all(got_w[:, :, mask] == np.uint32(SENTINEL))
+    assert np.all(np.isnan(got_n[:, :, mask]))
     return got_w, got_n
 
 
@@ -52,9 +56,9 @@ def check_encode(qjl, keys, m, seed=SEED, cap=None, pos=0, sample_rows=None, lab
 def enc_path(request, gpu_lib):
     """Runs a test through one encode kernel: the tile kernel (limit 0) or
     the small-set kernel (no limit), whatever the size."""
-    prev = gpu_lib.set_encode_small_max(0 if request.param == "tile" else 2 ** 31 - 1)
+    prev = gpu_lib.testing_set_encode_small_max(0 if request.param == "tile" else 2 ** 31 - 1)
     yield request.param
-    gpu_lib.set_encode_small_max(prev)
+    gpu_lib.testing_set_encode_small_max(prev)
 
 
 def test_small_workload_keys(gpu_lib, enc_path):
@@ -188,25 +192,22 @@ def test_long64k_keys_m512(gpu_lib):
     check_encode(gpu_lib, w.keys, w.m, label="long64k keys (m=512)")
 
 
-def test_mha16k_keys_sampled(gpu_lib):
-    w = wl.mha16k()
-    R = w.keys.shape[0] * w.keys.shape[1] * w.keys.shape[2]
-    rows = np.sort(np.random.default_rng(5).choice(R, 200_000, replace=False))
-    check_encode(gpu_lib, w.keys, w.m, sample_rows=rows, label="mha16k keys (sampled rows)")
+def test_mha16k_keys_full(gpu_lib):
+    """All 5 242 880 keys of the 40-head, batch-8, 16K cache (five launches)."""
+    w, ref_w, ref_n = cached_workload("mha16k")
+    check_encode(gpu_lib, w.keys, w.m, label="mha16k keys (all rows)",
+                 ref=(ref_w.reshape(-1, w.m // 32), ref_n.reshape(-1)))
 
 
 def test_large_ragged_uneven_split(gpu_lib):
     """Enough tiles that the first workgroup of each CU takes a larger share,
     with a tile count that is no multiple of the grid and a per-head row
     count that is no multiple of the 128-row tile (tiles cross heads);
-    every row of the first and last tiles plus a sample in between."""
+    every row."""
     rng = np.random.default_rng(11)
     B, H, n = 1, 8, 32768 + 77
     keys = wl.gaussian_keys(rng, B * H * n).reshape(B, H, n, 128)
-    R = B * H * n
-    rows = np.unique(np.concatenate([np.arange(0, 4096), np.arange(R - 4096, R),
-                                     np.random.default_rng(12).choice(R, 30_000, replace=False)]))
-    check_encode(gpu_lib, keys, 256, cap=n + 5, pos=3, sample_rows=rows, label="large ragged")
+    check_encode(gpu_lib, keys, 256, cap=n + 5, pos=3, label="large ragged")
 
 
 def launch_starts(R, m, cus=256):
@@ -226,15 +227,11 @@ def test_across_launch_chunks(gpu_lib, m, H, n):
     """Key sets around the size one launch takes, with a per-head row count
     that is no multiple of the tile: two launches at m = 256 (1.2 M keys) and
     at m = 512 (590 K keys), and one launch in which a workgroup takes a
-    seventeenth tile (65537 tokens of 8 heads at m = 512).  Rows around each
-    launch boundary, the first and last rows, and a sample."""
+    seventeenth tile (65537 tokens of 8 heads at m = 512).  Every row."""
     rng = np.random.default_rng(13 + m + H)
     keys = wl.gaussian_keys(rng, H * n).reshape(1, H, n, 128)
-    R = H * n
-    around = [np.arange(max(0, c - 3000), min(R, c + 3000)) for c in launch_starts(R, m)]
-    rows = np.unique(np.concatenate([np.arange(0, 2000), np.arange(R - 2000, R), *around,
-                                     np.random.default_rng(14).choice(R, 20_000, replace=False)]))
-    check_encode(gpu_lib, keys, m, sample_rows=rows, label="across launch chunks")
+    say("launch boundaries at rows", launch_starts(H * n, m))
+    check_encode(gpu_lib, keys, m, label="across launch chunks")
 
 
 def test_launch_starts_rule():
@@ -257,7 +254,7 @@ def test_default_limit_both_sides(gpu_lib, m):
     """With the default limit (512 keys), calls of 512 keys run the small-set
     kernel and calls of 513 the tile kernel; both match the oracle, and the
     one-token append of a decode step (one key per kv head) is exact."""
-    assert gpu_lib.set_encode_small_max(-1) == 512
+    assert gpu_lib.testing_set_encode_small_max(-1) == 512
     rng = np.random.default_rng(600 + m)
     for B, H, n in [(1, 4, 128), (1, 1, 513), (2, 8, 1)]:
         keys = wl.gaussian_keys(rng, B * H * n).reshape(B, H, n, 128)
