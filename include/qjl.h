@@ -145,6 +145,37 @@ QJL_API qjl_status qjl_decode_attention(const float *q, const uint32_t *signs, c
                                         int32_t m, uint64_t seed, float scale, float *out,
                                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device scratch the library holds per GPU for
+ * qjl_decode_attention_noalloc: the 4096-byte counter region plus 4 MiB of
+ * split partials. */
+#define QJL_NOALLOC_SCRATCH_BYTES (4096u + (4u << 20))
+
+/* qjl_decode_attention without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, semantics and results as
+ * qjl_decode_attention (same kernels and split plan), except:
+ *   - The split scratch (arrival counters and partials) is a static array of
+ *     QJL_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ *     on until the process ends.  Sizes whose plan needs more
+ *     (qjl_decode_workspace_bytes(...) > QJL_NOALLOC_SCRATCH_BYTES with more
+ *     than one split; only very many kv heads with G = 8 get there) return
+ *     QJL_EWORKSPACE before anything is launched.
+ *   - Nothing is allocated: no hipMalloc, hipFree or allocating library call.
+ *     S for (seed, d, m) must already be resident on the current device
+ *     (any earlier qjl_encode_keys or qjl_decode_attention call with this
+ *     seed, d and m on it uploads it); otherwise QJL_EINVAL.
+ *   - The first call on a device looks up the array's device address and
+ *     queues a small kernel on `stream` that clears its counter region.
+ *   - All calls on one GPU share its array, which keeps the last call's
+ *     contents: calls that may overlap on one GPU (several streams, several
+ *     threads) race and give wrong results.  Serialize them.
+ * Returns QJL_OK, QJL_EINVAL, QJL_EUNSUPPORTED, QJL_EWORKSPACE or QJL_EHIP. */
+QJL_API qjl_status qjl_decode_attention_noalloc(const float *q, const uint32_t *signs,
+                                                const float *norms, const void *values_bf16,
+                                                int32_t B, int32_t H_q, int32_t H_kv, int32_t N,
+                                                int32_t cap, int32_t d, int32_t m, uint64_t seed,
+                                                float scale, float *out, void *stream);
+
 /* Frees the library's device copies of S on every device (waits for the
  * device first).  Later calls re-create them on demand. */
 QJL_API qjl_status qjl_release_cache(void);

@@ -18,6 +18,16 @@
 #include "qjl.h"
 #include "qjl_testing.h"
 
+// ---- library-held scratch of the allocation-free decode ----
+// Arrival counters (the same fixed region a caller's workspace starts with)
+// and the split partials, in one static device array; every GPU the library
+// runs on holds its own copy until the process ends.  Host code never uses
+// this name as an address: the per-device address comes from
+// hipGetSymbolAddress (scratch_for_device below).
+static constexpr size_t kScratchBytes = QJL_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > qjl::kCounterRegionBytes, "scratch must hold the counter region");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 constexpr int32_t kAbiVersion = 2;
@@ -133,6 +143,126 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
   return QJL_OK;
 }
 
+// The cached S for (current device, seed, d, m), or QJL_EINVAL when it is
+// not resident yet.  Never allocates.
+qjl_status find_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QJL_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  auto it = g_cache.find(std::make_tuple(dev, seed, d, m));
+  if (it == g_cache.end())
+    return fail(QJL_EINVAL,
+                "S for seed %llu, d=%d, m=%d is not resident on device %d: a qjl_encode_keys or "
+                "qjl_decode_attention call with this seed on this device uploads it",
+                static_cast<unsigned long long>(seed), d, m, dev);
+  *out = it->second.view;
+  return QJL_OK;
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;   // device -> address of that device's `scratch`
+
+// Address of `scratch` on the current device.  The first call on a device
+// looks it up (hipGetSymbolAddress; the array's name in host code is only a
+// stand-in) and queues a fill kernel that clears the counter region on
+// `stream`.  Allocates nothing.
+qjl_status scratch_for_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QJL_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    *out = it->second;
+    return QJL_OK;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return fail(QJL_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  constexpr int kWords = static_cast<int>(qjl::kCounterRegionBytes / 4);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((kWords + 255) / 256), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(ptr), kWords);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(QJL_EHIP, "clearing the scratch counters: %s", hipGetErrorString(e));
+  g_scratch.emplace(dev, ptr);
+  *out = ptr;
+  return QJL_OK;
+}
+
+// Shared by qjl_decode_attention and its allocation-free variant: validation,
+// plan, sketch and launch.  With `noalloc`, the workspace is the library's
+// static scratch and S must already be resident.
+qjl_status decode_common(const char* fn, const float* q, const uint32_t* signs, const float* norms,
+                         const void* values_bf16, int32_t B, int32_t H_q, int32_t H_kv, int32_t N,
+                         int32_t cap, int32_t d, int32_t m, uint64_t seed, float scale, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+  g_last_error.clear();
+  if (!supported_dm(d, m))
+    return fail(QJL_EUNSUPPORTED, "%s: d=%d m=%d unsupported (d=128, m in {256,512})", fn, d, m);
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || cap <= 0 || N <= 0 || N > cap)
+    return fail(QJL_EINVAL, "%s: bad sizes B=%d H_q=%d H_kv=%d N=%d cap=%d", fn, B, H_q, H_kv, N, cap);
+  if (H_q % H_kv != 0)
+    return fail(QJL_EINVAL, "%s: H_q=%d is not a multiple of H_kv=%d", fn, H_q, H_kv);
+  const int G = H_q / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(QJL_EUNSUPPORTED, "%s: G=H_q/H_kv=%d unsupported (1, 2, 4, 8)", fn, G);
+  if (static_cast<int64_t>(B) * H_kv * cap > (int64_t{1} << 40))
+    return fail(QJL_EINVAL, "%s: cache too large", fn);
+  if (!(scale >= 0.0f) || std::isinf(scale))
+    return fail(QJL_EINVAL, "%s: scale must be finite and >= 0", fn);
+  if (q == nullptr || signs == nullptr || norms == nullptr || values_bf16 == nullptr || out == nullptr)
+    return fail(QJL_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned(q, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(values_bf16, 16) ||
+      !aligned(out, 16))
+    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+  qjl::DecodePlan plan;
+  if (!qjl::make_decode_plan(B, H_q, H_kv, N, d, m, &plan))
+    return fail(QJL_EINVAL, "%s: no plan for these sizes", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (noalloc) {
+    if (plan.n_split > 1 && plan.total_bytes > kScratchBytes)
+      return fail(QJL_EWORKSPACE,
+                  "%s: these sizes need %zu bytes of split scratch, more than the %zu the "
+                  "library holds; use qjl_decode_attention with a workspace",
+                  fn, plan.total_bytes, kScratchBytes);
+    qjl::DeviceSketch s;
+    qjl_status rc = find_sketch(seed, d, m, &s);
+    if (rc != QJL_OK) return rc;
+    rc = scratch_for_device(st, &workspace);
+    if (rc != QJL_OK) return rc;
+    workspace_bytes = kScratchBytes;
+    const float sc = scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d))) : scale;
+    const int e = qjl::launch_decode(s, plan, q, signs, norms, values_bf16, B, H_q, H_kv, N, cap, sc,
+                                     out, workspace, stream);
+    if (e != hipSuccess)
+      return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
+    return QJL_OK;
+  }
+  if (plan.n_split > 1) {
+    if (workspace == nullptr || !aligned(workspace, 256))
+      return fail(QJL_EWORKSPACE, "%s: workspace NULL or not 256-byte aligned", fn);
+    if (workspace_bytes < plan.total_bytes)
+      return fail(QJL_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
+                  plan.total_bytes);
+  }
+  qjl::DeviceSketch s;
+  qjl_status rc = get_sketch(seed, d, m, &s);
+  if (rc != QJL_OK) return rc;
+  const float sc = scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d))) : scale;
+  const int e = qjl::launch_decode(s, plan, q, signs, norms, values_bf16, B, H_q, H_kv, N, cap, sc,
+                                   out, workspace, stream);
+  if (e != hipSuccess)
+    return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
+  return QJL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,44 +332,17 @@ QJL_API qjl_status qjl_decode_attention(const float* q, const uint32_t* signs, c
                                         int32_t H_kv, int32_t N, int32_t cap, int32_t d,
                                         int32_t m, uint64_t seed, float scale, float* out,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  if (!supported_dm(d, m))
-    return fail(QJL_EUNSUPPORTED, "qjl_decode_attention: d=%d m=%d unsupported (d=128, m in {256,512})", d, m);
-  if (B <= 0 || H_q <= 0 || H_kv <= 0 || cap <= 0 || N <= 0 || N > cap)
-    return fail(QJL_EINVAL, "qjl_decode_attention: bad sizes B=%d H_q=%d H_kv=%d N=%d cap=%d", B, H_q, H_kv, N, cap);
-  if (H_q % H_kv != 0)
-    return fail(QJL_EINVAL, "qjl_decode_attention: H_q=%d is not a multiple of H_kv=%d", H_q, H_kv);
-  const int G = H_q / H_kv;
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(QJL_EUNSUPPORTED, "qjl_decode_attention: G=H_q/H_kv=%d unsupported (1, 2, 4, 8)", G);
-  if (static_cast<int64_t>(B) * H_kv * cap > (int64_t{1} << 40))
-    return fail(QJL_EINVAL, "qjl_decode_attention: cache too large");
-  if (!(scale >= 0.0f) || std::isinf(scale))
-    return fail(QJL_EINVAL, "qjl_decode_attention: scale must be finite and >= 0");
-  if (q == nullptr || signs == nullptr || norms == nullptr || values_bf16 == nullptr || out == nullptr)
-    return fail(QJL_EINVAL, "qjl_decode_attention: NULL pointer");
-  if (!aligned(q, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(values_bf16, 16) ||
-      !aligned(out, 16))
-    return fail(QJL_EINVAL, "qjl_decode_attention: misaligned pointer");
-  qjl::DecodePlan plan;
-  if (!qjl::make_decode_plan(B, H_q, H_kv, N, d, m, &plan))
-    return fail(QJL_EINVAL, "qjl_decode_attention: no plan for these sizes");
-  if (plan.n_split > 1) {
-    if (workspace == nullptr || !aligned(workspace, 256))
-      return fail(QJL_EWORKSPACE, "qjl_decode_attention: workspace NULL or not 256-byte aligned");
-    if (workspace_bytes < plan.total_bytes)
-      return fail(QJL_EWORKSPACE, "qjl_decode_attention: workspace %zu bytes < %zu needed",
-                  workspace_bytes, plan.total_bytes);
-  }
-  qjl::DeviceSketch s;
-  qjl_status st = get_sketch(seed, d, m, &s);
-  if (st != QJL_OK) return st;
-  const float sc = scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d))) : scale;
-  const int e = qjl::launch_decode(s, plan, q, signs, norms, values_bf16, B, H_q, H_kv, N, cap, sc,
-                                   out, workspace, stream);
-  if (e != hipSuccess)
-    return fail(QJL_EHIP, "qjl_decode_attention: launch failed: %s", hipGetErrorString(static_cast<hipError_t>(e)));
-  return QJL_OK;
+  return decode_common("qjl_decode_attention", q, signs, norms, values_bf16, B, H_q, H_kv, N, cap,
+                       d, m, seed, scale, out, workspace, workspace_bytes, stream, false);
+}
+
+QJL_API qjl_status qjl_decode_attention_noalloc(const float* q, const uint32_t* signs,
+                                                const float* norms, const void* values_bf16,
+                                                int32_t B, int32_t H_q, int32_t H_kv, int32_t N,
+                                                int32_t cap, int32_t d, int32_t m, uint64_t seed,
+                                                float scale, float* out, void* stream) {
+  return decode_common("qjl_decode_attention_noalloc", q, signs, norms, values_bf16, B, H_q, H_kv,
+                       N, cap, d, m, seed, scale, out, nullptr, 0, stream, true);
 }
 
 QJL_API qjl_status qjl_release_cache(void) {

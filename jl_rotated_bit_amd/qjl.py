@@ -10,6 +10,7 @@ Names and semantics follow the C entry points:
 * ``sketch_host(seed, d, m)``                 -> qjl_sketch_host
 * ``encode_keys(keys, signs, norms, pos, seed, m)``        -> qjl_encode_keys
 * ``decode_attention(q, signs, norms, values, N, seed, m, scale)`` -> qjl_decode_attention
+* ``decode_attention_noalloc(q, signs, norms, values, N, seed, m, out)``  -> qjl_decode_attention_noalloc
 * ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache``
 * ``testing_set_encode_small_max`` -> qjl_testing_set_encode_small_max (a
   per-thread test hook, not part of the public header)
@@ -69,6 +70,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.qjl_decode_attention.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                              c_int, c_int, c_int, c_u64, ctypes.c_float, c_vp,
                                              c_vp, c_sz, c_vp]
+        lib.qjl_decode_attention_noalloc.restype = c_int
+        lib.qjl_decode_attention_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
+                                                     c_int, c_int, c_int, c_int, c_u64,
+                                                     ctypes.c_float, c_vp, c_vp]
         lib.qjl_release_cache.restype = c_int
         lib.qjl_release_cache.argtypes = []
         lib.qjl_testing_set_encode_small_max.restype = c_int
@@ -185,6 +190,34 @@ def decode_attention(q, signs, norms, values, N: int, seed: int, m: int, scale: 
         seed & (2 ** 64 - 1), 0.0 if scale is None else float(scale), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), s.cuda_stream))
     return out
+
+
+def decode_attention_noalloc(q, signs, norms, values, N: int, seed: int, m: int, out,
+                             scale: float | None = None, stream=None):
+    """qjl_decode_attention_noalloc: one QJL decode step into ``out`` (fp32
+    [B][H_q][d], caller-provided) using the library's static per-GPU scratch;
+    nothing is allocated, here or in the library.  Calls that may overlap on
+    one GPU race (they share the scratch)."""
+    import torch
+    B, H_q, d = q.shape
+    _, H_kv, cap, _ = values.shape
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp32 [B][H_q][d]")
+    if values.element_size() != 2 or not values.is_contiguous():
+        raise ValueError("values must be contiguous 16-bit (bf16 bits) [B][H_kv][cap][d]")
+    if tuple(signs.shape) != (B, H_kv, cap, m // 32) or tuple(norms.shape) != (B, H_kv, cap):
+        raise ValueError("signs/norms shapes do not match values")
+    if out is None or tuple(out.shape) != (B, H_q, d) or out.dtype != torch.float32 \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [B][H_q][d] tensor")
+    _check(load().qjl_decode_attention_noalloc(
+        _ptr(q), _ptr(signs), _ptr(norms), _ptr(values), B, H_q, H_kv, N, cap, d, m,
+        seed & (2 ** 64 - 1), 0.0 if scale is None else float(scale), _ptr(out),
+        _stream_handle(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 4096 + (4 << 20)   # QJL_NOALLOC_SCRATCH_BYTES in include/qjl.h
 
 
 def testing_set_encode_small_max(keys: int) -> int:

@@ -162,6 +162,39 @@ def test_decode_validation(lib):
     assert dec(lib, ws_bytes=need - 1, **big) == EWS
 
 
+def dec_na(lib, q=A16, signs=A16, norms=A16, values=A16, B=1, Hq=4, Hkv=1, N=8, cap=8, d=128,
+           m=256, scale=0.0, out=A16):
+    return lib.qjl_decode_attention_noalloc(q, signs, norms, values, B, Hq, Hkv, N, cap, d, m, 1,
+                                            ctypes.c_float(scale), out, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode validates like qjl_decode_attention, and
+    rejects plans whose split scratch exceeds the library's static array
+    before any GPU call."""
+    header = open(HEADER).read()
+    assert "#define QJL_NOALLOC_SCRATCH_BYTES (4096u + (4u << 20))" in header
+    assert qjl.NOALLOC_SCRATCH_BYTES == 4096 + (4 << 20)
+    assert dec_na(lib, d=96) == EUNSUP
+    assert dec_na(lib, Hq=6, Hkv=2) == EUNSUP
+    assert dec_na(lib, N=9, cap=8) == EINVAL
+    assert dec_na(lib, scale=-1.0) == EINVAL
+    for name in ("q", "signs", "norms", "values", "out"):
+        assert dec_na(lib, **{name: None}) == EINVAL
+    assert dec_na(lib, out=A16 + 8) == EINVAL
+    # 511 kv heads x 8 query heads each, two splits: 8176 partials of 130 floats
+    big = dict(B=1, Hq=4088, Hkv=511, N=4096, cap=4096)
+    need = lib.qjl_decode_workspace_bytes(1, 4088, 511, 4096, 128, 256)
+    assert lib.qjl_decode_num_splits(1, 4088, 511, 4096, 128, 256) == 2
+    assert need > qjl.NOALLOC_SCRATCH_BYTES
+    assert dec_na(lib, **big) == EWS
+    assert "more than the" in qjl.last_error()
+    # the largest plans of the benchmark workloads fit
+    for B, Hq, Hkv, N, m in [(1, 32, 8, 32768, 256), (1, 32, 8, 65600, 512), (8, 40, 40, 16384, 256),
+                             (1, 2048, 256, 4096, 256)]:
+        assert lib.qjl_decode_workspace_bytes(B, Hq, Hkv, N, 128, m) <= qjl.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_plan_properties(lib):
     for B, Hq, Hkv, N, m in [(1, 8, 1, 4096, 256), (1, 32, 8, 32768, 256), (1, 32, 8, 65600, 512),
                              (8, 40, 40, 16384, 256), (1, 4, 4, 1, 256), (2, 16, 2, 777, 512),
