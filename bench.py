@@ -4,19 +4,34 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 encode the workload's cached keys (sign bits + norms), then one decode step
 over them (S^T q, bit-estimated scores, online softmax, weighted sum of bf16
-values).  The default workload is ``gqa32k``: Llama-3.1-8B-shaped GQA decode,
-32 query / 8 kv heads, d = 128, m = 256, batch 1, 32768 cached tokens.
+values).  The headline workload is ``gqa32k``: Llama-3.1-8B-shaped GQA
+decode, 32 query / 8 kv heads, d = 128, m = 256, batch 1, 32768 cached
+tokens.
 
-Reported ``value`` is the decode step's effective HBM bandwidth: algorithmic
+Headline ``value``: the decode step's effective HBM bandwidth, algorithmic
 bytes (sign words + norms + bf16 values + q + out) over the decode kernel's
-duration, timed with HIP events around K decode launches issued back to back
-(each on the next buffer set).  ``encode_keys_per_s`` is timed the same way.
-The event times of each kernel inside the K timed steps are reported too
-(``*_in_step``); they include the dispatch gap after the preceding event.  Inputs live in HBM before timing starts; every step uses the
-next of several buffer sets whose total exceeds 512 MB, so the 256 MB
-last-level cache cannot serve a step from an earlier one.
+duration, timed with HIP events on the launch stream around K decode
+launches issued back to back.  The encode is timed the same way.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa32k]
+Every timed loop cycles through a ring of buffer sets whose bytes touched by
+the timed kernels (read and written) add up to more than 600 MiB, more than
+twice the 256 MB last-level cache, so no launch finds its inputs left in that
+cache by an earlier one.
+
+With no ``--workload`` the line also carries ``configs``, one entry per
+other workload, each measured the same way in the same run:
+
+* ``small``    - 1 kv / 8 q heads, 4096 tokens: encode and decode latency;
+* ``prefill``  - 16 x 8192 tokens x 8 kv heads: encode keys/s, fraction of
+                 the bf16 matrix-core peak and of HBM bandwidth;
+* ``long64k``  - m = 512, 65536 cached tokens, then 64 consecutive decode
+                 steps that each append one token (encode of one key per kv
+                 head, then the decode over all tokens): per-step median,
+                 total and HBM fraction;
+* ``mha16k``   - 40 heads, batch 8, 16384 tokens: decode time and HBM
+                 fraction (and the encode of its 5.2 M keys).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
 from __future__ import annotations
@@ -31,10 +46,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 SEED = 42
-RING_BYTES = 600 * 2 ** 20      # > 2 x 256 MB last-level cache
+RING_BYTES = 600 * 2 ** 20      # > 2 x 256 MB last-level cache, per timed loop
+MAX_SETS = 512
+METRIC = "decode attention effective HBM GB/s (% peak) + encode keys/sec, 32K ctx"
 
 
 def log(*a):
@@ -67,38 +84,388 @@ def measured_traffic(kind, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def make_workload(name):
-    from jl_rotated_bit_amd import workloads as wl
-    if name == "gqa32k":
-        return wl.gqa32k()
-    if name == "mha16k":
-        return wl.mha16k()
-    if name == "small":
-        return wl.small()
-    if name == "long64k":
-        w = wl.long64k(steps=1)
-        w.N = w.cap
-        return w
-    raise SystemExit(f"unknown workload {name}")
-
-
 DESCRIPTIONS = {
     "gqa32k": "gqa32k: Llama-3.1-8B-shaped GQA decode, 32 q / 8 kv heads, d=128, m=256, batch 1, "
               "32768 cached tokens; encode of those 262144 keys + one decode step",
-    "mha16k": "mha16k: LLaMA-2-13B-shaped MHA decode, 40 heads, d=128, m=256, batch 8, 16384 tokens",
     "small": "small: 1 kv / 8 q heads, d=128, m=256, 4096 tokens",
-    "long64k": "long64k: 8 kv / 32 q heads, d=128, m=512, 65537 tokens",
+    "prefill": "prefill: encode of 16 x 8192 tokens x 8 kv heads (1048576 keys), d=128, m=256",
+    "long64k": "long64k: 8 kv / 32 q heads, d=128, m=512, 65536 cached tokens, then 64 decode steps "
+               "that each append one token",
+    "mha16k": "mha16k: LLaMA-2-13B-shaped MHA decode, 40 heads, d=128, m=256, batch 8, 16384 tokens",
 }
 
+
+def decode_bytes(B, Hq, Hkv, N, d, m):
+    """Algorithmic bytes of one decode call: per (token, kv head) m/8 bytes of
+    sign words, a 4-byte norm and 2d bytes of bf16 values; q and out."""
+    return B * Hkv * N * (m // 8 + 4 + 2 * d) + B * Hq * d * 4 * 2
+
+
+def encode_bytes_per_key(d, m):
+    """Per key: the bf16 key read, m/8 bytes of sign words and a norm written."""
+    return 2 * d + m // 8 + 4
+
+
+def ring_sets(touched_bytes):
+    return int(min(MAX_SETS, max(1, -(-RING_BYTES // max(1, touched_bytes)))))
+
+
+def roofline(achieved_gbs, traffic, kernel, alg_bytes):
+    return {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": kernel, "algorithmic_bytes_per_launch": int(alg_bytes)}
+
+
+class Timer:
+    """HIP events on the launch stream (torch's current stream, which is
+    the stream every call below is issued on)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def b2b(self, fn, reps):
+        """fn(i) for i < reps issued back to back between two events; ms per call."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def each(self, fn, reps):
+        """fn(i) back to back with an event between consecutive calls; returns
+        the per-call durations (ms) and the total (ms)."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(self.stream)
+        for i in range(reps):
+            fn(i)
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+        return per, ev[0].elapsed_time(ev[reps])
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def caches(B, Hkv, cap, m):
+    import torch
+    return (torch.zeros((B, Hkv, cap, m // 32), dtype=torch.int32, device="cuda"),
+            torch.zeros((B, Hkv, cap), dtype=torch.float32, device="cuda"))
+
+
+# ----------------------------------------------------------------------------
+# headline: gqa32k (encode of the cached keys + one decode step)
+# ----------------------------------------------------------------------------
+
+def bench_gqa32k(qjl, w, args, T):
+    import numpy as np
+    import torch
+    B, Hq, Hkv, N, cap, d, m = w.B, w.H_q, w.H_kv, w.N, w.cap, w.d, w.m
+    n_keys = B * Hkv * N
+    dbytes = decode_bytes(B, Hq, Hkv, N, d, m)
+    ebytes = n_keys * encode_bytes_per_key(d, m)
+    n_sets = ring_sets(min(dbytes, ebytes))
+    log(f"[bench] gqa32k: {n_sets} buffer sets (decode touches {dbytes / 2**20:.1f} MiB, "
+        f"encode {ebytes / 2**20:.1f} MiB per call)")
+    keys_h, vals_h = w.keys[:, :, :N], w.values
+    sets = []
+    for _ in range(n_sets):
+        signs, norms = caches(B, Hkv, cap, m)
+        sets.append(dict(keys=dev(keys_h), values=dev(vals_h), signs=signs, norms=norms,
+                         q=dev(w.q), out=torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")))
+    ws = torch.zeros(qjl.decode_workspace_bytes(B, Hq, Hkv, N, d, m), dtype=torch.uint8, device="cuda")
+    stream = T.stream
+
+    def enc(i):
+        s = sets[i % n_sets]
+        qjl.encode_keys(s["keys"], s["signs"], s["norms"], 0, SEED, m)
+
+    def dec(i):
+        s = sets[i % n_sets]
+        qjl.decode_attention(s["q"], s["signs"], s["norms"], s["values"], N, SEED, m,
+                             out=s["out"], workspace=ws)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        enc(i)
+        if ev is not None:
+            ev[1].record(stream)
+        dec(i)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"[bench] gqa32k warmup {args.warmup}")
+    for i in range(max(args.warmup, n_sets)):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] gqa32k timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    enc_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    # Kernel durations for the rooflines: each kernel launched back to back
+    # over the ring (events around single launches inside a step also hold
+    # the ~2-3 us of dispatch that a kernel following other work does not pay).
+    b2b_dec_ms = T.b2b(dec, args.steps)
+    b2b_enc_ms = T.b2b(enc, args.steps)
+    log(f"[bench] gqa32k back to back: decode {b2b_dec_ms * 1e3:.2f} us, encode {b2b_enc_ms * 1e3:.2f} us")
+
+    # A decode step that first appends one token: the newest key of every
+    # (batch, kv head) is encoded into row N - 1, then the decode runs over
+    # all N tokens.  (Writing the new value row is the caller's copy.)
+    new_keys = [s["keys"][:, :, N - 1:N].contiguous() for s in sets]
+
+    def append_step(i):
+        s = sets[i % n_sets]
+        qjl.encode_keys(new_keys[i % n_sets], s["signs"], s["norms"], N - 1, SEED, m)
+        dec(i)
+    append_ms = T.b2b(append_step, args.steps)
+    log(f"[bench] gqa32k append step (encode of {B * Hkv} keys + decode): {append_ms * 1e3:.2f} us")
+
+    if args.copy_calibration:
+        a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 256 MiB device copies done")
+
+    dec_s, enc_s = b2b_dec_ms / 1e3, b2b_enc_ms / 1e3
+    dec_gbs = dbytes / dec_s / 1e9
+    enc_gbs = ebytes / enc_s / 1e9
+    enc_tflops = 2.0 * n_keys * d * m / enc_s / 1e12
+    res = {
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "value": round(dec_gbs, 2),
+        "decode_frac_of_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_us": round(dec_s * 1e6, 3),
+        "decode_us_in_step": round(float(dec_ms.mean()) * 1e3, 3),
+        "decode_us_in_step_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+                                      round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
+        "append_step_us": round(append_ms * 1e3, 3),
+        "append_step_frac_of_hbm_peak": round(dbytes / (append_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "encode_keys_per_s": round(n_keys / enc_s, 1),
+        "encode_us": round(enc_s * 1e6, 3),
+        "encode_us_in_step": round(float(enc_ms.mean()) * 1e3, 3),
+        "ring_sets": n_sets,
+        "roofline": roofline(dec_gbs, measured_traffic("decode", "gqa32k"), "decode_kernel", dbytes),
+        "roofline_encode": dict(roofline(enc_gbs, measured_traffic("encode", "gqa32k"), "encode_kernel", ebytes),
+                                mfma_tflops=round(enc_tflops, 2),
+                                mfma_frac_of_bf16_peak=round(enc_tflops / BF16_MFMA_PEAK_TFLOPS, 4)),
+    }
+    del sets, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------
+# other workloads
+# ----------------------------------------------------------------------------
+
+def bench_small(qjl, w, args, T):
+    import torch
+    B, Hq, Hkv, N, d, m = w.B, w.H_q, w.H_kv, w.N, w.d, w.m
+    dbytes = decode_bytes(B, Hq, Hkv, N, d, m)
+    ebytes = B * Hkv * N * encode_bytes_per_key(d, m)
+    n_sets = ring_sets(min(dbytes, ebytes))
+    sets = []
+    keys_d, vals_d, q_d = dev(w.keys), dev(w.values), dev(w.q)
+    for _ in range(n_sets):
+        signs, norms = caches(B, Hkv, N, m)
+        sets.append(dict(keys=keys_d.clone(), values=vals_d.clone(), signs=signs, norms=norms, q=q_d.clone(),
+                         out=torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")))
+    ws = torch.zeros(qjl.decode_workspace_bytes(B, Hq, Hkv, N, d, m), dtype=torch.uint8, device="cuda")
+
+    def enc(i):
+        s = sets[i % n_sets]
+        qjl.encode_keys(s["keys"], s["signs"], s["norms"], 0, SEED, m)
+
+    def dec(i):
+        s = sets[i % n_sets]
+        qjl.decode_attention(s["q"], s["signs"], s["norms"], s["values"], N, SEED, m, out=s["out"], workspace=ws)
+    reps = max(args.steps, n_sets)
+    for i in range(n_sets):
+        enc(i)
+        dec(i)
+    enc_ms = T.b2b(enc, reps)
+    dec_ms = T.b2b(dec, reps)
+    log(f"[bench] small: encode {enc_ms * 1e3:.2f} us, decode {dec_ms * 1e3:.2f} us")
+    del sets
+    torch.cuda.empty_cache()
+    gbs = dbytes / (dec_ms / 1e3) / 1e9
+    return {"workload": DESCRIPTIONS["small"], "encode_us": round(enc_ms * 1e3, 3),
+            "encode_keys_per_s": round(B * Hkv * N / (enc_ms / 1e3), 1),
+            "decode_us": round(dec_ms * 1e3, 3), "decode_gbs": round(gbs, 2),
+            "roofline": roofline(gbs, None, "decode_kernel", dbytes), "ring_sets": n_sets,
+            "note": "latency-bound (1.2 MB per decode call)"}
+
+
+def bench_prefill(qjl, w, args, T):
+    import torch
+    B, Hkv, n, d, m = w.B, w.H_kv, w.N, w.d, w.m
+    n_keys = B * Hkv * n
+    ebytes = n_keys * encode_bytes_per_key(d, m)
+    n_sets = ring_sets(ebytes)
+    sets = []
+    for _ in range(n_sets):
+        signs, norms = caches(B, Hkv, n, m)
+        sets.append((dev(w.keys), signs, norms))
+
+    def enc(i):
+        k, s, nm = sets[i % n_sets]
+        qjl.encode_keys(k, s, nm, 0, SEED, m)
+    for i in range(max(args.warmup, n_sets)):
+        enc(i)
+    ms = T.b2b(enc, args.steps)
+    sec = ms / 1e3
+    gbs = ebytes / sec / 1e9
+    tflops = 2.0 * n_keys * d * m / sec / 1e12
+    log(f"[bench] prefill: encode {ms * 1e3:.2f} us ({n_keys / sec / 1e9:.2f} G keys/s, "
+        f"{tflops:.0f} TFLOP/s)")
+    del sets
+    torch.cuda.empty_cache()
+    r = roofline(gbs, measured_traffic("encode", "prefill"), "encode_kernel", ebytes)
+    return {"workload": DESCRIPTIONS["prefill"], "encode_us": round(sec * 1e6, 3),
+            "encode_keys_per_s": round(n_keys / sec, 1),
+            "mfma_tflops": round(tflops, 2),
+            "mfma_frac_of_bf16_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline": r,
+            "roofline_mfma": {"bound": "mfma", "achieved": round(tflops, 2),
+                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                              "flops_per_launch": 2 * n_keys * d * m},
+            "ring_sets": n_sets}
+
+
+def bench_long64k(qjl, w, args, T):
+    import numpy as np
+    import torch
+    B, Hq, Hkv, N0, cap, d, m = w.B, w.H_q, w.H_kv, w.N, w.cap, w.d, w.m
+    steps = len(w.steps)
+    dbytes_last = decode_bytes(B, Hq, Hkv, N0 + steps, d, m)
+    n_sets = ring_sets(decode_bytes(B, Hq, Hkv, N0 + 1, d, m))
+    sets = []
+    keys_d = dev(w.keys)
+    new_keys = [keys_d[:, :, N0 + s:N0 + s + 1].contiguous() for s in range(steps)]
+    qs = [dev(q) for q in w.steps]
+    ws = torch.zeros(qjl.decode_workspace_bytes(B, Hq, Hkv, cap, d, m), dtype=torch.uint8, device="cuda")
+    for _ in range(n_sets):
+        signs, norms = caches(B, Hkv, cap, m)
+        # every set holds the whole encoded cache (the prefill, and the rows
+        # the steps append, which they re-encode identically)
+        qjl.encode_keys(keys_d, signs, norms, 0, SEED, m)
+        sets.append(dict(values=dev(w.values), signs=signs, norms=norms,
+                         out=torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")))
+    del keys_d
+
+    def step(s):
+        st = sets[s % n_sets]
+        qjl.encode_keys(new_keys[s], st["signs"], st["norms"], N0 + s, SEED, m)
+        qjl.decode_attention(qs[s], st["signs"], st["norms"], st["values"], N0 + s + 1, SEED, m,
+                             out=st["out"], workspace=ws)
+    T.each(step, steps)                           # warmup: the 64 steps once
+    per, total = T.each(step, steps)
+    per = np.array(per)
+    med = float(np.median(per))
+    alg = np.array([decode_bytes(B, Hq, Hkv, N0 + s + 1, d, m) for s in range(steps)], dtype=np.float64)
+    gbs_med = float(np.median(alg / (per / 1e3) / 1e9))
+    # the decode kernel alone, back to back, at the last step's context
+    dec_ms = T.b2b(lambda i: qjl.decode_attention(qs[-1], sets[i % n_sets]["signs"], sets[i % n_sets]["norms"],
+                                                  sets[i % n_sets]["values"], N0 + steps, SEED, m,
+                                                  out=sets[i % n_sets]["out"], workspace=ws), args.steps)
+    dec_gbs = dbytes_last / (dec_ms / 1e3) / 1e9
+    log(f"[bench] long64k: step median {med * 1e3:.2f} us, total {total:.3f} ms for {steps} steps; "
+        f"decode alone {dec_ms * 1e3:.2f} us")
+    del sets, ws
+    torch.cuda.empty_cache()
+    return {"workload": DESCRIPTIONS["long64k"], "steps": steps,
+            "step_us_median": round(med * 1e3, 3),
+            "step_us_p10_p90": [round(float(np.percentile(per, 10)) * 1e3, 3),
+                                round(float(np.percentile(per, 90)) * 1e3, 3)],
+            "total_ms": round(total, 4),
+            "step_frac_of_hbm_peak": round(gbs_med / HBM_PEAK_GBS, 4),
+            "decode_us": round(dec_ms * 1e3, 3),
+            "roofline": roofline(dec_gbs, measured_traffic("decode", "long64k"), "decode_kernel", dbytes_last),
+            "ring_sets": n_sets,
+            "note": "a step = encode of the appended key of each kv head + decode over all tokens; "
+                    "step fraction = the step's decode bytes / the step's time"}
+
+
+def bench_mha16k(qjl, w, args, T):
+    import torch
+    B, Hq, Hkv, N, d, m = w.B, w.H_q, w.H_kv, w.N, w.d, w.m
+    n_keys = B * Hkv * N
+    dbytes = decode_bytes(B, Hq, Hkv, N, d, m)
+    ebytes = n_keys * encode_bytes_per_key(d, m)
+    n_sets = ring_sets(dbytes)       # one set of 1.5 GB already exceeds the ring size (n_sets = 1)
+    keys_d = dev(w.keys)
+    signs, norms = caches(B, Hkv, N, m)
+    enc_reps = max(2, min(args.steps, 5))
+    for _ in range(2):
+        qjl.encode_keys(keys_d, signs, norms, 0, SEED, m)
+    enc_ms = T.b2b(lambda i: qjl.encode_keys(keys_d, signs, norms, 0, SEED, m), enc_reps)
+    del keys_d
+    torch.cuda.empty_cache()
+    sets = [dict(values=dev(w.values), signs=signs if k == 0 else signs.clone(),
+                 norms=norms if k == 0 else norms.clone(), q=dev(w.q),
+                 out=torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")) for k in range(n_sets)]
+    ws = torch.zeros(qjl.decode_workspace_bytes(B, Hq, Hkv, N, d, m), dtype=torch.uint8, device="cuda")
+
+    def dec(i):
+        s = sets[i % n_sets]
+        qjl.decode_attention(s["q"], s["signs"], s["norms"], s["values"], N, SEED, m, out=s["out"], workspace=ws)
+    for i in range(max(2, args.warmup)):
+        dec(i)
+    dec_ms = T.b2b(dec, args.steps)
+    gbs = dbytes / (dec_ms / 1e3) / 1e9
+    log(f"[bench] mha16k: decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s), encode {enc_ms * 1e3:.2f} us")
+    del sets, ws, signs, norms
+    torch.cuda.empty_cache()
+    return {"workload": DESCRIPTIONS["mha16k"], "decode_us": round(dec_ms * 1e3, 3),
+            "decode_gbs": round(gbs, 2), "decode_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "roofline": roofline(gbs, measured_traffic("decode", "mha16k"), "decode_kernel", dbytes),
+            "encode_us": round(enc_ms * 1e3, 3), "encode_keys_per_s": round(n_keys / (enc_ms / 1e3), 1),
+            "encode_hbm_frac": round(ebytes / (enc_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ring_sets": n_sets}
+
+
+# ----------------------------------------------------------------------------
+# the oracle on the host (cpu_baseline)
+# ----------------------------------------------------------------------------
 
 def cpu_baseline(w, min_decode_s=8.0, min_encode_s=4.0):
     """The oracle, as it stands, on this host: decode steps of the same
     workload (repeated until ~8 s) and an encode of a bounded key sample."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+        info = threadpool_info()
+        threads = max(i.get("num_threads", 1) for i in info) if info else 1
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     d, m = w.d, w.m
@@ -107,7 +474,7 @@ def cpu_baseline(w, min_decode_s=8.0, min_encode_s=4.0):
     t0 = time.perf_counter()
     enc_reps = 0
     while True:
-        words_s, _ = oracle.encode(sample_keys, S)
+        oracle.encode(sample_keys, S)
         enc_reps += 1
         if time.perf_counter() - t0 >= min_encode_s:
             break
@@ -123,9 +490,9 @@ def cpu_baseline(w, min_decode_s=8.0, min_encode_s=4.0):
         if time.perf_counter() - t0 >= min_decode_s:
             break
     dec_time = time.perf_counter() - t0
-    dec_bytes = decode_bytes(w)
+    dbytes = decode_bytes(w.B, w.H_q, w.H_kv, w.N, d, m)
     return {
-        "value": dec_bytes * reps / dec_time / 1e9,
+        "value": dbytes * reps / dec_time / 1e9,
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
@@ -138,21 +505,14 @@ def cpu_baseline(w, min_decode_s=8.0, min_encode_s=4.0):
     }
 
 
-def decode_bytes(w):
-    per_token = w.m // 8 + 4 + 2 * w.d
-    return w.B * w.H_kv * w.N * per_token + w.B * w.H_q * w.d * 4 * 2
-
-
-def encode_bytes_per_key(w):
-    return 2 * w.d + w.m // 8 + 4
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa32k", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--workload", default="all", choices=["all", *sorted(DESCRIPTIONS)],
+                    help="all (default): the gqa32k headline plus every other workload in `configs`; "
+                         "a name: that workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration runs)")
@@ -164,167 +524,61 @@ def main():
               "the QJL path runs on one GPU (no sharding or collectives).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from jl_rotated_bit_amd import qjl
+    from jl_rotated_bit_amd import workloads as wl
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
     qjl.load()
+    T = Timer()
 
-    log(f"[bench] generating workload {args.workload}")
-    w = make_workload(args.workload)
-    B, Hq, Hkv, N, cap, d, m = w.B, w.H_q, w.H_kv, w.N, w.cap, w.d, w.m
-    n_keys = B * Hkv * N
+    runners = {"small": bench_small, "prefill": bench_prefill, "long64k": bench_long64k,
+               "mha16k": bench_mha16k}
+    if args.workload not in ("all", "gqa32k"):
+        name = args.workload
+        log(f"[bench] generating workload {name}")
+        res = runners[name](qjl, wl.WORKLOADS[name](), args, T)
+        if args.copy_calibration:
+            a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
+            b = torch.empty_like(a)
+            for _ in range(3):
+                b.copy_(a)
+            torch.cuda.synchronize()
+        print(json.dumps({"workload_only": name, **res}), flush=True)
+        return
 
-    set_bytes = (w.keys.nbytes + w.values.nbytes + B * Hkv * cap * (m // 8 + 4))
-    n_sets = max(2, -(-RING_BYTES // set_bytes))
-    log(f"[bench] {n_sets} buffer sets of {set_bytes / 2**20:.0f} MiB")
-    keys_h = torch.from_numpy(w.keys[:, :, :N].copy().view(np.int16))
-    vals_h = torch.from_numpy(w.values.view(np.int16))
-    sets = []
-    for _ in range(n_sets):
-        sets.append(dict(
-            keys=keys_h.cuda(), values=vals_h.cuda(),
-            signs=torch.zeros((B, Hkv, cap, m // 32), dtype=torch.int32, device="cuda"),
-            norms=torch.zeros((B, Hkv, cap), dtype=torch.float32, device="cuda"),
-            q=torch.from_numpy(w.q).cuda(),
-            out=torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")))
-    ws = torch.zeros(qjl.decode_workspace_bytes(B, Hq, Hkv, N, d, m), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        s = sets[i % n_sets]
-        if ev is not None:
-            ev[0].record(stream)
-        qjl.encode_keys(s["keys"], s["signs"], s["norms"], 0, SEED, m)
-        if ev is not None:
-            ev[1].record(stream)
-        qjl.decode_attention(s["q"], s["signs"], s["norms"], s["values"], N, SEED, m,
-                             out=s["out"], workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
-
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-    enc_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    log(f"[bench] done: {total_ms:.3f} ms total, wall {t_wall * 1e3:.1f} ms")
-
-    # Per-kernel durations for the rooflines: each kernel launched back to back
-    # over the same buffer sets (a different set per launch), two events
-    # around the whole run.  Events around single launches inside the step
-    # (enc_ms / dec_ms above) also hold the ~2-3 us of dispatch that a kernel
-    # following other work in a stream does not pay.
-    def back_to_back(kind, reps):
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            s = sets[i % n_sets]
-            if kind == "encode":
-                qjl.encode_keys(s["keys"], s["signs"], s["norms"], 0, SEED, m)
-            else:
-                qjl.decode_attention(s["q"], s["signs"], s["norms"], s["values"], N, SEED, m,
-                                     out=s["out"], workspace=ws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
-    b2b_dec_ms = back_to_back("decode", args.steps)
-    b2b_enc_ms = back_to_back("encode", args.steps)
-    log(f"[bench] back to back: decode {b2b_dec_ms * 1e3:.2f} us, encode {b2b_enc_ms * 1e3:.2f} us")
-
-    # A decode step that first appends one token: the newest key of every
-    # (batch, kv head) is encoded into row N - 1 of the caches, then the
-    # decode runs over all N tokens.  (Writing the new value row is the
-    # caller's copy and is not timed.)
-    new_keys = [s["keys"][:, :, N - 1:N].contiguous() for s in sets]
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        s = sets[i % n_sets]
-        qjl.encode_keys(new_keys[i % n_sets], s["signs"], s["norms"], N - 1, SEED, m)
-        qjl.decode_attention(s["q"], s["signs"], s["norms"], s["values"], N, SEED, m,
-                             out=s["out"], workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    append_ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] append step (encode of {B * Hkv} keys + decode): {append_ms * 1e3:.2f} us")
-
-    if args.copy_calibration:
-        a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("[bench] copy calibration: 3 x 256 MiB device copies done")
-
-    dbytes = decode_bytes(w)
-    dec_s = b2b_dec_ms / 1e3
-    enc_s = b2b_enc_ms / 1e3
-    dec_gbs = dbytes / dec_s / 1e9
-    ebytes = n_keys * encode_bytes_per_key(w)
-    enc_gbs = ebytes / enc_s / 1e9
-    enc_tflops = 2.0 * n_keys * d * m / enc_s / 1e12
-    trf_dec = measured_traffic("decode", args.workload)
-    trf_enc = measured_traffic("encode", args.workload)
-
+    log("[bench] generating workload gqa32k")
+    w = wl.gqa32k()
+    head = bench_gqa32k(qjl, w, args, T)
+    configs = {}
+    if args.workload == "all":
+        for name in ("small", "prefill", "long64k", "mha16k"):
+            log(f"[bench] generating workload {name}")
+            t0 = time.perf_counter()
+            wk = wl.WORKLOADS[name]()
+            log(f"[bench] {name} generated in {time.perf_counter() - t0:.1f} s")
+            configs[name] = runners[name](qjl, wk, args, T)
+            del wk
     line = {
-        "metric": "decode attention effective HBM GB/s (% peak) + encode keys/sec, 32K ctx",
-        "value": round(dec_gbs, 2),
+        "metric": METRIC,
+        "value": head.pop("value"),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total_ms / args.steps, 5),
+        "ms_per_step": head.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": DESCRIPTIONS[args.workload], "batch": B, "q_heads": Hq,
-                   "kv_heads": Hkv, "context": N, "head_dim": d, "sketch_m": m,
+        "config": {"workload": DESCRIPTIONS["gqa32k"], "batch": w.B, "q_heads": w.H_q,
+                   "kv_heads": w.H_kv, "context": w.N, "head_dim": w.d, "sketch_m": w.m,
                    "sketch_seed": SEED},
-        "decode_frac_of_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
-        "decode_us": round(dec_s * 1e6, 3),
-        "decode_us_in_step": round(float(dec_ms.mean()) * 1e3, 3),
-        "decode_us_in_step_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
-                                      round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
-        "append_step_us": round(append_ms * 1e3, 3),
-        "append_step_frac_of_hbm_peak": round(dbytes / (append_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-        "encode_keys_per_s": round(n_keys / enc_s, 1),
-        "encode_us": round(enc_s * 1e6, 3),
-        "encode_us_in_step": round(float(enc_ms.mean()) * 1e3, 3),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": trf_dec, "kernel": "decode_kernel",
-                     "algorithmic_bytes_per_launch": dbytes},
-        "roofline_encode": {"bound": "hbm", "achieved": round(enc_gbs, 2), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
-                            "traffic": trf_enc, "kernel": "encode_kernel",
-                            "algorithmic_bytes_per_launch": ebytes,
-                            "mfma_tflops": round(enc_tflops, 2),
-                            "mfma_frac_of_bf16_peak": round(enc_tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+        **head,
+        "configs": configs,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
