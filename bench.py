@@ -247,6 +247,18 @@ def bench_gqa32k(qjl, w, args, T):
     append_ms = T.b2b(append_step, args.steps)
     log(f"[bench] gqa32k append step (encode of {B * Hkv} keys + decode): {append_ms * 1e3:.2f} us")
 
+    # The same step in one launch (qjl_decode_step): the append of token
+    # N - 1 (its key encoded, its value row copied) happens inside the decode.
+    new_vals = [s["values"][:, :, N - 1].contiguous() for s in sets]
+    new_keys1 = [k.reshape(B, Hkv, d) for k in new_keys]
+
+    def fused_step(i):
+        s = sets[i % n_sets]
+        qjl.decode_step(s["q"], new_keys1[i % n_sets], new_vals[i % n_sets], s["signs"], s["norms"],
+                        s["values"], N - 1, SEED, m, out=s["out"], workspace=ws)
+    fused_ms = T.b2b(fused_step, args.steps)
+    log(f"[bench] gqa32k fused step (append inside the decode launch): {fused_ms * 1e3:.2f} us")
+
     if args.copy_calibration:
         a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
@@ -269,6 +281,8 @@ def bench_gqa32k(qjl, w, args, T):
                                       round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
         "append_step_us": round(append_ms * 1e3, 3),
         "append_step_frac_of_hbm_peak": round(dbytes / (append_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "fused_step_us": round(fused_ms * 1e3, 3),
+        "fused_step_frac_of_hbm_peak": round(dbytes / (fused_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "encode_keys_per_s": round(n_keys / enc_s, 1),
         "encode_us": round(enc_s * 1e6, 3),
         "encode_us_in_step": round(float(enc_ms.mean()) * 1e3, 3),
@@ -383,13 +397,22 @@ def bench_long64k(qjl, w, args, T):
                          out=torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")))
     del keys_d
 
-    def step(s):
+    new_keys1 = [k.reshape(B, Hkv, d) for k in new_keys]
+    new_vals = [dev(w.values[:, :, N0 + s].copy()) for s in range(steps)]
+
+    def step(s):       # one launch: qjl_decode_step appends token N0 + s, then attends
+        st = sets[s % n_sets]
+        qjl.decode_step(qs[s], new_keys1[s], new_vals[s], st["signs"], st["norms"], st["values"],
+                        N0 + s, SEED, m, out=st["out"], workspace=ws)
+
+    def step2(s):      # two calls: encode of the new keys, then the decode
         st = sets[s % n_sets]
         qjl.encode_keys(new_keys[s], st["signs"], st["norms"], N0 + s, SEED, m)
         qjl.decode_attention(qs[s], st["signs"], st["norms"], st["values"], N0 + s + 1, SEED, m,
                              out=st["out"], workspace=ws)
     T.each(step, steps)                           # warmup: the 64 steps once
     per, total = T.each(step, steps)
+    per2, total2 = T.each(step2, steps)
     per = np.array(per)
     med = float(np.median(per))
     alg = np.array([decode_bytes(B, Hq, Hkv, N0 + s + 1, d, m) for s in range(steps)], dtype=np.float64)
@@ -399,8 +422,8 @@ def bench_long64k(qjl, w, args, T):
                                                   sets[i % n_sets]["values"], N0 + steps, SEED, m,
                                                   out=sets[i % n_sets]["out"], workspace=ws), args.steps)
     dec_gbs = dbytes_last / (dec_ms / 1e3) / 1e9
-    log(f"[bench] long64k: step median {med * 1e3:.2f} us, total {total:.3f} ms for {steps} steps; "
-        f"decode alone {dec_ms * 1e3:.2f} us")
+    log(f"[bench] long64k: fused step median {med * 1e3:.2f} us, total {total:.3f} ms for {steps} steps; "
+        f"two calls {float(np.median(per2)) * 1e3:.2f} us; decode alone {dec_ms * 1e3:.2f} us")
     del sets, ws
     torch.cuda.empty_cache()
     return {"workload": DESCRIPTIONS["long64k"], "steps": steps,
@@ -408,12 +431,16 @@ def bench_long64k(qjl, w, args, T):
             "step_us_p10_p90": [round(float(np.percentile(per, 10)) * 1e3, 3),
                                 round(float(np.percentile(per, 90)) * 1e3, 3)],
             "total_ms": round(total, 4),
+            "two_call_step_us_median": round(float(np.median(per2)) * 1e3, 3),
+            "two_call_total_ms": round(total2, 4),
             "step_frac_of_hbm_peak": round(gbs_med / HBM_PEAK_GBS, 4),
             "decode_us": round(dec_ms * 1e3, 3),
             "roofline": roofline(dec_gbs, measured_traffic("decode", "long64k"), "decode_kernel", dbytes_last),
             "ring_sets": n_sets,
-            "note": "a step = encode of the appended key of each kv head + decode over all tokens; "
-                    "step fraction = the step's decode bytes / the step's time"}
+            "note": "a step = qjl_decode_step: the append of one token per kv head (key encoded, value "
+                    "row copied) and the decode over all tokens, in one launch; two_call_* = "
+                    "qjl_encode_keys of the new keys then qjl_decode_attention; step fraction = the "
+                    "step's decode bytes / the step's time"}
 
 
 def bench_mha16k(qjl, w, args, T):

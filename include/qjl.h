@@ -145,6 +145,37 @@ QJL_API qjl_status qjl_decode_attention(const float *q, const uint32_t *signs, c
                                         int32_t m, uint64_t seed, float scale, float *out,
                                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* One decode step that first appends a token, in a single launch: token
+ * `pos` of every (batch, kv head) is encoded from new_keys_bf16 (sign bits
+ * of S^T k and ||k||, exactly as qjl_encode_keys defines them) into row `pos`
+ * of signs / norms, its value row is copied from new_values_bf16 into row
+ * `pos` of values_bf16, and query head h then attends over tokens [0, pos]
+ * as in qjl_decode_attention with N = pos + 1.  (The encode: "QJL: 1-Bit
+ * Quantized JL Transform ...", Abstract; "The Geometry of Forgetting", QJL
+ * section; every generated token leaves a key and a value in the cache and
+ * the next token attends over all of them, "The Geometry of Forgetting",
+ * opening section.)
+ *
+ *   q                fp32 [B][H_q][d], 16-byte aligned.
+ *   new_keys_bf16    bf16 [B][H_kv][d], 16-byte aligned (not inside the caches).
+ *   new_values_bf16  bf16 [B][H_kv][d], 16-byte aligned (not inside the caches).
+ *   signs, norms, values_bf16  the caches, [B][H_kv][cap][.], as for
+ *                    qjl_decode_attention; row `pos` is written, rows
+ *                    [0, pos) are read, other rows are untouched.
+ *   0 <= pos < cap.  scale, out: as for qjl_decode_attention.
+ *   workspace        as for qjl_decode_attention, at least
+ *                    qjl_decode_workspace_bytes(B, H_q, H_kv, pos + 1, d, m).
+ * The new sign words equal those qjl_encode_keys writes; the norm may differ
+ * from the tile encode's in the last fp32 bit (it is the fp32 rounding of the
+ * fp64 norm).  Returns QJL_OK, QJL_EINVAL, QJL_EUNSUPPORTED, QJL_EWORKSPACE,
+ * QJL_ENOMEM or QJL_EHIP. */
+QJL_API qjl_status qjl_decode_step(const float *q, const void *new_keys_bf16,
+                                   const void *new_values_bf16, uint32_t *signs, float *norms,
+                                   void *values_bf16, int32_t B, int32_t H_q, int32_t H_kv,
+                                   int32_t pos, int32_t cap, int32_t d, int32_t m, uint64_t seed,
+                                   float scale, float *out, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* Bytes of device scratch the library holds per GPU for
  * qjl_decode_attention_noalloc: the 4096-byte counter region plus 4 MiB of
  * split partials. */

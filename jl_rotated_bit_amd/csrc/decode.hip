@@ -46,6 +46,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "exact_sign.h"
 #include "internal.h"
 
 namespace qjl {
@@ -197,6 +198,83 @@ __device__ __forceinline__ int reduce_scatter4(int x0, int x1, int x2, int x3) {
   return static_cast<int>(c[0] + c[1]);
 }
 
+// ---- the decode step's append (one new token per (batch, kv head)) ----
+// Four waves (256 threads) of the workgroup whose token range ends with the
+// new token encode its key exactly as the encode kernels do: the sign of
+// every coordinate of S^T k, certified (four lanes per coordinate multiply
+// 32 channels each in fp64, a quad sum joins them: at most 34 roundings, so
+// the sum lies within 2^-47 ||k|| max_i ||s_i|| of the exact value and a sum
+// beyond 2^-45 ||k|| max_i ||s_i|| fixes the sign; others go to the exact
+// integer accumulator), sign(0) = +1, an all-zero key gives all ones.  The
+// norm is fp32 of the fp64 root of the fp64 sum of squares.  The bits, the
+// norm and the value row are stored to row `pos` of the caches and the
+// stores are waited for, so that the workgroup's barrier that follows makes
+// them visible to its own tile loads.
+template <int M>
+__device__ void append_token(const AppendArgs& a, int64_t bh, int cap, int atid, float cnmax,
+                             uint32_t* scratch) {
+  constexpr int WPR = M / 32;
+  const int lane = atid & 63;
+  const int aw = atid >> 6;
+  const int sub = lane & 3;
+  const int quad = atid >> 2;
+  const uint16_t* krow = a.key + bh * D;
+  const uint4* kr4 = reinterpret_cast<const uint4*>(krow);
+  uint4 kc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kc[u] = kr4[4 * u + sub];
+  double sq = 0.0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t kw[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const double lo = bf16_lo_f64(kw[t]), hi = bf16_hi_f64(kw[t]);
+      sq += lo * lo;   // squares of bf16 values are exact in fp64
+      sq += hi * hi;
+    }
+  }
+  const double ksq = quad_sum_f64(sq);
+  const double knorm = __builtin_sqrt(ksq);
+  const double thr = 0x1.0p-45 * knorm * static_cast<double>(cnmax);
+  const int64_t row = bh * cap + a.pos;
+  uint16_t* srow_out = reinterpret_cast<uint16_t*>(a.signs + row * WPR);
+#pragma unroll 1
+  for (int r = 0; r < M / 64; ++r) {
+    const int i = 64 * r + quad;   // this quad's coordinate
+    const uint4* srow = reinterpret_cast<const uint4*>(a.s_md + static_cast<int64_t>(i) * D);
+    double acc = 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 sv = srow[4 * u + sub];
+      const uint32_t kw[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+      const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc = __builtin_fma(bf16_lo_f64(kw[t]), bf16_lo_f64(sw[t]), acc);
+        acc = __builtin_fma(bf16_hi_f64(kw[t]), bf16_hi_f64(sw[t]), acc);
+      }
+    }
+    const double sum = quad_sum_f64(acc);
+    bool bit = ksq == 0.0 || sum >= 0.0;   // all-(+/-)zero key: every projection is exactly 0
+    const bool decided = ksq == 0.0 || __builtin_fabs(sum) > thr;
+    for (uint64_t open = __ballot(!decided && sub == 0); open != 0; open &= open - 1) {
+      const int l = __builtin_ctzll(open);   // wave-uniform
+      if (lane == l) bit = exact_sign_long_inl(krow, a.s_md + static_cast<int64_t>(i) * D, scratch + aw * 2 * ACC_WORDS);
+    }
+    // lane 4q holds the bit of coordinate 64 r + 16 aw + q
+    const uint64_t mask = __ballot(bit && sub == 0);
+    uint32_t half = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) half |= static_cast<uint32_t>((mask >> (4 * q)) & 1u) << q;
+    if (lane == 0) srow_out[4 * r + aw] = static_cast<uint16_t>(half);
+  }
+  if (atid == 0) a.norms[row] = static_cast<float>(knorm);
+  if (atid < 16)
+    reinterpret_cast<uint4*>(a.values + row * D)[atid] = reinterpret_cast<const uint4*>(a.val + bh * D)[atid];
+  __builtin_amdgcn_s_waitcnt(0);   // the stores are complete before the barrier
+}
+
 template <int M, int G, int NW>
 struct DecodeLds {
   static constexpr int NT = 64 * NW;
@@ -220,13 +298,15 @@ struct DecodeLds {
   static constexpr int TOTAL = VB_BYTES + LIMB_BYTES + P_BYTES;
 };
 
-template <int M, int G, int NW>
+// APPEND: the step first appends token N - 1 (see append_token); the caches
+// are then written and read in one launch, so their pointers carry no
+// __restrict__.
+template <int M, int G, int NW, bool APPEND>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
-    const float* __restrict__ q, const uint32_t* __restrict__ signs,
-    const float* __restrict__ norms, const uint16_t* __restrict__ values,
+    const float* __restrict__ q, const uint32_t* signs, const float* norms, const uint16_t* values,
     const uint16_t* __restrict__ s_frag, float cnmax, int H_kv, int N, int cap, int n_split,
     int tps, float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
-    float* __restrict__ part_acc, float* __restrict__ part_ml) {
+    float* __restrict__ part_acc, float* __restrict__ part_ml, AppendArgs app) {
   using L = DecodeLds<M, G, NW>;
   constexpr int NT = 64 * NW;
   constexpr int WPR = M / 32;        // sign words per token
@@ -239,6 +319,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ float red_ml[NW][G][2];
   __shared__ int sumq[G];
   __shared__ int is_last;
+  __shared__ uint32_t app_scratch[APPEND ? 4 * 2 * ACC_WORDS : 1];
   uint8_t* vb_all = smem;
   uint8_t* limbs = smem + L::VB_BYTES;
   uint8_t* p_all = smem + L::VB_BYTES + L::LIMB_BYTES;
@@ -309,6 +390,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
   int t0 = t_begin + wave * TILE;
+  // With APPEND, the workgroup whose range ends with the new token appends
+  // it during the prologue; a wave whose first tile holds that token loads
+  // the tile only after the append (behind the prologue's last barrier).
+  const bool app_wg = APPEND && app.pos >= t_begin && app.pos < t_end;
+  const bool defer_first = app_wg && app.pos >= t0 && app.pos < t0 + TILE;
 
   // ---- prologue ----
   // q (straight into the split entries) and the S^T fragments are requested
@@ -400,7 +486,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     load_values(t0, std::integral_constant<int, 0>{});
     if constexpr (M == 256) load_values(t0, std::integral_constant<int, 1>{});
   };
-  if (!kLateTile || wave >= SQW) first_tile();
+  if ((!kLateTile || wave >= SQW) && !defer_first) first_tile();
 
   // quantization step 2^E of head h: 2^(E + 21) exceeds ||q_h|| max_i ||s_i||
   // (with margin for the rounding of S^T q and of the norm itself)
@@ -471,10 +557,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     if (col < G) atomicAdd(&sumq[col], qsum);
-    if constexpr (kLateTile) first_tile();
+    if constexpr (kLateTile) {
+      if (!defer_first) first_tile();
+    }
   }
-  if constexpr (M != 256) load_values(t0, std::integral_constant<int, 1>{});
+  if constexpr (M != 256) {
+    if (!defer_first) load_values(t0, std::integral_constant<int, 1>{});
+  }
+  if constexpr (APPEND) {
+    // the last four waves (idle during S^T q in eight-wave workgroups)
+    if (app_wg && wave >= NW - 4) append_token<M>(app, bh, cap, tid - (NW - 4) * 64, cnmax, app_scratch);
+  }
   __syncthreads();
+  if constexpr (APPEND) {
+    if (defer_first) {
+      load_signs(t0, sw, nv);
+      load_values(t0, std::integral_constant<int, 0>{});
+      load_values(t0, std::integral_constant<int, 1>{});
+    }
+  }
 
   // ---- main loop setup ----
   // Per head: logit (base 2) = (kap[h] * sum_i b_i Q_i + bet[h]) * ||k||,
@@ -893,17 +994,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 template <int M, int G, int NW>
 int launch_decode_mgw(const DeviceSketch& s, const DecodePlan& plan, const float* q,
-                     const uint32_t* signs, const float* norms, const void* values, int B,
-                     int H_kv, int N, int cap, float coef, float* out, void* workspace,
-                     hipStream_t stream) {
+                      const uint32_t* signs, const float* norms, const void* values, int B,
+                      int H_kv, int N, int cap, float coef, float* out, void* workspace,
+                      const AppendArgs* app, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
   float* part_acc = reinterpret_cast<float*>(ws + plan.counter_bytes);
   float* part_ml = part_acc + static_cast<size_t>(B) * H_kv * G * plan.n_split * D;
   dim3 grid(plan.n_split, H_kv, B);
-  hipLaunchKernelGGL((decode_kernel<M, G, NW>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
-                     static_cast<const uint16_t*>(values), s.s_frag, s.col_norm_all, H_kv, N, cap,
-                     plan.n_split, plan.tokens_per_split, coef, out, counters, part_acc, part_ml);
+  const uint16_t* v = static_cast<const uint16_t*>(values);
+  if (app != nullptr) {
+    hipLaunchKernelGGL((decode_kernel<M, G, NW, true>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
+                       v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
+                       coef, out, counters, part_acc, part_ml, *app);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<M, G, NW, false>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
+                       v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
+                       coef, out, counters, part_acc, part_ml, AppendArgs{});
+  }
   return hipGetLastError();
 }
 
@@ -911,22 +1019,22 @@ template <int M, int G>
 int launch_decode_mg(const DeviceSketch& s, const DecodePlan& plan, const float* q,
                      const uint32_t* signs, const float* norms, const void* values, int B,
                      int H_kv, int N, int cap, float coef, float* out, void* workspace,
-                     hipStream_t stream) {
+                     const AppendArgs* app, hipStream_t stream) {
   if (plan.waves == 8)
-    return launch_decode_mgw<M, G, 8>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, stream);
-  return launch_decode_mgw<M, G, 4>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, stream);
+    return launch_decode_mgw<M, G, 8>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, stream);
+  return launch_decode_mgw<M, G, 4>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, stream);
 }
 
 template <int M>
 int launch_decode_m(int G, const DeviceSketch& s, const DecodePlan& plan, const float* q,
                     const uint32_t* signs, const float* norms, const void* values, int B,
                     int H_kv, int N, int cap, float coef, float* out, void* workspace,
-                    hipStream_t st) {
+                    const AppendArgs* app, hipStream_t st) {
   switch (G) {
-    case 1: return launch_decode_mg<M, 1>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
-    case 2: return launch_decode_mg<M, 2>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
-    case 4: return launch_decode_mg<M, 4>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
-    case 8: return launch_decode_mg<M, 8>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+    case 1: return launch_decode_mg<M, 1>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
+    case 2: return launch_decode_mg<M, 2>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
+    case 4: return launch_decode_mg<M, 4>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
+    case 8: return launch_decode_mg<M, 8>(s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -995,15 +1103,15 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
 int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,
                   const uint32_t* signs, const float* norms, const void* values, int B, int H_q,
                   int H_kv, int N, int cap, float scale, float* out, void* workspace,
-                  void* stream) {
+                  const AppendArgs* app, void* stream) {
   const int G = H_q / H_kv;
   // logits are kept in base 2: coef = sqrt(pi/2)/m * scale * log2(e)
   const double c = 1.2533141373155002512 / s.m * static_cast<double>(scale) * 1.4426950408889634074;
   const float coef = static_cast<float>(c);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.m == 256)
-    return launch_decode_m<256>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
-  return launch_decode_m<512>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, st);
+    return launch_decode_m<256>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
+  return launch_decode_m<512>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
 }
 
 }  // namespace qjl

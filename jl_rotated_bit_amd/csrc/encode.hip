@@ -46,6 +46,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "exact_sign.h"
 #include "internal.h"
 
 namespace qjl {
@@ -64,66 +65,16 @@ constexpr int ROW_B = D * 2;         // 256 bytes per key
 constexpr int LDS_ROW = ROW_B + 16;  // padded LDS row: spreads lanes over banks
 constexpr int TILE_LDS = KT * LDS_ROW;
 constexpr int CHUNKS = KT * ROW_B / 16;  // 16-byte chunks per key tile (2048)
-constexpr int ACC_WORDS = 18;        // long accumulator: 576 bits
 constexpr int QCAP = 112;            // deferred-fix queue entries per wave
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
-
-// Adds v (< 2^48) << (32 * w) into a little-endian multiword integer in LDS.
-__device__ void long_add(uint32_t* acc, int w, uint64_t v) {
-  uint64_t carry = v;
-  for (int i = w; i < ACC_WORDS && carry != 0; ++i) {
-    const uint64_t t = static_cast<uint64_t>(acc[i]) + (carry & 0xFFFFFFFFull);
-    acc[i] = static_cast<uint32_t>(t);
-    carry = (carry >> 32) + (t >> 32);
-  }
-}
-
-// Exact sign of sum_c key[c] * s[c] over the 128 channels, from bf16 bits.
-// Serial (one lane); only reached when a tree sum in fp64 cannot decide.
-// Every bf16 value is sig * 2^(E - 134) with sig < 2^8 and 1 <= E <= 254, so
-// each product is an integer sig_k*sig_s < 2^16 times 2^(Ek + Es - 268):
-// it is added, shifted by Ek + Es - 2 bits, into one of two 576-bit
-// magnitudes (positive / negative terms), which are compared at the end.
-__device__ __attribute__((noinline)) bool exact_sign_long(const uint16_t* key_lds, const uint16_t* s_row,
-                                                          uint32_t* scratch) {
-  uint32_t* pos = scratch;
-  uint32_t* neg = scratch + ACC_WORDS;
-  for (int i = 0; i < 2 * ACC_WORDS; ++i) scratch[i] = 0;
-  for (int c = 0; c < D; ++c) {
-    const uint32_t uk = key_lds[c];
-    const uint32_t us = s_row[c];
-    uint32_t ek = (uk >> 7) & 0xFF, es = (us >> 7) & 0xFF;
-    const uint32_t sk = ek ? ((uk & 0x7F) | 0x80) : (uk & 0x7F);
-    const uint32_t ss = es ? ((us & 0x7F) | 0x80) : (us & 0x7F);
-    if (sk == 0 || ss == 0) continue;
-    ek = ek ? (ek > 254 ? 254 : ek) : 1;  // Inf/NaN inputs: undefined but in bounds
-    es = es ? (es > 254 ? 254 : es) : 1;
-    const uint32_t shift = ek + es - 2;   // 0 .. 506
-    const uint64_t v = static_cast<uint64_t>(sk * ss) << (shift & 31);
-    long_add(((uk ^ us) & 0x8000) ? neg : pos, static_cast<int>(shift >> 5), v);
-  }
-  for (int i = ACC_WORDS - 1; i >= 0; --i) {
-    if (pos[i] != neg[i]) return pos[i] > neg[i];
-  }
-  return true;  // exact zero: sign(0) = +1
-}
 
 // DPP move of a float with every lane enabled and no old value (the
 // compiler folds it into the consuming add)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-// Exact bf16 -> fp64 via fp32: a bf16 value is an fp32 value whose low 16
-// bits are zero (normal or subnormal), and fp32 -> fp64 is exact.
-__device__ __forceinline__ double bf16_lo_f64(uint32_t pair) {
-  return static_cast<double>(__uint_as_float(pair << 16));
-}
-__device__ __forceinline__ double bf16_hi_f64(uint32_t pair) {
-  return static_cast<double>(__uint_as_float(pair & 0xFFFF0000u));
 }
 
 // Norm of a key whose fp32 sum of squares under- or overflowed: scale by a
@@ -150,30 +101,6 @@ __device__ float scaled_norm(const uint16_t* key) {
     s = __builtin_fmaf(v, v, s);
   }
   return __builtin_ldexpf(__builtin_sqrtf(s), e);
-}
-
-// fp64 move within a quad of lanes through DPP (each half separately)
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const uint64_t u = __double_as_longlong(x);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), CTRL, 0xF, 0xF, true);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, 0xF, 0xF, true);
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-}
-constexpr int kQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
-constexpr int kQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
-// Sum over a quad of lanes: each step adds a lane's value to its partner's
-// and the partner adds the same two numbers, so all four lanes end with
-// bit-identical totals.
-__device__ __forceinline__ double quad_sum_f64(double x) {
-  x += dpp_f64<kQuadXor1>(x);
-  x += dpp_f64<kQuadXor2>(x);
-  return x;
-}
-__device__ __forceinline__ uint32_t quad_or(uint32_t x) {
-  x |= __builtin_amdgcn_update_dpp(0u, x, kQuadXor1, 0xF, 0xF, true);
-  x |= __builtin_amdgcn_update_dpp(0u, x, kQuadXor2, 0xF, 0xF, true);
-  return x;
 }
 
 // Buffer descriptor over [base, base + bytes): loads past the end return

@@ -59,9 +59,23 @@ int launch_encode(const DeviceSketch& s, const void* keys, int B, int H_kv, int 
 constexpr int kEncodeSmallMaxDefault = 512;
 int set_encode_small_max(int keys);
 
+// The decode step's append: token `pos` (= N - 1) of every (batch, kv head)
+// is encoded from `key` and its value copied from `val` (both bf16
+// [B][H_kv][d]) into row `pos` of the caches, inside the decode launch.
+struct AppendArgs {
+  const uint16_t* key = nullptr;
+  const uint16_t* val = nullptr;
+  const uint16_t* s_md = nullptr;   // S^T [m][d] bf16 bits
+  uint32_t* signs = nullptr;
+  float* norms = nullptr;
+  uint16_t* values = nullptr;
+  int pos = 0;
+};
+
+// app == nullptr: a plain decode step; otherwise the step appends first.
 int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,
                   const uint32_t* signs, const float* norms, const void* values, int B, int H_q,
                   int H_kv, int N, int cap, float scale, float* out, void* workspace,
-                  void* stream);
+                  const AppendArgs* app, void* stream);
 
 }  // namespace qjl

@@ -202,7 +202,8 @@ qjl_status scratch_for_device(hipStream_t stream, void** out) {
 qjl_status decode_common(const char* fn, const float* q, const uint32_t* signs, const float* norms,
                          const void* values_bf16, int32_t B, int32_t H_q, int32_t H_kv, int32_t N,
                          int32_t cap, int32_t d, int32_t m, uint64_t seed, float scale, float* out,
-                         void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+                         void* workspace, size_t workspace_bytes, void* stream, bool noalloc,
+                         const qjl::AppendArgs* append = nullptr) {
   g_last_error.clear();
   if (!supported_dm(d, m))
     return fail(QJL_EUNSUPPORTED, "%s: d=%d m=%d unsupported (d=128, m in {256,512})", fn, d, m);
@@ -240,7 +241,7 @@ qjl_status decode_common(const char* fn, const float* q, const uint32_t* signs, 
     workspace_bytes = kScratchBytes;
     const float sc = scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d))) : scale;
     const int e = qjl::launch_decode(s, plan, q, signs, norms, values_bf16, B, H_q, H_kv, N, cap, sc,
-                                     out, workspace, stream);
+                                     out, workspace, nullptr, stream);
     if (e != hipSuccess)
       return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
     return QJL_OK;
@@ -256,8 +257,13 @@ qjl_status decode_common(const char* fn, const float* q, const uint32_t* signs, 
   qjl_status rc = get_sketch(seed, d, m, &s);
   if (rc != QJL_OK) return rc;
   const float sc = scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d))) : scale;
+  qjl::AppendArgs app;
+  if (append != nullptr) {
+    app = *append;
+    app.s_md = s.s_md;
+  }
   const int e = qjl::launch_decode(s, plan, q, signs, norms, values_bf16, B, H_q, H_kv, N, cap, sc,
-                                   out, workspace, stream);
+                                   out, workspace, append != nullptr ? &app : nullptr, stream);
   if (e != hipSuccess)
     return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
   return QJL_OK;
@@ -343,6 +349,30 @@ QJL_API qjl_status qjl_decode_attention_noalloc(const float* q, const uint32_t* 
                                                 float scale, float* out, void* stream) {
   return decode_common("qjl_decode_attention_noalloc", q, signs, norms, values_bf16, B, H_q, H_kv,
                        N, cap, d, m, seed, scale, out, nullptr, 0, stream, true);
+}
+
+QJL_API qjl_status qjl_decode_step(const float* q, const void* new_keys_bf16,
+                                   const void* new_values_bf16, uint32_t* signs, float* norms,
+                                   void* values_bf16, int32_t B, int32_t H_q, int32_t H_kv,
+                                   int32_t pos, int32_t cap, int32_t d, int32_t m, uint64_t seed,
+                                   float scale, float* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  g_last_error.clear();
+  if (pos < 0 || cap <= 0 || pos >= cap)
+    return fail(QJL_EINVAL, "qjl_decode_step: pos=%d outside [0, cap=%d)", pos, cap);
+  if (new_keys_bf16 == nullptr || new_values_bf16 == nullptr)
+    return fail(QJL_EINVAL, "qjl_decode_step: NULL pointer");
+  if (!aligned(new_keys_bf16, 16) || !aligned(new_values_bf16, 16))
+    return fail(QJL_EINVAL, "qjl_decode_step: misaligned pointer (new keys/values need 16 B)");
+  qjl::AppendArgs app;
+  app.key = static_cast<const uint16_t*>(new_keys_bf16);
+  app.val = static_cast<const uint16_t*>(new_values_bf16);
+  app.signs = signs;
+  app.norms = norms;
+  app.values = static_cast<uint16_t*>(values_bf16);
+  app.pos = pos;
+  return decode_common("qjl_decode_step", q, signs, norms, values_bf16, B, H_q, H_kv, pos + 1, cap,
+                       d, m, seed, scale, out, workspace, workspace_bytes, stream, false, &app);
 }
 
 QJL_API qjl_status qjl_release_cache(void) {

@@ -10,6 +10,7 @@ Names and semantics follow the C entry points:
 * ``sketch_host(seed, d, m)``                 -> qjl_sketch_host
 * ``encode_keys(keys, signs, norms, pos, seed, m)``        -> qjl_encode_keys
 * ``decode_attention(q, signs, norms, values, N, seed, m, scale)`` -> qjl_decode_attention
+* ``decode_step(q, new_keys, new_values, signs, norms, values, pos, seed, m)`` -> qjl_decode_step
 * ``decode_attention_noalloc(q, signs, norms, values, N, seed, m, out)``  -> qjl_decode_attention_noalloc
 * ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache``
 * ``testing_set_encode_small_max`` -> qjl_testing_set_encode_small_max (a
@@ -74,6 +75,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.qjl_decode_attention_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
                                                      c_int, c_int, c_int, c_int, c_u64,
                                                      ctypes.c_float, c_vp, c_vp]
+        lib.qjl_decode_step.restype = c_int
+        lib.qjl_decode_step.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
+                                        c_int, c_int, c_int, c_int, c_u64, ctypes.c_float, c_vp,
+                                        c_vp, c_sz, c_vp]
         lib.qjl_release_cache.restype = c_int
         lib.qjl_release_cache.argtypes = []
         lib.qjl_testing_set_encode_small_max.restype = c_int
@@ -189,6 +194,39 @@ def decode_attention(q, signs, norms, values, N: int, seed: int, m: int, scale: 
         _ptr(q), _ptr(signs), _ptr(norms), _ptr(values), B, H_q, H_kv, N, cap, d, m,
         seed & (2 ** 64 - 1), 0.0 if scale is None else float(scale), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), s.cuda_stream))
+    return out
+
+
+def decode_step(q, new_keys, new_values, signs, norms, values, pos: int, seed: int, m: int,
+                scale: float | None = None, out=None, workspace=None, stream=None):
+    """qjl_decode_step: appends token ``pos`` (new_keys / new_values, bf16
+    [B][H_kv][d]) to the caches (sign bits + norm, value row) and decodes
+    over tokens [0, pos] in one launch; returns out fp32 [B][H_q][d]."""
+    import torch
+    B, H_q, d = q.shape
+    _, H_kv, cap, _ = values.shape
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp32 [B][H_q][d]")
+    for name, t in (("new_keys", new_keys), ("new_values", new_values)):
+        if tuple(t.shape) != (B, H_kv, d) or t.element_size() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous 16-bit (bf16 bits) [B][H_kv][d]")
+    if values.element_size() != 2 or not values.is_contiguous():
+        raise ValueError("values must be contiguous 16-bit (bf16 bits) [B][H_kv][cap][d]")
+    if tuple(signs.shape) != (B, H_kv, cap, m // 32) or tuple(norms.shape) != (B, H_kv, cap):
+        raise ValueError("signs/norms shapes do not match values")
+    if not signs.is_contiguous() or not norms.is_contiguous():
+        raise ValueError("signs and norms must be contiguous")
+    s = _resolve_stream(stream)
+    if out is None:
+        with torch.cuda.stream(s):
+            out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H_q, H_kv, pos + 1, d, m)
+    if workspace is None:
+        workspace = workspace_for(need, q.device, s)
+    _check(load().qjl_decode_step(
+        _ptr(q), _ptr(new_keys), _ptr(new_values), _ptr(signs), _ptr(norms), _ptr(values),
+        B, H_q, H_kv, pos, cap, d, m, seed & (2 ** 64 - 1), 0.0 if scale is None else float(scale),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), s.cuda_stream))
     return out
 
 

@@ -195,6 +195,30 @@ def test_decode_noalloc_validation(lib):
         assert lib.qjl_decode_workspace_bytes(B, Hq, Hkv, N, 128, m) <= qjl.NOALLOC_SCRATCH_BYTES
 
 
+def step(lib, q=A16, nk=A16, nv=A16, signs=A16, norms=A16, values=A16, B=1, Hq=4, Hkv=1, pos=7,
+         cap=8, d=128, m=256, scale=0.0, out=A16, ws=A16, ws_bytes=1 << 30):
+    return lib.qjl_decode_step(q, nk, nv, signs, norms, values, B, Hq, Hkv, pos, cap, d, m, 1,
+                               ctypes.c_float(scale), out, ws, ws_bytes, None)
+
+
+def test_decode_step_validation(lib):
+    assert step(lib, pos=-1) == EINVAL
+    assert step(lib, pos=8, cap=8) == EINVAL
+    assert "outside" in qjl.last_error()
+    assert step(lib, nk=None) == EINVAL
+    assert step(lib, nv=None) == EINVAL
+    assert step(lib, nk=A16 + 8) == EINVAL
+    assert step(lib, nv=A16 + 2) == EINVAL
+    assert step(lib, d=64) == EUNSUP
+    assert step(lib, Hq=6, Hkv=2) == EUNSUP
+    for name in ("q", "signs", "norms", "values", "out"):
+        assert step(lib, **{name: None}) == EINVAL
+    big = dict(B=1, Hq=32, Hkv=8, pos=32767, cap=32768)
+    need = lib.qjl_decode_workspace_bytes(1, 32, 8, 32768, 128, 256)
+    assert step(lib, ws=None, **big) == EWS
+    assert step(lib, ws_bytes=need - 1, **big) == EWS
+
+
 def test_decode_plan_properties(lib):
     for B, Hq, Hkv, N, m in [(1, 8, 1, 4096, 256), (1, 32, 8, 32768, 256), (1, 32, 8, 65600, 512),
                              (8, 40, 40, 16384, 256), (1, 4, 4, 1, 256), (2, 16, 2, 777, 512),
