@@ -68,7 +68,8 @@ def sha256_of(paths):
 
 def kernel_sources(kind):
     csrc = os.path.join(ROOT, "jl_rotated_bit_amd", "csrc")
-    return [os.path.join(csrc, f"{kind}.hip"), os.path.join(csrc, "internal.h")]
+    return [os.path.join(csrc, f"{kind}.hip"), os.path.join(csrc, "internal.h"),
+            os.path.join(csrc, "exact_sign.h")]
 
 
 def measured_traffic(kind, workload):
@@ -99,6 +100,11 @@ def decode_bytes(B, Hq, Hkv, N, d, m):
     """Algorithmic bytes of one decode call: per (token, kv head) m/8 bytes of
     sign words, a 4-byte norm and 2d bytes of bf16 values; q and out."""
     return B * Hkv * N * (m // 8 + 4 + 2 * d) + B * Hq * d * 4 * 2
+
+
+def baseline_bytes(B, Hq, Hkv, N, d):
+    """Algorithmic bytes of the uncompressed baseline: bf16 keys and values."""
+    return B * Hkv * N * 4 * d + B * Hq * d * 4 * 2
 
 
 def encode_bytes_per_key(d, m):
@@ -259,6 +265,18 @@ def bench_gqa32k(qjl, w, args, T):
     fused_ms = T.b2b(fused_step, args.steps)
     log(f"[bench] gqa32k fused step (append inside the decode launch): {fused_ms * 1e3:.2f} us")
 
+    # The uncompressed baseline at the same context: exact attention over the
+    # bf16 keys and values (2 x 256 bytes per token and kv head), same ring.
+    bbytes = baseline_bytes(B, Hq, Hkv, N, d)
+    nb = ring_sets(bbytes)
+
+    def base(i):
+        s = sets[i % min(nb, n_sets)]
+        qjl.baseline_decode_attention_bf16(s["q"], s["keys"], s["values"], N, out=s["out"], workspace=ws)
+    base(0)
+    base_ms = T.b2b(base, args.steps)
+    log(f"[bench] gqa32k bf16-KV baseline decode: {base_ms * 1e3:.2f} us")
+
     if args.copy_calibration:
         a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
@@ -282,6 +300,9 @@ def bench_gqa32k(qjl, w, args, T):
         "append_step_us": round(append_ms * 1e3, 3),
         "append_step_frac_of_hbm_peak": round(dbytes / (append_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "fused_step_us": round(fused_ms * 1e3, 3),
+        "baseline_bf16_decode_us": round(base_ms * 1e3, 3),
+        "baseline_bf16_frac_of_hbm_peak": round(bbytes / (base_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "speedup_vs_bf16_kv": round(base_ms / b2b_dec_ms, 3),
         "fused_step_frac_of_hbm_peak": round(dbytes / (fused_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "encode_keys_per_s": round(n_keys / enc_s, 1),
         "encode_us": round(enc_s * 1e6, 3),
@@ -456,8 +477,6 @@ def bench_mha16k(qjl, w, args, T):
     for _ in range(2):
         qjl.encode_keys(keys_d, signs, norms, 0, SEED, m)
     enc_ms = T.b2b(lambda i: qjl.encode_keys(keys_d, signs, norms, 0, SEED, m), enc_reps)
-    del keys_d
-    torch.cuda.empty_cache()
     sets = [dict(values=dev(w.values), signs=signs if k == 0 else signs.clone(),
                  norms=norms if k == 0 else norms.clone(), q=dev(w.q),
                  out=torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")) for k in range(n_sets)]
@@ -470,14 +489,25 @@ def bench_mha16k(qjl, w, args, T):
         dec(i)
     dec_ms = T.b2b(dec, args.steps)
     gbs = dbytes / (dec_ms / 1e3) / 1e9
-    log(f"[bench] mha16k: decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s), encode {enc_ms * 1e3:.2f} us")
-    del sets, ws, signs, norms
+    # the uncompressed baseline over the same bf16 keys and values (2.7 GB)
+    bbytes = baseline_bytes(B, Hq, Hkv, N, d)
+    s0 = sets[0]
+    base = lambda i: qjl.baseline_decode_attention_bf16(s0["q"], keys_d, s0["values"], N, out=s0["out"],
+                                                        workspace=ws)
+    base(0)
+    base_ms = T.b2b(base, max(2, args.steps // 2))
+    log(f"[bench] mha16k: decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s), encode {enc_ms * 1e3:.2f} us, "
+        f"bf16-KV baseline {base_ms * 1e3:.2f} us")
+    del sets, ws, signs, norms, keys_d
     torch.cuda.empty_cache()
     return {"workload": DESCRIPTIONS["mha16k"], "decode_us": round(dec_ms * 1e3, 3),
             "decode_gbs": round(gbs, 2), "decode_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "roofline": roofline(gbs, measured_traffic("decode", "mha16k"), "decode_kernel", dbytes),
             "encode_us": round(enc_ms * 1e3, 3), "encode_keys_per_s": round(n_keys / (enc_ms / 1e3), 1),
             "encode_hbm_frac": round(ebytes / (enc_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "baseline_bf16_decode_us": round(base_ms * 1e3, 3),
+            "baseline_bf16_frac_of_hbm_peak": round(bbytes / (base_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "speedup_vs_bf16_kv": round(base_ms / dec_ms, 3),
             "ring_sets": n_sets}
 
 

@@ -176,6 +176,28 @@ QJL_API qjl_status qjl_decode_step(const float *q, const void *new_keys_bf16,
                                    float scale, float *out, void *workspace, size_t workspace_bytes,
                                    void *stream);
 
+/* The uncompressed baseline on the same kernel skeleton: exact scaled
+ * dot-product attention over bf16 keys and values, so that the decode's
+ * speed-up from 1-bit keys can be measured at equal context (the QJL page
+ * claims a faster runtime than full-precision keys: "QJL: 1-Bit Quantized
+ * JL Transform ...", Abstract).  Not part of the QJL method.
+ *   out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t over t in [0, N)
+ * of kv head h / (H_q / H_kv).  q is split into three bf16 parts (their sum
+ * is fp32 q to 2^-24), the products run on the bf16 matrix cores with fp32
+ * accumulation; softmax, the weighted sum and the split merge are those of
+ * qjl_decode_attention (same plan and workspace size:
+ * qjl_decode_workspace_bytes(B, H_q, H_kv, N, d, 256)).
+ *   q           fp32 [B][H_q][d], 16-byte aligned.
+ *   keys_bf16   bf16 [B][H_kv][cap][d], values_bf16 likewise; 16-byte aligned.
+ *   d == 128; G = H_q / H_kv in {1, 2, 4, 8}; 1 <= N <= cap; scale as for
+ *   qjl_decode_attention; out fp32 [B][H_q][d]; workspace as for it.
+ * Returns QJL_OK, QJL_EINVAL, QJL_EUNSUPPORTED, QJL_EWORKSPACE or QJL_EHIP. */
+QJL_API qjl_status qjl_baseline_decode_attention_bf16(const float *q, const void *keys_bf16,
+                                                      const void *values_bf16, int32_t B, int32_t H_q,
+                                                      int32_t H_kv, int32_t N, int32_t cap, int32_t d,
+                                                      float scale, float *out, void *workspace,
+                                                      size_t workspace_bytes, void *stream);
+
 /* Bytes of device scratch the library holds per GPU for
  * qjl_decode_attention_noalloc: the 4096-byte counter region plus 4 MiB of
  * split partials. */

@@ -275,6 +275,15 @@ __device__ void append_token(const AppendArgs& a, int64_t bh, int cap, int atid,
   __builtin_amdgcn_s_waitcnt(0);   // the stores are complete before the barrier
 }
 
+__device__ __forceinline__ float reduce_scatter4f(float x0, float x1, float x2, float x3) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x2), __float_as_uint(x3), false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(__uint_as_float(a[0]) + __uint_as_float(a[1])),
+                                                  __float_as_uint(__uint_as_float(b[0]) + __uint_as_float(b[1])),
+                                                  false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 template <int M, int G, int NW>
 struct DecodeLds {
   static constexpr int NT = 64 * NW;
@@ -301,12 +310,20 @@ struct DecodeLds {
 // APPEND: the step first appends token N - 1 (see append_token); the caches
 // are then written and read in one launch, so their pointers carry no
 // __restrict__.
-template <int M, int G, int NW, bool APPEND>
+// BF16K: the uncompressed baseline.  Scores are the exact q . k over bf16
+// keys `kbf` ([B][H_kv][cap][d]) on the bf16 matrix cores (q split into three
+// bf16 parts, the A operand; the key rows, loaded straight into registers in
+// operand order, the B operand), logit = scale * q . k; the sign words, norms
+// and S^T q are not used.  Softmax, P.V and the split merge are shared.
+template <int M, int G, int NW, bool APPEND, bool BF16K = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     const float* __restrict__ q, const uint32_t* signs, const float* norms, const uint16_t* values,
     const uint16_t* __restrict__ s_frag, float cnmax, int H_kv, int N, int cap, int n_split,
     int tps, float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
-    float* __restrict__ part_acc, float* __restrict__ part_ml, AppendArgs app) {
+    float* __restrict__ part_acc, float* __restrict__ part_ml, AppendArgs app,
+    const uint16_t* kbf) {
+  static_assert(!(APPEND && BF16K), "the baseline kernel has no append");
+  static_assert(!BF16K || M == 256, "the baseline kernel reuses the m = 256 LDS layout (256-byte q rows)");
   using L = DecodeLds<M, G, NW>;
   constexpr int NT = 64 * NW;
   constexpr int WPR = M / 32;        // sign words per token
@@ -347,6 +364,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   uint4 vc[VCH];
   uint32_t sw[4][CW];
   float nv = 0.f;
+  uint4 kc[BF16K ? 16 : 1];   // BF16K: key chunks of the current tile
+  const uint16_t* k_base = BF16K ? kbf + bh * cap * D : nullptr;
   // Tile loads go through buffer descriptors that start at the tile and end
   // at the split's end: rows past the end read as zero (their logits are
   // masked to -inf), with no per-lane clamping or 64-bit address arithmetic,
@@ -378,6 +397,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, 0, kStream));
   };
+  // BF16K key chunk 4 j + ks: token 16 j + l16 of the tile, channels
+  // 32 ks + 8 grp .. +7 (the B operand of v_mfma_f32_16x16x32_bf16 for
+  // token block j and channel step ks)
+  auto load_keys = [&](int t0_) {
+    const rsrc_t rk = make_rsrc(k_base + static_cast<int64_t>(t0_) * D, tile_rows(t0_) * D * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rk, (16 * j + l16) * D * 2 + 64 * ks + 16 * grp, 0, kStream);
+        kc[4 * j + ks] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+  };
   // value chunk c of a tile: token t0 + 4c + lane/16, channels 8*(lane%16) .. +7
   const int vo_lane = grp * D * 2 + l16 * 16;
   auto load_values = [&](int t0_, auto half_const) {
@@ -396,6 +428,40 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bool app_wg = APPEND && app.pos >= t_begin && app.pos < t_end;
   const bool defer_first = app_wg && app.pos >= t0 && app.pos < t0 + TILE;
 
+  int e_all[G] = {};
+  if constexpr (BF16K) {
+    // ---- prologue (baseline) ----
+    // rows >= 3G of the q operand and the probability rows stay zero
+    constexpr int ZERO_U4 = (16 * L::NSQ - 3 * G) * L::LROW / 16;
+    for (int i = tid; i < ZERO_U4; i += NT)
+      reinterpret_cast<uint4*>(limbs + 3 * G * L::LROW)[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < L::P_BYTES / 16; i += NT) reinterpret_cast<uint4*>(p_all)[i] = make_uint4(0, 0, 0, 0);
+    load_keys(t0);
+    load_values(t0, std::integral_constant<int, 0>{});
+    load_values(t0, std::integral_constant<int, 1>{});
+    // q -> three bf16 parts (hi + mid + lo equals fp32 q to within 2^-24
+    // relative): row part * G + head, 256 bytes per row
+    const float* qb = q + bh * G * D;
+    for (int e = tid; e < G * (D / 8); e += NT) {
+      const int h = e / (D / 8), c8 = e % (D / 8);
+      const float4* src = reinterpret_cast<const float4*>(qb + h * D + 8 * c8);
+      const float4 a0 = src[0], a1 = src[1];
+      const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float x0 = x[2 * u], x1 = x[2 * u + 1];
+        hi[u] = cvt2_bf16(x0, x1);
+        const float r0 = x0 - __uint_as_float(hi[u] << 16), r1 = x1 - __uint_as_float(hi[u] & 0xFFFF0000u);
+        mid[u] = cvt2_bf16(r0, r1);
+        lo[u] = cvt2_bf16(r0 - __uint_as_float(mid[u] << 16), r1 - __uint_as_float(mid[u] & 0xFFFF0000u));
+      }
+      *reinterpret_cast<uint4*>(limbs + h * L::LROW + 16 * c8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(limbs + (G + h) * L::LROW + 16 * c8) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
+      *reinterpret_cast<uint4*>(limbs + (2 * G + h) * L::LROW + 16 * c8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    __syncthreads();
+  } else {
   // ---- prologue ----
   // q (straight into the split entries) and the S^T fragments are requested
   // first; the first tile is requested once q is split (or, in the S^T q
@@ -503,7 +569,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // Exponents of all heads, and of the head of this lane's S^T q columns
   // (col % G); taken here because the q^2 sums share LDS with the value tiles.
-  int e_all[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) e_all[h] = __builtin_amdgcn_readfirstlane(head_exp(h));
   const int e_h = head_exp(col % G);
@@ -577,6 +642,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   }
 
+  }
+
   // ---- main loop setup ----
   // Per head: logit (base 2) = (kap[h] * sum_i b_i Q_i + bet[h]) * ||k||,
   // kap = 2 coef 2^E, bet = -coef 2^E sum_i Q_i.
@@ -591,7 +658,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // (M/4) grp + 16 ks .. +15
   const uint8_t* brow[NSQ];
 #pragma unroll
-  for (int cb = 0; cb < NSQ; ++cb) brow[cb] = limbs + (16 * cb + l16) * L::LROW + (M / 4) * grp;
+  for (int cb = 0; cb < NSQ; ++cb)
+    brow[cb] = limbs + (16 * cb + l16) * L::LROW + (BF16K ? 16 * grp : (M / 4) * grp);
   // Score accumulator of block j: lane (grp, l16), register r holds limb row
   // 16 cb + 4 grp + r (limb p = row / G, head row % G) for token 16 j + l16.
   // Rows are weighted 2^16, 2^8, 1 by limb, then summed over the lane
@@ -626,77 +694,135 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int t_next = t0 + NW * TILE;
     uint32_t swn[4][CW];
     float nvn = 0.f;
-    if constexpr (PF) load_signs(t_next, swn, nvn);
-
-    // scores: block j, limb-row set cb (A = limbs, B = token bits)
-    i32x4_t sacc[NSQ][4];
+    if constexpr (PF && !BF16K) load_signs(t_next, swn, nvn);
+    float logit[G];
+    if constexpr (BF16K) {
+      // scores: block j, q-row set cb (A = q parts, B = key rows)
+      f32x4_t fsacc[NSQ][4];
 #pragma unroll
-    for (int cb = 0; cb < NSQ; ++cb)
+      for (int cb = 0; cb < NSQ; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sacc[cb][j] = i32x4_t{0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) fsacc[cb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      i32x4_t lop[NSQ];
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8_t lop[NSQ];
 #pragma unroll
-      for (int cb = 0; cb < NSQ; ++cb) lop[cb] = *reinterpret_cast<const i32x4_t*>(brow[cb] + 16 * ks);
+        for (int cb = 0; cb < NSQ; ++cb) lop[cb] = *reinterpret_cast<const bf16x8_t*>(brow[cb] + 64 * ks);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = sw[j][ks >> 1];
-        // register qd, byte b: bit 8 b + 4 (ks % 2) + qd of the word (the
-        // limbs were stored in this order)
-        i32x4_t bits;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) bits[qd] = static_cast<int>((w >> (4 * (ks & 1) + qd)) & 0x01010101u);
-#pragma unroll
-        for (int cb = 0; cb < NSQ; ++cb)
-          sacc[cb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lop[cb], bits, sacc[cb][j], 0, 0, 0);
+          for (int cb = 0; cb < NSQ; ++cb)
+            fsacc[cb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                lop[cb], __builtin_bit_cast(bf16x8_t, kc[4 * j + ks]), fsacc[cb][j], 0, 0, 0);
       }
-    }
-    // sum_i b_i Q_i of token t0 + lane, per head
-    int tot[G];
-    auto u = [](int x) { return static_cast<uint32_t>(x); };
-    if constexpr (G == 1) {
-      int x[4];
+      if constexpr (PF) load_keys(t_next);   // the next tile's keys reuse kc
+      // q . k of token t0 + lane per head: the three part rows summed, with
+      // the same reduce-scatter as the integer scores (weights 1)
+      if constexpr (G == 1) {
+        float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[j] = static_cast<int>((u(sacc[0][j][0]) << 16) + (u(sacc[0][j][1]) << 8) + u(sacc[0][j][2]));
-      tot[0] = reduce_scatter4(x[0], x[1], x[2], x[3]);
-    } else if constexpr (G == 2) {
+        for (int j = 0; j < 4; ++j) x[j] = fsacc[0][j][0] + fsacc[0][j][1] + fsacc[0][j][2];
+        logit[0] = reduce_scatter4f(x[0], x[1], x[2], x[3]);
+      } else if constexpr (G == 2) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 2; ++h) {
+          float x[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = fsacc[0][j][h] + fsacc[0][j][2 + h];
+          logit[h] = reduce_scatter4f(x[0], x[1], x[2], x[3]);
+        }
+      } else if constexpr (G == 4) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          logit[h] = reduce_scatter4f(fsacc[0][0][h], fsacc[0][1][h], fsacc[0][2][h], fsacc[0][3][h]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t z[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) z[j] = __float_as_uint(fsacc[0][j][r] + fsacc[1][j][r]);
+          const auto a01 = __builtin_amdgcn_permlane32_swap(z[0], z[1], false, false);
+          const auto a23 = __builtin_amdgcn_permlane32_swap(z[2], z[3], false, false);
+          const auto c = __builtin_amdgcn_permlane32_swap(
+              __float_as_uint(__uint_as_float(a01[0]) + __uint_as_float(a01[1])),
+              __float_as_uint(__uint_as_float(a23[0]) + __uint_as_float(a23[1])), false, false);
+          const auto dd = __builtin_amdgcn_permlane16_swap(c[0], c[1], false, false);
+          logit[r] = __uint_as_float(dd[0]);
+          logit[4 + r] = __uint_as_float(dd[1]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) logit[h] *= coef;
+    } else {
+      // scores: block j, limb-row set cb (A = limbs, B = token bits)
+      i32x4_t sacc[NSQ][4];
+#pragma unroll
+      for (int cb = 0; cb < NSQ; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[cb][j] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        i32x4_t lop[NSQ];
+#pragma unroll
+        for (int cb = 0; cb < NSQ; ++cb) lop[cb] = *reinterpret_cast<const i32x4_t*>(brow[cb] + 16 * ks);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = sw[j][ks >> 1];
+          // register qd, byte b: bit 8 b + 4 (ks % 2) + qd of the word (the
+          // limbs were stored in this order)
+          i32x4_t bits;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) bits[qd] = static_cast<int>((w >> (4 * (ks & 1) + qd)) & 0x01010101u);
+#pragma unroll
+          for (int cb = 0; cb < NSQ; ++cb)
+            sacc[cb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lop[cb], bits, sacc[cb][j], 0, 0, 0);
+        }
+      }
+      // sum_i b_i Q_i of token t0 + lane, per head
+      int tot[G];
+      auto u = [](int x) { return static_cast<uint32_t>(x); };
+      if constexpr (G == 1) {
         int x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          x[j] = static_cast<int>((u(sacc[0][j][h]) << sh_g2) + (u(sacc[0][j][2 + h]) << 8));
-        tot[h] = reduce_scatter4(x[0], x[1], x[2], x[3]);
+          x[j] = static_cast<int>((u(sacc[0][j][0]) << 16) + (u(sacc[0][j][1]) << 8) + u(sacc[0][j][2]));
+        tot[0] = reduce_scatter4(x[0], x[1], x[2], x[3]);
+      } else if constexpr (G == 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int x[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            x[j] = static_cast<int>((u(sacc[0][j][h]) << sh_g2) + (u(sacc[0][j][2 + h]) << 8));
+          tot[h] = reduce_scatter4(x[0], x[1], x[2], x[3]);
+        }
+      } else if constexpr (G == 4) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          tot[h] = reduce_scatter4(static_cast<int>(u(sacc[0][0][h]) << sh_grp), static_cast<int>(u(sacc[0][1][h]) << sh_grp),
+                                   static_cast<int>(u(sacc[0][2][h]) << sh_grp), static_cast<int>(u(sacc[0][3][h]) << sh_grp));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int z[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) z[j] = static_cast<int>((u(sacc[0][j][r]) << sh_g8) + u(sacc[1][j][r]));
+          const auto a01 = __builtin_amdgcn_permlane32_swap(z[0], z[1], false, false);
+          const auto a23 = __builtin_amdgcn_permlane32_swap(z[2], z[3], false, false);
+          const auto c = __builtin_amdgcn_permlane32_swap(a01[0] + a01[1], a23[0] + a23[1], false, false);
+          const auto d = __builtin_amdgcn_permlane16_swap(c[0], c[1], false, false);
+          tot[r] = static_cast<int>(d[0]);
+          tot[4 + r] = static_cast<int>(d[1]);
+        }
       }
-    } else if constexpr (G == 4) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        tot[h] = reduce_scatter4(static_cast<int>(u(sacc[0][0][h]) << sh_grp), static_cast<int>(u(sacc[0][1][h]) << sh_grp),
-                                 static_cast<int>(u(sacc[0][2][h]) << sh_grp), static_cast<int>(u(sacc[0][3][h]) << sh_grp));
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int z[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) z[j] = static_cast<int>((u(sacc[0][j][r]) << sh_g8) + u(sacc[1][j][r]));
-        const auto a01 = __builtin_amdgcn_permlane32_swap(z[0], z[1], false, false);
-        const auto a23 = __builtin_amdgcn_permlane32_swap(z[2], z[3], false, false);
-        const auto c = __builtin_amdgcn_permlane32_swap(a01[0] + a01[1], a23[0] + a23[1], false, false);
-        const auto d = __builtin_amdgcn_permlane16_swap(c[0], c[1], false, false);
-        tot[r] = static_cast<int>(d[0]);
-        tot[4 + r] = static_cast<int>(d[1]);
-      }
+      for (int h = 0; h < G; ++h) logit[h] = __builtin_fmaf(static_cast<float>(tot[h]), kap[h], bet[h]) * nv;
     }
     // online softmax per head (maxima and rescale factors are wave-uniform)
     const bool live = PF || (t0 + lane < t_end);
     float p[G], al[G], tmax[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float v = __builtin_fmaf(static_cast<float>(tot[h]), kap[h], bet[h]) * nv;
-      p[h] = live ? v : -INFINITY;   // logit
-    }
+    for (int h = 0; h < G; ++h) p[h] = live ? logit[h] : -INFINITY;
     if constexpr (G == 1) {
       tmax[0] = wave_max(p[0]);
     } else {
@@ -791,11 +917,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     if constexpr (PF) {
       t0 = t_next;
+      if constexpr (!BF16K) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int w = 0; w < CW; ++w) sw[j][w] = swn[j][w];
-      nv = nvn;
+          for (int w = 0; w < CW; ++w) sw[j][w] = swn[j][w];
+        nv = nvn;
+      }
     }
   };
   if (t0 < t_end) {
@@ -992,6 +1120,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (tid == 0) __hip_atomic_store(&counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int G, int NW>
+int launch_decode_bf16_gw(const DecodePlan& plan, const float* q, const void* keys, const void* values,
+                          int B, int H_kv, int N, int cap, float coef, float* out, void* workspace,
+                          hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+  float* part_acc = reinterpret_cast<float*>(ws + plan.counter_bytes);
+  float* part_ml = part_acc + static_cast<size_t>(B) * H_kv * G * plan.n_split * D;
+  dim3 grid(plan.n_split, H_kv, B);
+  hipLaunchKernelGGL((decode_kernel<256, G, NW, false, true>), grid, dim3(64 * NW), 0, stream, q,
+                     nullptr, nullptr, static_cast<const uint16_t*>(values), nullptr, 0.f, H_kv, N, cap,
+                     plan.n_split, plan.tokens_per_split, coef, out, counters, part_acc, part_ml,
+                     AppendArgs{}, static_cast<const uint16_t*>(keys));
+  return hipGetLastError();
+}
+
+template <int G>
+int launch_decode_bf16_g(const DecodePlan& plan, const float* q, const void* keys, const void* values,
+                         int B, int H_kv, int N, int cap, float coef, float* out, void* workspace,
+                         hipStream_t stream) {
+  if (plan.waves == 8)
+    return launch_decode_bf16_gw<G, 8>(plan, q, keys, values, B, H_kv, N, cap, coef, out, workspace, stream);
+  return launch_decode_bf16_gw<G, 4>(plan, q, keys, values, B, H_kv, N, cap, coef, out, workspace, stream);
+}
+
 template <int M, int G, int NW>
 int launch_decode_mgw(const DeviceSketch& s, const DecodePlan& plan, const float* q,
                       const uint32_t* signs, const float* norms, const void* values, int B,
@@ -1006,11 +1159,11 @@ int launch_decode_mgw(const DeviceSketch& s, const DecodePlan& plan, const float
   if (app != nullptr) {
     hipLaunchKernelGGL((decode_kernel<M, G, NW, true>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
                        v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
-                       coef, out, counters, part_acc, part_ml, *app);
+                       coef, out, counters, part_acc, part_ml, *app, nullptr);
   } else {
     hipLaunchKernelGGL((decode_kernel<M, G, NW, false>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
                        v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
-                       coef, out, counters, part_acc, part_ml, AppendArgs{});
+                       coef, out, counters, part_acc, part_ml, AppendArgs{}, nullptr);
   }
   return hipGetLastError();
 }
@@ -1112,6 +1265,22 @@ int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,
   if (s.m == 256)
     return launch_decode_m<256>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
   return launch_decode_m<512>(G, s, plan, q, signs, norms, values, B, H_kv, N, cap, coef, out, workspace, app, st);
+}
+
+int launch_decode_bf16(const DecodePlan& plan, const float* q, const void* keys, const void* values,
+                       int B, int H_q, int H_kv, int N, int cap, float scale, float* out,
+                       void* workspace, void* stream) {
+  const int G = H_q / H_kv;
+  // logits in base 2: scale * log2(e) * q . k
+  const float coef = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (G) {
+    case 1: return launch_decode_bf16_g<1>(plan, q, keys, values, B, H_kv, N, cap, coef, out, workspace, st);
+    case 2: return launch_decode_bf16_g<2>(plan, q, keys, values, B, H_kv, N, cap, coef, out, workspace, st);
+    case 4: return launch_decode_bf16_g<4>(plan, q, keys, values, B, H_kv, N, cap, coef, out, workspace, st);
+    case 8: return launch_decode_bf16_g<8>(plan, q, keys, values, B, H_kv, N, cap, coef, out, workspace, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qjl

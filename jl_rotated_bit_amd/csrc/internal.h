@@ -78,4 +78,10 @@ int launch_decode(const DeviceSketch& s, const DecodePlan& plan, const float* q,
                   int H_kv, int N, int cap, float scale, float* out, void* workspace,
                   const AppendArgs* app, void* stream);
 
+// The uncompressed baseline: exact softmax attention over bf16 keys and
+// values with the same split plan, softmax, P.V and merge as the decode.
+int launch_decode_bf16(const DecodePlan& plan, const float* q, const void* keys, const void* values,
+                       int B, int H_q, int H_kv, int N, int cap, float scale, float* out,
+                       void* workspace, void* stream);
+
 }  // namespace qjl

@@ -375,6 +375,43 @@ QJL_API qjl_status qjl_decode_step(const float* q, const void* new_keys_bf16,
                        d, m, seed, scale, out, workspace, workspace_bytes, stream, false, &app);
 }
 
+QJL_API qjl_status qjl_baseline_decode_attention_bf16(const float* q, const void* keys_bf16,
+                                                      const void* values_bf16, int32_t B, int32_t H_q,
+                                                      int32_t H_kv, int32_t N, int32_t cap, int32_t d,
+                                                      float scale, float* out, void* workspace,
+                                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "qjl_baseline_decode_attention_bf16";
+  g_last_error.clear();
+  if (d != qjl::kHeadDim) return fail(QJL_EUNSUPPORTED, "%s: d=%d unsupported (d=128)", fn, d);
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || cap <= 0 || N <= 0 || N > cap)
+    return fail(QJL_EINVAL, "%s: bad sizes B=%d H_q=%d H_kv=%d N=%d cap=%d", fn, B, H_q, H_kv, N, cap);
+  if (H_q % H_kv != 0)
+    return fail(QJL_EINVAL, "%s: H_q=%d is not a multiple of H_kv=%d", fn, H_q, H_kv);
+  const int G = H_q / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(QJL_EUNSUPPORTED, "%s: G=H_q/H_kv=%d unsupported (1, 2, 4, 8)", fn, G);
+  if (static_cast<int64_t>(B) * H_kv * cap > (int64_t{1} << 40)) return fail(QJL_EINVAL, "%s: cache too large", fn);
+  if (!(scale >= 0.0f) || std::isinf(scale)) return fail(QJL_EINVAL, "%s: scale must be finite and >= 0", fn);
+  if (q == nullptr || keys_bf16 == nullptr || values_bf16 == nullptr || out == nullptr)
+    return fail(QJL_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned(q, 16) || !aligned(keys_bf16, 16) || !aligned(values_bf16, 16) || !aligned(out, 16))
+    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+  qjl::DecodePlan plan;
+  if (!qjl::make_decode_plan(B, H_q, H_kv, N, d, 256, &plan)) return fail(QJL_EINVAL, "%s: no plan", fn);
+  if (plan.n_split > 1) {
+    if (workspace == nullptr || !aligned(workspace, 256))
+      return fail(QJL_EWORKSPACE, "%s: workspace NULL or not 256-byte aligned", fn);
+    if (workspace_bytes < plan.total_bytes)
+      return fail(QJL_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, plan.total_bytes);
+  }
+  const float sc = scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(d))) : scale;
+  const int e = qjl::launch_decode_bf16(plan, q, keys_bf16, values_bf16, B, H_q, H_kv, N, cap, sc, out,
+                                        workspace, stream);
+  if (e != hipSuccess)
+    return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
+  return QJL_OK;
+}
+
 QJL_API qjl_status qjl_release_cache(void) {
   g_last_error.clear();
   std::lock_guard<std::mutex> lock(g_cache_mu);

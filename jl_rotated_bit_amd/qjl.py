@@ -12,6 +12,7 @@ Names and semantics follow the C entry points:
 * ``decode_attention(q, signs, norms, values, N, seed, m, scale)`` -> qjl_decode_attention
 * ``decode_step(q, new_keys, new_values, signs, norms, values, pos, seed, m)`` -> qjl_decode_step
 * ``decode_attention_noalloc(q, signs, norms, values, N, seed, m, out)``  -> qjl_decode_attention_noalloc
+* ``baseline_decode_attention_bf16(q, keys, values, N)`` -> qjl_baseline_decode_attention_bf16
 * ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache``
 * ``testing_set_encode_small_max`` -> qjl_testing_set_encode_small_max (a
   per-thread test hook, not part of the public header)
@@ -79,6 +80,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.qjl_decode_step.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
                                         c_int, c_int, c_int, c_int, c_u64, ctypes.c_float, c_vp,
                                         c_vp, c_sz, c_vp]
+        lib.qjl_baseline_decode_attention_bf16.restype = c_int
+        lib.qjl_baseline_decode_attention_bf16.argtypes = [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                                           c_int, c_int, ctypes.c_float, c_vp, c_vp,
+                                                           c_sz, c_vp]
         lib.qjl_release_cache.restype = c_int
         lib.qjl_release_cache.argtypes = []
         lib.qjl_testing_set_encode_small_max.restype = c_int
@@ -227,6 +232,32 @@ def decode_step(q, new_keys, new_values, signs, norms, values, pos: int, seed: i
         _ptr(q), _ptr(new_keys), _ptr(new_values), _ptr(signs), _ptr(norms), _ptr(values),
         B, H_q, H_kv, pos, cap, d, m, seed & (2 ** 64 - 1), 0.0 if scale is None else float(scale),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), s.cuda_stream))
+    return out
+
+
+def baseline_decode_attention_bf16(q, keys, values, N: int, scale: float | None = None, out=None,
+                                   workspace=None, stream=None):
+    """qjl_baseline_decode_attention_bf16: exact softmax attention over bf16
+    keys and values (the uncompressed baseline); returns out fp32 [B][H_q][d]."""
+    import torch
+    B, H_q, d = q.shape
+    _, H_kv, cap, _ = values.shape
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp32 [B][H_q][d]")
+    for name, t in (("keys", keys), ("values", values)):
+        if tuple(t.shape) != (B, H_kv, cap, d) or t.element_size() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous 16-bit (bf16 bits) [B][H_kv][cap][d]")
+    s = _resolve_stream(stream)
+    if out is None:
+        with torch.cuda.stream(s):
+            out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H_q, H_kv, N, d, 256)
+    if workspace is None:
+        workspace = workspace_for(need, q.device, s)
+    _check(load().qjl_baseline_decode_attention_bf16(
+        _ptr(q), _ptr(keys), _ptr(values), B, H_q, H_kv, N, cap, d,
+        0.0 if scale is None else float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), s.cuda_stream))
     return out
 
 

@@ -219,6 +219,25 @@ def test_decode_step_validation(lib):
     assert step(lib, ws_bytes=need - 1, **big) == EWS
 
 
+def base(lib, q=A16, k=A16, v=A16, B=1, Hq=4, Hkv=1, N=8, cap=8, d=128, scale=0.0, out=A16, ws=A16,
+         ws_bytes=1 << 30):
+    return lib.qjl_baseline_decode_attention_bf16(q, k, v, B, Hq, Hkv, N, cap, d, ctypes.c_float(scale),
+                                                  out, ws, ws_bytes, None)
+
+
+def test_baseline_validation(lib):
+    assert base(lib, d=64) == EUNSUP
+    assert base(lib, Hq=6, Hkv=2) == EUNSUP
+    assert base(lib, Hq=6, Hkv=4) == EINVAL
+    assert base(lib, N=9) == EINVAL
+    assert base(lib, scale=-2.0) == EINVAL
+    for name in ("q", "k", "v", "out"):
+        assert base(lib, **{name: None}) == EINVAL
+    assert base(lib, k=A16 + 2) == EINVAL
+    big = dict(Hq=32, Hkv=8, N=32768, cap=32768)
+    assert base(lib, ws=None, **big) == EWS
+
+
 def test_decode_plan_properties(lib):
     for B, Hq, Hkv, N, m in [(1, 8, 1, 4096, 256), (1, 32, 8, 32768, 256), (1, 32, 8, 65600, 512),
                              (8, 40, 40, 16384, 256), (1, 4, 4, 1, 256), (2, 16, 2, 777, 512),
