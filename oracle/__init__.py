@@ -21,8 +21,15 @@ Sources (cited by page title and section):
   a seed, the per-block overhead arithmetic, random rotations and the
   scaled-Beta coordinate density.
 
+* The same page, section "TurboQuant: bridging MSE and inner product, in two
+  stages" -- TurboQuant_prod on keys (``oracle.turboquant``): a Lloyd-Max
+  codebook for the rotated-coordinate density after a random rotation, then
+  QJL on the residual.
+
 Parity status of each function is stated in its module header.
 """
+
+from . import turboquant  # noqa: F401
 
 from .qjl import (  # noqa: F401
     splitmix64_mix,
