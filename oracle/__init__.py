@@ -26,10 +26,14 @@ Sources (cited by page title and section):
   codebook for the rotated-coordinate density after a random rotation, then
   QJL on the residual.
 
+* The same page, section "PolarQuant: skipping Cartesian altogether" -- the
+  PolarQuant key encode (``oracle.polarquant``): a recursive polar transform
+  of the rotated key and per-level angle codebooks.
+
 Parity status of each function is stated in its module header.
 """
 
-from . import turboquant  # noqa: F401
+from . import polarquant, turboquant  # noqa: F401
 
 from .qjl import (  # noqa: F401
     splitmix64_mix,
