@@ -82,6 +82,37 @@ QJL_API const char *qjl_last_error(void);
  * Errors: QJL_EINVAL (out == NULL, d <= 0, m <= 0, d*m > 2^26). */
 QJL_API qjl_status qjl_sketch_host(uint64_t seed, int32_t d, int32_t m, uint16_t *out);
 
+/* ---- Rotate-then-quantize tables (pure host code, no GPU needed) ----
+ * "The Geometry of Forgetting", sections "Random rotation, and what high
+ * dimensions do to your intuitions", "TurboQuant: bridging MSE and inner
+ * product, in two stages" and "PolarQuant: skipping Cartesian altogether".
+ *
+ * qjl_rotation_host: the seeded random rotation Pi, fp32 [d][d] row-major
+ * (y = Pi k): the Q factor of a QR of the d x d standard normals drawn from
+ * `seed` exactly as S is (element e = j*d + i), with R's diagonal made
+ * positive (the uniform, Haar-distributed rotation), rounded to fp32.
+ * Errors: QJL_EINVAL (out NULL, d outside [2, 1024]). */
+QJL_API qjl_status qjl_rotation_host(uint64_t seed, int32_t d, float *out);
+
+/* qjl_tq_codebook_host: the 2^k centroids (ascending) of the optimal scalar
+ * quantizer (Lloyd-Max) for one coordinate of a randomly rotated unit
+ * vector in d dimensions, each rounded to the nearest multiple of 2^-20.
+ * Cell boundaries are the midpoints of adjacent centroids.
+ * Errors: QJL_EINVAL (NULL, d outside [4, 65536], k outside [1, 4]). */
+QJL_API qjl_status qjl_tq_codebook_host(int32_t d, int32_t k, float *centroids);
+
+/* qjl_pq_codebook_host: PolarQuant's codebook of one level.  Level 1
+ * (angles uniform on [0, 2 pi)): 2^bits equal cells, centroids at the cell
+ * middles, and the 2^bits / 4 - 1 thresholds tan(t 2 pi / 2^bits),
+ * t = 1 .. 2^bits / 4 - 1, that split one quadrant.  Level l >= 2 (density
+ * proportional to sin^(2^(l-1) - 1)(2 psi) on [0, pi/2]): the Lloyd-Max
+ * centroids rounded to multiples of 2^-20 and the 2^bits - 1 thresholds
+ * tan(midpoint of adjacent centroids).  Thresholds are rounded to multiples
+ * of 2^-20.  Errors: QJL_EINVAL (NULL, level outside [1, 10], bits outside
+ * [1, 5], or bits < 2 at level 1). */
+QJL_API qjl_status qjl_pq_codebook_host(int32_t level, int32_t bits, float *centroids,
+                                        float *thresholds);
+
 /* Encode n new keys per (batch, kv head): sign bits of S^T k plus ||k||.
  * ("QJL: 1-Bit Quantized JL Transform ...", Abstract: JL transform then sign
  *  bits, no quantization constants; "The Geometry of Forgetting", QJL

@@ -28,7 +28,7 @@ HIP_SOURCES = ["qjl_abi.hip", "encode.hip", "decode.hip"]
 # otherwise cost an instruction per operand and block folding cross-lane
 # moves into the max).
 HIP_EXTRA = {"decode.hip": ["-fno-honor-nans"], "encode.hip": ["-fno-honor-nans"]}
-HOST_SOURCES = ["sketch.cpp"]
+HOST_SOURCES = ["sketch.cpp", "rotq_host.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

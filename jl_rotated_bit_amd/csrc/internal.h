@@ -11,6 +11,21 @@ constexpr int kHeadDim = 128;
 
 // bf16 bit patterns of S ([d][m] row-major) for a seed; see sketch.cpp.
 void generate_sketch_bf16(uint64_t seed, int d, int m, uint16_t* out);
+// The fp64 normals behind it (element e = j*m + i), before any rounding.
+void generate_normals_f64(uint64_t seed, int d, int m, double* out);
+
+// ---- rotate-then-quantize tables (rotq_host.cpp) ----
+// The Haar rotation of a seed: QR of the d x d normals of generate_normals_f64
+// with R's diagonal made positive, Q rounded to fp32, row-major Pi[i][j].
+void make_rotation_f32(uint64_t seed, int d, float* out);
+// TurboQuant: the Lloyd-Max codebook (2^k centroids, ascending) of one
+// coordinate of a randomly rotated unit vector in d dimensions, rounded to
+// multiples of 2^-20.
+void make_tq_codebook(int d, int k, float* centroids);
+// PolarQuant: centroids (2^bits angles) and tangent thresholds of a level's
+// codebook (level 1: the 2^bits / 4 - 1 thresholds inside one quadrant;
+// level >= 2: the 2^bits - 1 thresholds), multiples of 2^-20.
+void make_pq_codebook(int level, int bits, float* centroids, float* thresholds);
 
 // Device-resident copies of one S, kept by the cache in qjl_abi.hip.
 struct DeviceSketch {

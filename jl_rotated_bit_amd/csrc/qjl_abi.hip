@@ -287,6 +287,32 @@ QJL_API qjl_status qjl_sketch_host(uint64_t seed, int32_t d, int32_t m, uint16_t
   return QJL_OK;
 }
 
+QJL_API qjl_status qjl_rotation_host(uint64_t seed, int32_t d, float* out) {
+  g_last_error.clear();
+  if (out == nullptr) return fail(QJL_EINVAL, "qjl_rotation_host: out is NULL");
+  if (d < 2 || d > 1024) return fail(QJL_EINVAL, "qjl_rotation_host: d=%d outside [2, 1024]", d);
+  qjl::make_rotation_f32(seed, d, out);
+  return QJL_OK;
+}
+
+QJL_API qjl_status qjl_tq_codebook_host(int32_t d, int32_t k, float* centroids) {
+  g_last_error.clear();
+  if (centroids == nullptr) return fail(QJL_EINVAL, "qjl_tq_codebook_host: centroids is NULL");
+  if (d < 4 || d > 65536 || k < 1 || k > 4)
+    return fail(QJL_EINVAL, "qjl_tq_codebook_host: d=%d k=%d outside d in [4, 65536], k in [1, 4]", d, k);
+  qjl::make_tq_codebook(d, k, centroids);
+  return QJL_OK;
+}
+
+QJL_API qjl_status qjl_pq_codebook_host(int32_t level, int32_t bits, float* centroids, float* thresholds) {
+  g_last_error.clear();
+  if (centroids == nullptr || thresholds == nullptr) return fail(QJL_EINVAL, "qjl_pq_codebook_host: NULL pointer");
+  if (level < 1 || level > 10 || bits < 1 || bits > 5 || (level == 1 && bits < 2))
+    return fail(QJL_EINVAL, "qjl_pq_codebook_host: level=%d bits=%d unsupported", level, bits);
+  qjl::make_pq_codebook(level, bits, centroids, thresholds);
+  return QJL_OK;
+}
+
 QJL_API qjl_status qjl_encode_keys(const void* keys_bf16, int32_t B, int32_t H_kv, int32_t n,
                                    int32_t d, int32_t m, uint64_t seed, uint32_t* signs,
                                    float* norms, int32_t cap, int32_t pos, void* stream) {

@@ -13,6 +13,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 namespace qjl {
 
@@ -45,7 +46,7 @@ inline uint16_t fp32_to_bf16_rne(float f) {
 
 }  // namespace
 
-void generate_sketch_bf16(uint64_t seed, int d, int m, uint16_t* out) {
+void generate_normals_f64(uint64_t seed, int d, int m, double* out) {
   const int64_t n = static_cast<int64_t>(d) * m;
   const double two_pi = 2.0 * M_PI;
   for (int64_t pair = 0; 2 * pair < n; ++pair) {
@@ -53,11 +54,16 @@ void generate_sketch_bf16(uint64_t seed, int d, int m, uint16_t* out) {
     const double u1 = to_unit_interval(stream_output(seed, 2 * pair + 2));
     const double r = std::sqrt(-2.0 * std::log(u0));
     const double a = two_pi * u1;
-    const double z0 = r * std::cos(a);
-    const double z1 = r * std::sin(a);
-    out[2 * pair] = fp32_to_bf16_rne(static_cast<float>(z0));
-    if (2 * pair + 1 < n) out[2 * pair + 1] = fp32_to_bf16_rne(static_cast<float>(z1));
+    out[2 * pair] = r * std::cos(a);
+    if (2 * pair + 1 < n) out[2 * pair + 1] = r * std::sin(a);
   }
+}
+
+void generate_sketch_bf16(uint64_t seed, int d, int m, uint16_t* out) {
+  const int64_t n = static_cast<int64_t>(d) * m;
+  std::vector<double> z(static_cast<size_t>(n));
+  generate_normals_f64(seed, d, m, z.data());
+  for (int64_t e = 0; e < n; ++e) out[e] = fp32_to_bf16_rne(static_cast<float>(z[e]));
 }
 
 }  // namespace qjl

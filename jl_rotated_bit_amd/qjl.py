@@ -61,6 +61,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.qjl_last_error.argtypes = []
         lib.qjl_sketch_host.restype = c_int
         lib.qjl_sketch_host.argtypes = [c_u64, c_int, c_int, c_vp]
+        lib.qjl_rotation_host.restype = c_int
+        lib.qjl_rotation_host.argtypes = [c_u64, c_int, c_vp]
+        lib.qjl_tq_codebook_host.restype = c_int
+        lib.qjl_tq_codebook_host.argtypes = [c_int, c_int, c_vp]
+        lib.qjl_pq_codebook_host.restype = c_int
+        lib.qjl_pq_codebook_host.argtypes = [c_int, c_int, c_vp, c_vp]
         lib.qjl_encode_keys.restype = c_int
         lib.qjl_encode_keys.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, c_u64, c_vp, c_vp,
                                         c_int, c_int, c_vp]
@@ -109,6 +115,29 @@ def sketch_host(seed: int, d: int, m: int) -> np.ndarray:
     out = np.empty((d, m), dtype=np.uint16)
     _check(load().qjl_sketch_host(seed & (2 ** 64 - 1), d, m, out.ctypes.data))
     return out
+
+
+def rotation_host(seed: int, d: int) -> np.ndarray:
+    """The seeded rotation Pi, fp32 [d][d] (host only)."""
+    out = np.empty((d, d), dtype=np.float32)
+    _check(load().qjl_rotation_host(seed & (2 ** 64 - 1), d, out.ctypes.data))
+    return out
+
+
+def tq_codebook_host(d: int, k: int) -> np.ndarray:
+    """TurboQuant's 2^k Lloyd-Max centroids for dimension d (host only)."""
+    out = np.empty(2 ** k, dtype=np.float32)
+    _check(load().qjl_tq_codebook_host(d, k, out.ctypes.data))
+    return out
+
+
+def pq_codebook_host(level: int, bits: int):
+    """PolarQuant's (centroids, thresholds) of one level (host only)."""
+    cents = np.empty(2 ** bits, dtype=np.float32)
+    nt = 2 ** bits // 4 - 1 if level == 1 else 2 ** bits - 1
+    thr = np.empty(max(1, nt), dtype=np.float32)
+    _check(load().qjl_pq_codebook_host(level, bits, cents.ctypes.data, thr.ctypes.data))
+    return cents, thr[:nt]
 
 
 def _resolve_stream(stream):

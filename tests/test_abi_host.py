@@ -249,3 +249,45 @@ def test_decode_plan_properties(lib):
         assert ws >= B * Hq * ns * 130 * 4
     assert lib.qjl_decode_num_splits(1, 8, 3, 100, 128, 256) == 0
     assert lib.qjl_decode_workspace_bytes(1, 8, 8, 0, 128, 256) == 0
+
+
+@pytest.mark.parametrize("seed", [42, 0, 7, 2 ** 64 - 5])
+def test_host_rotation_is_bit_identical_to_oracle(seed):
+    """The library's Householder QR and the oracle's numpy QR of the same
+    seeded normals give the same fp32 rotation."""
+    from oracle import turboquant as tq
+    assert np.array_equal(qjl.rotation_host(seed, 128), tq.rotation(seed, 128))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_host_tq_codebook_is_bit_identical_to_oracle(k):
+    """Two independent Lloyd-Max solvers (Gauss-Legendre quadrature here,
+    the incomplete Beta function in the oracle) agree after rounding to the
+    2^-20 grid."""
+    from oracle import turboquant as tq
+    assert np.array_equal(qjl.tq_codebook_host(128, k), tq.codebook(128, k)[0])
+
+
+@pytest.mark.parametrize("level,bits", [(1, 4), (1, 3), (2, 2), (3, 2), (4, 2), (5, 2), (6, 2), (7, 2),
+                                        (2, 3), (7, 1)])
+def test_host_pq_codebook_matches_oracle(level, bits):
+    """Tangent thresholds bit for bit; centroids exactly on the grid for
+    levels >= 2, to fp32 rounding at level 1."""
+    from oracle import polarquant as pq
+    c, T = qjl.pq_codebook_host(level, bits)
+    co, _, To = pq.level_codebook(level, bits)
+    assert np.array_equal(T.astype(np.float64), To)
+    if level == 1:
+        assert np.allclose(c, co, rtol=2 ** -23, atol=0)
+    else:
+        assert np.array_equal(c.astype(np.float64), co)
+
+
+def test_host_table_errors(lib):
+    buf = np.zeros(64, np.float32)
+    assert lib.qjl_rotation_host(1, 1, buf.ctypes.data) == EINVAL
+    assert lib.qjl_rotation_host(1, 8, None) == EINVAL
+    assert lib.qjl_tq_codebook_host(128, 0, buf.ctypes.data) == EINVAL
+    assert lib.qjl_tq_codebook_host(128, 5, buf.ctypes.data) == EINVAL
+    assert lib.qjl_pq_codebook_host(1, 1, buf.ctypes.data, buf.ctypes.data) == EINVAL
+    assert lib.qjl_pq_codebook_host(0, 2, buf.ctypes.data, buf.ctypes.data) == EINVAL
