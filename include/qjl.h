@@ -113,6 +113,69 @@ QJL_API qjl_status qjl_tq_codebook_host(int32_t d, int32_t k, float *centroids);
 QJL_API qjl_status qjl_pq_codebook_host(int32_t level, int32_t bits, float *centroids,
                                         float *thresholds);
 
+/* TurboQuant_prod encode ("The Geometry of Forgetting", section "TurboQuant:
+ * bridging MSE and inner product, in two stages"): k bits per coordinate of
+ * the rotated, normalized key from the Lloyd-Max codebook
+ * (qjl_tq_codebook_host(d, k)), then one QJL bit per coordinate on the
+ * residual.  For each key, exactly (every decision is unique):
+ *   norms  = fp32(sqrt(fp64 sum of k_j^2, channel order));
+ *   y_i    = fp32 rounding (nearest even) of the exact sum_j Pi[i][j] k_j,
+ *            Pi = qjl_rotation_host(seed, d);
+ *   u_i    = fp32(y_i / norm) (0 for a zero key);  idx_i = number of cell
+ *            boundaries (midpoints of adjacent centroids) <= u_i;
+ *   r_i    = fp32(u_i - c[idx_i]);  gammas = fp32(sqrt(fp64 sum r_i^2));
+ *   bit_l  = [exact sum_i S[i][l] r_i >= 0], S = the QJL sketch of seed + 1
+ *            with m = d (bf16, as qjl_sketch_host(seed + 1, d, d)).
+ * Layouts (rows [pos, pos + n) of every (b, h) written, others untouched):
+ *   codes  uint32 [B][H_kv][cap][d k / 32]: idx_i in bits k i .. k i + k - 1
+ *          of the row's bit stream (least significant bit first);
+ *   bits   uint32 [B][H_kv][cap][d / 32] (as QJL sign words);
+ *   norms, gammas fp32 [B][H_kv][cap].
+ * keys_bf16 [B][H_kv][n][d]; d == 128; k in {1, 2, 3}; pointers 4-byte
+ * aligned.  Other sizes as for qjl_encode_keys.  The first call for a seed
+ * on a device uploads its tables (~100 KB).  Returns QJL_OK, QJL_EINVAL,
+ * QJL_EUNSUPPORTED, QJL_ENOMEM or QJL_EHIP. */
+QJL_API qjl_status qjl_tq_encode_keys(const void *keys_bf16, int32_t B, int32_t H_kv, int32_t n,
+                                      int32_t d, int32_t k, uint64_t seed, uint32_t *codes,
+                                      uint32_t *bits, float *norms, float *gammas, int32_t cap,
+                                      int32_t pos, void *stream);
+
+/* TurboQuant_prod scores: the estimate of <q, k_t> for every query head and
+ * cached token t < N (same section: the reconstruction's inner product plus
+ * the QJL estimate of the residual's, unbiased):
+ *   scores[b][h][t] = norm_t (<Pi q, c[idx_t]> + sqrt(pi/2)/d gamma_t
+ *                     <S^T Pi q, 2 bit_t - 1>),  kv head h / (H_q / H_kv).
+ * q fp32 [B][H_q][d]; caches as written by qjl_tq_encode_keys (same k,
+ * seed); scores fp32 [B][H_q][N].  G = H_q / H_kv in {1, 2, 4, 8};
+ * 1 <= N <= cap.  fp32 arithmetic (relative error ~1e-6 of the score
+ * scale).  Returns QJL_OK, QJL_EINVAL, QJL_EUNSUPPORTED, QJL_ENOMEM or
+ * QJL_EHIP. */
+QJL_API qjl_status qjl_tq_scores(const float *q, const uint32_t *codes, const uint32_t *bits,
+                                 const float *norms, const float *gammas, int32_t B, int32_t H_q,
+                                 int32_t H_kv, int32_t N, int32_t cap, int32_t d, int32_t k,
+                                 uint64_t seed, float *scores, void *stream);
+
+/* PolarQuant encode ("The Geometry of Forgetting", section "PolarQuant:
+ * skipping Cartesian altogether"): the rotated key y (as for
+ * qjl_tq_encode_keys) is turned into polar form recursively and each angle
+ * stored as its cell in the level's codebook (qjl_pq_codebook_host; 4 bits
+ * at level 1, 2 bits at levels 2..7 for d = 128), with the radius in fp32:
+ *   level 1, pair (a, b) = (y_2j, y_2j+1): quadrant q from the signs (the
+ *     angle lies in [q pi/2, (q+1) pi/2); (0, 0) has angle 0), the pair turned
+ *     into the first quadrant ((a,b), (b,-a), (-a,-b), (-b,a)) = (a', b'), cell
+ *     = 4 q + #{thresholds T : b' >= T a'} (fp64; 0 for (0, 0));
+ *   level l >= 2: with fp64 slice sums of squares (pairs a^2 + b^2, then sums
+ *     of adjacent slices), cell = #{thresholds T : s_b >= (T T) s_a};
+ *   radius = fp32(sqrt(fp64 total)).
+ *   codes  uint32 [B][H_kv][cap][12]: the 64 level-1 cells (4 bits each, pair
+ *          0 first), then the 63 cells of levels 2..7 (2 bits each, level
+ *          by level), least significant bit first; 2 bits of padding.
+ *   radii  fp32 [B][H_kv][cap].
+ * d == 128; other sizes and errors as for qjl_tq_encode_keys. */
+QJL_API qjl_status qjl_pq_encode_keys(const void *keys_bf16, int32_t B, int32_t H_kv, int32_t n,
+                                      int32_t d, uint64_t seed, uint32_t *codes, float *radii,
+                                      int32_t cap, int32_t pos, void *stream);
+
 /* Encode n new keys per (batch, kv head): sign bits of S^T k plus ||k||.
  * ("QJL: 1-Bit Quantized JL Transform ...", Abstract: JL transform then sign
  *  bits, no quantization constants; "The Geometry of Forgetting", QJL

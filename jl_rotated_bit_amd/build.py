@@ -22,12 +22,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqjl.so")
 
-HIP_SOURCES = ["qjl_abi.hip", "encode.hip", "decode.hip"]
+HIP_SOURCES = ["qjl_abi.hip", "encode.hip", "decode.hip", "rotq.hip"]
 # Per-source extras.  NaN inputs are outside the contract of both kernels, and
 # without NaNs a min/max needs no operand canonicalization (which would
 # otherwise cost an instruction per operand and block folding cross-lane
 # moves into the max).
-HIP_EXTRA = {"decode.hip": ["-fno-honor-nans"], "encode.hip": ["-fno-honor-nans"]}
+HIP_EXTRA = {"decode.hip": ["-fno-honor-nans"], "encode.hip": ["-fno-honor-nans"],
+             # every operation that feeds a code decision rounds as written
+             "rotq.hip": ["-ffp-contract=off"]}
 HOST_SOURCES = ["sketch.cpp", "rotq_host.cpp"]
 ARCH = "gfx950"
 

@@ -99,4 +99,26 @@ int launch_decode_bf16(const DecodePlan& plan, const float* q, const void* keys,
                        int B, int H_q, int H_kv, int N, int cap, float scale, float* out,
                        void* workspace, void* stream);
 
+// Device copies of the rotate-then-quantize tables of one seed.
+struct RotqTables {
+  const float* rot = nullptr;     // Pi [i][j] fp32
+  const float* rotT = nullptr;    // Pi^T [j][i] fp32
+  const uint16_t* s_il = nullptr; // QJL sketch of seed + 1 with m = d, bf16 [i][l]
+  const float* tq_cents = nullptr;  // TurboQuant centroids, k = 1..3 at 8 * (k - 1)
+  const float* pq_thr = nullptr;    // PolarQuant thresholds [7 levels][8]
+  float rot_row_max = 0.f;        // max_i ||Pi_i|| rounded up
+  float s_col_max = 0.f;          // max_l ||S[:, l]|| rounded up
+};
+constexpr int kPqBits[7] = {4, 2, 2, 2, 2, 2, 2};   // PolarQuant bits per level (d = 128)
+
+// method 0: TurboQuant_prod with k MSE bits (codes, bits, norms, gammas);
+// method 1: PolarQuant (codes -> cells, norms -> radii).  margin_log2 > 0
+// widens the certificates (test hook: routes values to the exact paths).
+int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys, int B, int H_kv, int n,
+                       uint32_t* codes, uint32_t* bits, float* norms, float* gammas, int cap, int pos,
+                       int margin_log2, void* stream);
+int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t* codes,
+                     const uint32_t* bits, const float* norms, const float* gammas, int B, int H_q,
+                     int H_kv, int N, int cap, float* out, void* stream);
+
 }  // namespace qjl

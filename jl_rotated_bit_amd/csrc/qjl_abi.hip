@@ -7,6 +7,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
+#include <climits>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -140,6 +142,96 @@ qjl_status get_sketch(uint64_t seed, int d, int m, qjl::DeviceSketch* out) {
   ce.view.m = m;
   g_cache.emplace(key, ce);
   *out = ce.view;
+  return QJL_OK;
+}
+
+// ---- device cache of the rotate-then-quantize tables, keyed by (device, seed) ----
+struct RotqEntry {
+  qjl::RotqTables view;
+  void* mem = nullptr;
+};
+std::map<std::tuple<int, uint64_t>, RotqEntry> g_rotq;   // guarded by g_cache_mu
+thread_local int g_rotq_margin = 0;                       // test hook
+
+float round_up_f32(double x) { return std::nextafter(static_cast<float>(x), INFINITY); }
+
+qjl_status get_rotq(uint64_t seed, qjl::RotqTables* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QJL_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  const auto key = std::make_tuple(dev, seed);
+  auto it = g_rotq.find(key);
+  if (it != g_rotq.end()) {
+    *out = it->second.view;
+    return QJL_OK;
+  }
+  constexpr int d = qjl::kHeadDim;
+  std::vector<float> rot(d * d), rotT(d * d);
+  qjl::make_rotation_f32(seed, d, rot.data());
+  double rmax = 0.0;
+  for (int i = 0; i < d; ++i) {
+    double ss = 0.0;
+    for (int j = 0; j < d; ++j) {
+      rotT[j * d + i] = rot[i * d + j];
+      ss += static_cast<double>(rot[i * d + j]) * rot[i * d + j];
+    }
+    rmax = std::max(rmax, std::sqrt(ss));
+  }
+  std::vector<uint16_t> s_il(d * d);
+  qjl::generate_sketch_bf16(seed + 1, d, d, s_il.data());
+  double smax = 0.0;
+  for (int l = 0; l < d; ++l) {
+    double ss = 0.0;
+    for (int i = 0; i < d; ++i) {
+      uint32_t u = static_cast<uint32_t>(s_il[i * d + l]) << 16;
+      float f;
+      std::memcpy(&f, &u, sizeof(f));
+      ss += static_cast<double>(f) * f;
+    }
+    smax = std::max(smax, std::sqrt(ss));
+  }
+  std::vector<float> cents(24, 0.f), thr(7 * 8, 0.f), pc(32);
+  for (int k = 1; k <= 3; ++k) qjl::make_tq_codebook(d, k, cents.data() + 8 * (k - 1));
+  for (int lev = 1; lev <= 7; ++lev) qjl::make_pq_codebook(lev, qjl::kPqBits[lev - 1], pc.data(), thr.data() + 8 * (lev - 1));
+  const size_t b_rot = d * d * 4, b_s = d * d * 2, b_c = 24 * 4, b_t = 56 * 4;
+  const size_t o_rotT = b_rot, o_s = 2 * b_rot, o_c = o_s + b_s, o_t = o_c + 256, total = o_t + b_t;
+  void* mem = nullptr;
+  e = hipMalloc(&mem, total);
+  if (e != hipSuccess) return fail(QJL_ENOMEM, "hipMalloc(%zu) for the rotation tables: %s", total, hipGetErrorString(e));
+  auto* base = static_cast<uint8_t*>(mem);
+  e = hipMemcpy(base, rot.data(), b_rot, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_rotT, rotT.data(), b_rot, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_s, s_il.data(), b_s, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_c, cents.data(), b_c, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_t, thr.data(), b_t, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    return fail(QJL_EHIP, "uploading the rotation tables: %s", hipGetErrorString(e));
+  }
+  RotqEntry ent;
+  ent.mem = mem;
+  ent.view.rot = reinterpret_cast<const float*>(base);
+  ent.view.rotT = reinterpret_cast<const float*>(base + o_rotT);
+  ent.view.s_il = reinterpret_cast<const uint16_t*>(base + o_s);
+  ent.view.tq_cents = reinterpret_cast<const float*>(base + o_c);
+  ent.view.pq_thr = reinterpret_cast<const float*>(base + o_t);
+  ent.view.rot_row_max = round_up_f32(rmax);
+  ent.view.s_col_max = round_up_f32(smax);
+  g_rotq.emplace(key, ent);
+  *out = ent.view;
+  return QJL_OK;
+}
+
+qjl_status check_rows(const char* fn, int32_t B, int32_t H_kv, int32_t n, int32_t cap, int32_t pos) {
+  if (B <= 0 || H_kv <= 0 || n < 0 || cap <= 0 || pos < 0)
+    return fail(QJL_EINVAL, "%s: bad sizes B=%d H_kv=%d n=%d cap=%d pos=%d", fn, B, H_kv, n, cap, pos);
+  if (static_cast<int64_t>(pos) + n > cap)
+    return fail(QJL_EINVAL, "%s: pos+n=%lld exceeds cap=%d", fn, static_cast<long long>(pos) + n, cap);
+  if (static_cast<int64_t>(B) * H_kv * cap > (int64_t{1} << 40)) return fail(QJL_EINVAL, "%s: cache too large", fn);
+  if (static_cast<int64_t>(B) * H_kv * n > INT32_MAX)
+    return fail(QJL_EINVAL, "%s: B*H_kv*n=%lld keys in one call (at most 2^31 - 1)", fn,
+                static_cast<long long>(B) * H_kv * n);
   return QJL_OK;
 }
 
@@ -438,6 +530,84 @@ QJL_API qjl_status qjl_baseline_decode_attention_bf16(const float* q, const void
   return QJL_OK;
 }
 
+QJL_API qjl_status qjl_tq_encode_keys(const void* keys_bf16, int32_t B, int32_t H_kv, int32_t n,
+                                      int32_t d, int32_t k, uint64_t seed, uint32_t* codes,
+                                      uint32_t* bits, float* norms, float* gammas, int32_t cap,
+                                      int32_t pos, void* stream) {
+  const char* fn = "qjl_tq_encode_keys";
+  g_last_error.clear();
+  if (d != qjl::kHeadDim || k < 1 || k > 3)
+    return fail(QJL_EUNSUPPORTED, "%s: d=%d k=%d unsupported (d=128, k in {1,2,3})", fn, d, k);
+  qjl_status st = check_rows(fn, B, H_kv, n, cap, pos);
+  if (st != QJL_OK || n == 0) return st;
+  if (keys_bf16 == nullptr || codes == nullptr || bits == nullptr || norms == nullptr || gammas == nullptr)
+    return fail(QJL_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned(keys_bf16, 4) || !aligned(codes, 4) || !aligned(bits, 4) || !aligned(norms, 4) || !aligned(gammas, 4))
+    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+  qjl::RotqTables tb;
+  st = get_rotq(seed, &tb);
+  if (st != QJL_OK) return st;
+  const int e = qjl::launch_rotq_encode(tb, 0, k, keys_bf16, B, H_kv, n, codes, bits, norms, gammas, cap, pos,
+                                        g_rotq_margin, stream);
+  if (e != hipSuccess) return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
+  return QJL_OK;
+}
+
+QJL_API qjl_status qjl_pq_encode_keys(const void* keys_bf16, int32_t B, int32_t H_kv, int32_t n,
+                                      int32_t d, uint64_t seed, uint32_t* codes, float* radii,
+                                      int32_t cap, int32_t pos, void* stream) {
+  const char* fn = "qjl_pq_encode_keys";
+  g_last_error.clear();
+  if (d != qjl::kHeadDim) return fail(QJL_EUNSUPPORTED, "%s: d=%d unsupported (d=128)", fn, d);
+  qjl_status st = check_rows(fn, B, H_kv, n, cap, pos);
+  if (st != QJL_OK || n == 0) return st;
+  if (keys_bf16 == nullptr || codes == nullptr || radii == nullptr) return fail(QJL_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned(keys_bf16, 4) || !aligned(codes, 4) || !aligned(radii, 4))
+    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+  qjl::RotqTables tb;
+  st = get_rotq(seed, &tb);
+  if (st != QJL_OK) return st;
+  const int e = qjl::launch_rotq_encode(tb, 1, 0, keys_bf16, B, H_kv, n, codes, nullptr, radii, nullptr, cap,
+                                        pos, g_rotq_margin, stream);
+  if (e != hipSuccess) return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
+  return QJL_OK;
+}
+
+QJL_API qjl_status qjl_tq_scores(const float* q, const uint32_t* codes, const uint32_t* bits,
+                                 const float* norms, const float* gammas, int32_t B, int32_t H_q,
+                                 int32_t H_kv, int32_t N, int32_t cap, int32_t d, int32_t k,
+                                 uint64_t seed, float* scores, void* stream) {
+  const char* fn = "qjl_tq_scores";
+  g_last_error.clear();
+  if (d != qjl::kHeadDim || k < 1 || k > 3)
+    return fail(QJL_EUNSUPPORTED, "%s: d=%d k=%d unsupported (d=128, k in {1,2,3})", fn, d, k);
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || cap <= 0 || N <= 0 || N > cap)
+    return fail(QJL_EINVAL, "%s: bad sizes B=%d H_q=%d H_kv=%d N=%d cap=%d", fn, B, H_q, H_kv, N, cap);
+  if (H_q % H_kv != 0) return fail(QJL_EINVAL, "%s: H_q=%d is not a multiple of H_kv=%d", fn, H_q, H_kv);
+  const int G = H_q / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(QJL_EUNSUPPORTED, "%s: G=H_q/H_kv=%d unsupported (1, 2, 4, 8)", fn, G);
+  if (static_cast<int64_t>(B) * H_kv * cap > (int64_t{1} << 40)) return fail(QJL_EINVAL, "%s: cache too large", fn);
+  if (static_cast<int64_t>(B) * H_q * N > (int64_t{1} << 40)) return fail(QJL_EINVAL, "%s: output too large", fn);
+  if (q == nullptr || codes == nullptr || bits == nullptr || norms == nullptr || gammas == nullptr || scores == nullptr)
+    return fail(QJL_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned(q, 4) || !aligned(codes, 4) || !aligned(bits, 4) || !aligned(norms, 4) || !aligned(gammas, 4) ||
+      !aligned(scores, 4))
+    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+  qjl::RotqTables tb;
+  qjl_status st = get_rotq(seed, &tb);
+  if (st != QJL_OK) return st;
+  const int e = qjl::launch_tq_scores(tb, k, q, codes, bits, norms, gammas, B, H_q, H_kv, N, cap, scores, stream);
+  if (e != hipSuccess) return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
+  return QJL_OK;
+}
+
+QJL_API int32_t qjl_testing_set_rotq_margin(int32_t log2_factor) {
+  const int prev = g_rotq_margin;
+  if (log2_factor >= 0 && log2_factor <= 60) g_rotq_margin = log2_factor;
+  return prev;
+}
+
 QJL_API qjl_status qjl_release_cache(void) {
   g_last_error.clear();
   std::lock_guard<std::mutex> lock(g_cache_mu);
@@ -452,6 +622,13 @@ QJL_API qjl_status qjl_release_cache(void) {
     }
   }
   g_cache.clear();
+  for (auto& kv : g_rotq) {
+    if (hipSetDevice(std::get<0>(kv.first)) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      if (hipFree(kv.second.mem) != hipSuccess) rc = fail(QJL_EHIP, "qjl_release_cache: hipFree failed");
+    }
+  }
+  g_rotq.clear();
   if (have_dev) (void)hipSetDevice(cur);
   return rc;
 }

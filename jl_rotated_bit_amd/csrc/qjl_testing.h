@@ -24,6 +24,14 @@ extern "C" {
  * kernels give identical sign words; norms may differ in the last bit. */
 QJL_API int32_t qjl_testing_set_encode_small_max(int32_t keys);
 
+/* Rotate-then-quantize encodes (qjl_tq_encode_keys, qjl_pq_encode_keys)
+ * made by the CALLING THREAD widen their two error certificates (the fp32
+ * rounding of the rotated key, the signs of the residual's sketch) by
+ * 2^log2_factor, so that many values take the exact integer paths; the
+ * results must not change.  0 (the default) is the production margin;
+ * values outside [0, 60] change nothing.  Returns the previous value. */
+QJL_API int32_t qjl_testing_set_rotq_margin(int32_t log2_factor);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,597 @@
+// Rotate-then-quantize key encoders for gfx950: TurboQuant_prod and
+// PolarQuant, plus TurboQuant's inner-product scores.
+//
+// "The Geometry of Forgetting: How Three Papers Cracked KV Cache
+// Quantization":
+// * section "TurboQuant: bridging MSE and inner product, in two stages":
+//   rotate the (unit) key by a random rotation, quantize every coordinate
+//   with the Lloyd-Max codebook of the rotated-coordinate density (b - 1
+//   bits), then spend one bit per coordinate on QJL of the residual; the
+//   estimate of <q, k> adds the QJL estimate of <q, residual> to
+//   <q, reconstruction> and is unbiased;
+// * section "PolarQuant: skipping Cartesian altogether": rotate, transform
+//   recursively to polar form (pairs of coordinates, then pairs of radii),
+//   store each angle's cell in its level's codebook and the radius.
+//
+// Every value that decides a code is defined exactly, so codes and bits
+// are unique (the same definitions as the CPU oracle):
+//   n   = fp32(sqrt(fp64 sum of k_j^2 in channel order));
+//   y_i = the fp32 rounding (nearest even) of the exact sum_j Pi[i][j] k_j;
+// TurboQuant: u = fp32(y / n) (0 for a zero key), idx = #{boundaries <= u},
+//   r = fp32(u - c[idx]), g = fp32(sqrt(fp64 sum of r_i^2 in order)),
+//   bit_l = [exact sum_i S[i][l] r_i >= 0];
+// PolarQuant: level-1 pair cells by quadrant and fp64 comparisons
+//   b' >= T a'; level-l cells by s_b >= T^2 s_a on fp64 tree sums of
+//   squares; radius = fp32(sqrt(total)).
+//
+// Kernel design.  A workgroup (256 threads) keeps Pi^T (fp32, 64 KB) and, for
+// TurboQuant, S (bf16, 32 KB) in LDS for the whole launch and walks over
+// tiles of 32 keys.  The rotation is an fp64 product (each product of an fp32
+// and a bf16 value is exact in fp64; MI355X runs fp64 FMAs at its full fp64
+// rate on the vector units): thread (coordinate i, key half h) accumulates
+// 16 keys, reading Pi^T[j][i] (consecutive lanes, no bank conflicts) and the
+// 16 keys' channel j as a broadcast.  The fp32 rounding is certified: with
+// E = 2 d 2^-53 ||k|| max_i ||Pi_i|| bounding the fp64 error, y = fp32(v + E)
+// when that equals fp32(v - E); otherwise (about one value in 10^5) the sum
+// is recomputed exactly in a 576-bit integer accumulator and rounded from
+// there.  The residual's QJL signs are certified the same way (the sign of
+// the fp64 sum when it exceeds its error bound, else the exact integer sum).
+// This file is compiled with -ffp-contract=off: every fp64/fp32 operation
+// that feeds a decision rounds exactly as written.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "exact_sign.h"
+#include "internal.h"
+
+namespace qjl {
+namespace {
+
+constexpr int D = kHeadDim;      // 128
+constexpr int TK = 32;           // keys per tile
+constexpr int NT = 256;          // threads per workgroup
+constexpr int PQ_LEVELS = 7;     // log2(128)
+constexpr int PQ_WORDS = 12;     // 64 * 4 + 63 * 2 = 382 bits
+constexpr int PQ_MAXT = 8;       // thresholds per level (<= 2^3 - 1 or 2^bits/4 - 1)
+
+// ---- exact fallbacks: 576-bit signed sums of fp32 x bf16 products ----
+// A bf16 value is sk 2^(ek - 134) (sk < 2^8, ek >= 1) and an fp32 value
+// sp 2^(ep - 150) (sp < 2^24); each product is the integer sk sp < 2^32
+// times 2^(ek + ep - 284), added shifted by ek + ep - 2 bits, so the sum is
+// N 2^-282 with N held as two 576-bit magnitudes (positive / negative terms).
+__device__ __forceinline__ void add_product(uint32_t* pos, uint32_t* neg, uint32_t kb, float p) {
+  const uint32_t up = __float_as_uint(p);
+  uint32_t ek = (kb >> 7) & 0xFF, ep = (up >> 23) & 0xFF;
+  const uint32_t sk = ek ? ((kb & 0x7F) | 0x80) : (kb & 0x7F);
+  const uint32_t sp = ep ? ((up & 0x7FFFFF) | 0x800000) : (up & 0x7FFFFF);
+  if (sk == 0 || sp == 0) return;
+  ek = ek ? (ek > 254 ? 254 : ek) : 1;   // Inf/NaN inputs: undefined but in bounds
+  ep = ep ? (ep > 254 ? 254 : ep) : 1;
+  const uint32_t shift = ek + ep - 2;
+  const uint64_t v = (static_cast<uint64_t>(sk) * sp) << (shift & 31);
+  long_add(((kb >> 15) ^ (up >> 31)) & 1 ? neg : pos, static_cast<int>(shift >> 5), v);
+}
+
+// Sign of pos - neg (true for >= 0).
+__device__ bool long_sign(const uint32_t* pos, const uint32_t* neg) {
+  for (int i = ACC_WORDS - 1; i >= 0; --i)
+    if (pos[i] != neg[i]) return pos[i] > neg[i];
+  return true;
+}
+
+// fp32 rounding (nearest, ties to even) of (pos - neg) 2^-282.
+__device__ float long_to_f32(uint32_t* pos, uint32_t* neg) {
+  const bool nonneg = long_sign(pos, neg);
+  uint32_t* a = nonneg ? pos : neg;
+  const uint32_t* b = nonneg ? neg : pos;
+  // a -= b (a >= b)
+  uint64_t borrow = 0;
+  for (int i = 0; i < ACC_WORDS; ++i) {
+    const uint64_t t = static_cast<uint64_t>(a[i]) - b[i] - borrow;
+    a[i] = static_cast<uint32_t>(t);
+    borrow = (t >> 63) & 1;
+  }
+  int top = -1;
+  for (int i = ACC_WORDS - 1; i >= 0 && top < 0; --i)
+    if (a[i]) top = 32 * i + 31 - __builtin_clz(a[i]);
+  if (top < 0) return 0.0f;
+  // quantum of the result: 24 significant bits, or 2^-149 for subnormals
+  // (bit 133 of N is 2^-149)
+  const int q = max(top - 23, 133);
+  auto bit = [&](int p) -> uint32_t { return p < 0 ? 0u : (a[p >> 5] >> (p & 31)) & 1u; };
+  uint32_t mant = 0;
+  for (int p = top; p >= q; --p) mant = (mant << 1) | bit(p);
+  const uint32_t rbit = bit(q - 1);
+  bool sticky = false;
+  for (int p = q - 2; p >= 0 && !sticky; --p) sticky = bit(p) != 0;
+  if (rbit && (sticky || (mant & 1u))) ++mant;
+  const float r = __builtin_ldexpf(static_cast<float>(mant), q - 282);
+  return nonneg ? r : -r;
+}
+
+__device__ __forceinline__ void long_clear(uint32_t* s) {
+  for (int i = 0; i < 2 * ACC_WORDS; ++i) s[i] = 0;
+}
+
+// Tables of one launch (device pointers; see RotqTables in internal.h).
+struct RotqArgs {
+  const uint16_t* keys;     // bf16 [R][d] (this launch's rows)
+  int R;                    // keys in this launch
+  int n;                    // keys per (batch, kv head) of the call
+  int cap, pos;
+  uint32_t r0;              // global row of keys[0]
+  const float* rotT;        // Pi^T [j][i] fp32
+  const float* rot;         // Pi [i][j] fp32 (exact fallback rows)
+  float rot_row_max;        // max_i ||Pi_i||, rounded up
+  // TurboQuant
+  const uint16_t* s_il;     // S [i][l] bf16 (i = coordinate, l = sketch row), m = d
+  float s_col_max;          // max_l ||S[:, l]||, rounded up
+  const float* cents;       // 2^k
+  int k;
+  uint32_t* codes;          // [rows][d k / 32]
+  uint32_t* bits;           // [rows][d / 32]
+  float* norms;
+  float* gammas;
+  // PolarQuant
+  const float* pq_thr;      // [PQ_LEVELS][PQ_MAXT] tangent thresholds
+  uint32_t* pq_codes;       // [rows][PQ_WORDS]
+  float* radii;
+  int margin_log2;          // test hook: widens both certificates by 2^margin_log2
+};
+
+__device__ __forceinline__ int64_t dest_row(uint32_t r, uint32_t un, int cap, int pos) {
+  const uint32_t bh = r / un;
+  return static_cast<int64_t>(bh) * cap + pos + (r - bh * un);
+}
+
+struct RotqLds {
+  float rotT[D * D];               // 64 KB
+  uint16_t s_il[D * D];            // 32 KB (TurboQuant)
+  double kt[D * TK];               // keys (then residuals), [j][t]: 32 KB
+  float y[TK][D + 1];              // rotated keys
+  double nsq[TK];                  // fp64 sums of squares
+  float nrm[TK];
+  uint8_t cell[TK][D];             // codes / level cells
+  uint32_t qwords[TK][4];          // TurboQuant sign words
+  uint32_t scratch[NT / 64][2 * ACC_WORDS];
+};
+
+// Stage A: y = RN32(exact Pi k) for the tile's keys (rows t < nk valid).
+__device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  // keys -> LDS as fp64, transposed ([j][t]); missing rows are zero
+  for (int e = tid; e < TK * D / 2; e += NT) {
+    const int t = e / (D / 2), jp = e % (D / 2);
+    uint32_t pair = 0;
+    if (t < nk) pair = reinterpret_cast<const uint32_t*>(a.keys + static_cast<int64_t>(row0 + t) * D)[jp];
+    L.kt[(2 * jp) * TK + t] = static_cast<double>(__uint_as_float(pair << 16));
+    L.kt[(2 * jp + 1) * TK + t] = static_cast<double>(__uint_as_float(pair & 0xFFFF0000u));
+  }
+  __syncthreads();
+  // ||k||^2 in channel order (one thread per key)
+  if (tid < TK) {
+    double s = 0.0;
+    for (int j = 0; j < D; ++j) {
+      const double v = L.kt[j * TK + tid];
+      s = s + v * v;
+    }
+    L.nsq[tid] = s;
+    L.nrm[tid] = static_cast<float>(__builtin_sqrt(s));
+  }
+  // the fp64 product
+  const int i = tid & (D - 1), h = tid >> 7;
+  double acc[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc[u] = 0.0;
+#pragma unroll 4
+  for (int j = 0; j < D; ++j) {
+    const double p = static_cast<double>(L.rotT[j * D + i]);
+    const double2* kv = reinterpret_cast<const double2*>(&L.kt[j * TK + 16 * h]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double2 k2 = kv[u];
+      acc[2 * u] = __builtin_fma(k2.x, p, acc[2 * u]);
+      acc[2 * u + 1] = __builtin_fma(k2.y, p, acc[2 * u + 1]);
+    }
+  }
+  __syncthreads();   // nsq ready
+  // certify the fp32 rounding: |v - exact| <= 2 d 2^-53 ||k|| ||Pi_i||
+  const double wide = __builtin_ldexp(1.0, a.margin_log2);
+  uint32_t open = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int t = 16 * h + u;
+    const double kn = __builtin_sqrt(L.nsq[t]) * (1.0 + 0x1.0p-40);
+    const double E = 2.0 * D * 0x1.0p-53 * kn * static_cast<double>(a.rot_row_max) * wide + 0x1.0p-1060;
+    const float lo = static_cast<float>(acc[u] - E);
+    const float hi = static_cast<float>(acc[u] + E);
+    L.y[t][i] = hi;
+    if (lo != hi && t < nk) open |= 1u << u;
+  }
+  // exact sums for the uncertified values (about one in 10^5): the lanes
+  // of a wave take turns with the wave's integer accumulator
+  for (uint64_t any = __ballot(open != 0); any != 0; any = __ballot(open != 0)) {
+    const int l = __builtin_ctzll(any);   // wave-uniform
+    if (lane == l) {
+      uint32_t* pos = L.scratch[wave];
+      uint32_t* neg = pos + ACC_WORDS;
+      for (uint32_t o = open; o; o &= o - 1) {
+        const int t = 16 * h + __builtin_ctz(o);
+        long_clear(pos);
+        const uint16_t* krow = a.keys + static_cast<int64_t>(row0 + t) * D;
+        for (int j = 0; j < D; ++j) add_product(pos, neg, krow[j], a.rot[i * D + j]);
+        L.y[t][i] = long_to_f32(pos, neg);
+      }
+      open = 0;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// TurboQuant_prod encode
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
+  __shared__ __attribute__((aligned(16))) RotqLds L;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < D * D / 4; e += NT)
+    reinterpret_cast<float4*>(L.rotT)[e] = reinterpret_cast<const float4*>(a.rotT)[e];
+  for (int e = tid; e < D * D / 8; e += NT)
+    reinterpret_cast<uint4*>(L.s_il)[e] = reinterpret_cast<const uint4*>(a.s_il)[e];
+  const int K = a.k;
+  const int L2 = 1 << K;
+  float cents[8], bnds[7];
+  for (int v = 0; v < 8; ++v) cents[v] = v < L2 ? a.cents[v] : 0.f;
+  for (int v = 0; v < 7; ++v) bnds[v] = v < L2 - 1 ? 0.5f * (cents[v] + cents[v + 1]) : INFINITY;
+  const double wide = __builtin_ldexp(1.0, a.margin_log2);
+  __syncthreads();
+
+  for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int row0 = tile * TK;
+    const int nk = min(TK, a.R - row0);
+    rotate_tile(L, a, row0, nk);
+    // u, codes, residual (thread per (coordinate, key half))
+    const int i = tid & (D - 1), h = tid >> 7;
+    for (int u8 = 0; u8 < 16; ++u8) {
+      const int t = 16 * h + u8;
+      const float n = L.nrm[t];
+      const float u = n > 0.f ? L.y[t][i] / n : 0.f;
+      int idx = 0;
+      for (int v = 0; v < L2 - 1; ++v) idx += u >= bnds[v] ? 1 : 0;
+      float c = cents[0];
+      for (int v = 1; v < L2; ++v) c = idx == v ? cents[v] : c;
+      const float r = u - c;
+      L.cell[t][i] = static_cast<uint8_t>(idx);
+      L.y[t][i] = r;   // the residual replaces y
+    }
+    __syncthreads();
+    // residuals -> fp64 [i][t]; g in coordinate order
+    for (int e = tid; e < TK * D; e += NT) {
+      const int t = e / D, ii = e % D;
+      L.kt[ii * TK + t] = static_cast<double>(L.y[t][ii]);
+    }
+    __syncthreads();
+    if (tid < TK) {
+      double s = 0.0;
+      for (int ii = 0; ii < D; ++ii) {
+        const double v = L.kt[ii * TK + tid];
+        s = s + v * v;
+      }
+      L.nsq[tid] = s;
+    }
+    // z = S^T r (thread per (sketch row l, key half))
+    const int l = i;
+    double acc[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc[u] = 0.0;
+#pragma unroll 4
+    for (int ii = 0; ii < D; ++ii) {
+      const double s = static_cast<double>(__uint_as_float(static_cast<uint32_t>(L.s_il[ii * D + l]) << 16));
+      const double2* rv = reinterpret_cast<const double2*>(&L.kt[ii * TK + 16 * h]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const double2 r2 = rv[u];
+        acc[2 * u] = __builtin_fma(r2.x, s, acc[2 * u]);
+        acc[2 * u + 1] = __builtin_fma(r2.y, s, acc[2 * u + 1]);
+      }
+    }
+    __syncthreads();   // nsq (residual) ready
+    uint32_t open = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = 16 * h + u;
+      const double rn = __builtin_sqrt(L.nsq[t]) * (1.0 + 0x1.0p-40);
+      const double E = 2.0 * D * 0x1.0p-53 * rn * static_cast<double>(a.s_col_max) * wide + 0x1.0p-1060;
+      if (!(__builtin_fabs(acc[u]) > E) && t < nk) open |= 1u << u;
+    }
+    // exact signs for the uncertified sums (rare): lanes take turns with the
+    // wave's integer accumulator
+    for (uint64_t any = __ballot(open != 0); any != 0; any = __ballot(open != 0)) {
+      const int ln = __builtin_ctzll(any);
+      if (lane == ln) {
+        uint32_t* pos = L.scratch[wave];
+        uint32_t* neg = pos + ACC_WORDS;
+        for (uint32_t o = open; o; o &= o - 1) {
+          const int u = __builtin_ctz(o);
+          const int t = 16 * h + u;
+          long_clear(pos);
+          for (int ii = 0; ii < D; ++ii) add_product(pos, neg, L.s_il[ii * D + l], L.y[t][ii]);
+          acc[u] = long_sign(pos, neg) ? 1.0 : -1.0;
+        }
+        open = 0;
+      }
+    }
+    // sign words: wave (l / 64, h) holds coordinates 64 (wave & 1) .. +63
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint64_t m = __ballot(acc[u] >= 0.0);
+      if (lane == 0) {
+        const int t = 16 * h + u;
+        L.qwords[t][2 * (wave & 1)] = static_cast<uint32_t>(m);
+        L.qwords[t][2 * (wave & 1) + 1] = static_cast<uint32_t>(m >> 32);
+      }
+    }
+    __syncthreads();
+    // stores: codes (bit stream, k bits per coordinate), sign words, n, g
+    const int cw = D * K / 32;
+    for (int e = tid; e < TK * (cw + 4); e += NT) {
+      const int t = e / (cw + 4), w = e % (cw + 4);
+      if (t >= nk) continue;
+      const int64_t row = dest_row(a.r0 + row0 + t, static_cast<uint32_t>(a.n), a.cap, a.pos);
+      if (w < cw) {
+        uint32_t word = 0;
+        for (int p = 0; p < 32; ++p) {
+          const int b = 32 * w + p;
+          word |= ((static_cast<uint32_t>(L.cell[t][b / K]) >> (b % K)) & 1u) << p;
+        }
+        a.codes[row * cw + w] = word;
+      } else {
+        a.bits[row * 4 + (w - cw)] = L.qwords[t][w - cw];
+      }
+    }
+    if (tid < nk) {
+      const int64_t row = dest_row(a.r0 + row0 + tid, static_cast<uint32_t>(a.n), a.cap, a.pos);
+      a.norms[row] = L.nrm[tid];
+      a.gammas[row] = static_cast<float>(__builtin_sqrt(L.nsq[tid]));
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// PolarQuant encode
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
+  __shared__ __attribute__((aligned(16))) RotqLds L;
+  double* sq = L.kt;   // tree sums of squares (two buffers in the key tile's LDS)
+  const int tid = threadIdx.x;
+  for (int e = tid; e < D * D / 4; e += NT)
+    reinterpret_cast<float4*>(L.rotT)[e] = reinterpret_cast<const float4*>(a.rotT)[e];
+  __syncthreads();
+  // bits per level: 4, then 2; thresholds per level: 3 (level 1), 3
+  constexpr int kBits[PQ_LEVELS] = {4, 2, 2, 2, 2, 2, 2};
+
+  for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int row0 = tile * TK;
+    const int nk = min(TK, a.R - row0);
+    rotate_tile(L, a, row0, nk);
+    // level 1: pair cells and the pairs' sums of squares
+    for (int e = tid; e < TK * (D / 2); e += NT) {
+      const int t = e / (D / 2), j = e % (D / 2);
+      const double av = static_cast<double>(L.y[t][2 * j]);
+      const double bv = static_cast<double>(L.y[t][2 * j + 1]);
+      int q;
+      double ap, bp;
+      if (bv > 0.0) {
+        q = av > 0.0 ? 0 : 1;
+      } else if (bv < 0.0) {
+        q = av < 0.0 ? 2 : 3;
+      } else {
+        q = av < 0.0 ? 2 : 0;
+      }
+      ap = q == 0 ? av : (q == 1 ? bv : (q == 2 ? -av : -bv));
+      bp = q == 0 ? bv : (q == 1 ? -av : (q == 2 ? -bv : av));
+      int within = 0;
+      for (int u = 0; u < (1 << kBits[0]) / 4 - 1; ++u) {
+        const double T = static_cast<double>(a.pq_thr[u]);
+        within += bp >= T * ap ? 1 : 0;
+      }
+      if (ap == 0.0 && bp == 0.0) within = 0;
+      L.cell[t][j] = static_cast<uint8_t>(q * ((1 << kBits[0]) / 4) + within);
+      sq[t * (D / 2) + j] = av * av + bv * bv;   // [t][pair]
+    }
+    __syncthreads();
+    // levels 2 .. 7: cells from the slice sums, then the pairwise sums
+    // (ping-pong between two halves of the key tile's LDS)
+    double* cur = sq;
+    double* nxt = sq + TK * (D / 2);
+    int width = D / 2;       // sums at the level below
+    int cell_off = D / 2;    // cells of level l follow those of lower levels
+    for (int lev = 2; lev <= PQ_LEVELS; ++lev) {
+      const int half = width / 2;
+      const int nthr = (1 << kBits[lev - 1]) - 1;
+      for (int e = tid; e < TK * half; e += NT) {
+        const int t = e / half, j = e % half;
+        const double sa = cur[t * width + 2 * j], sb = cur[t * width + 2 * j + 1];
+        int c = 0;
+        for (int u = 0; u < nthr; ++u) {
+          const double T = static_cast<double>(a.pq_thr[(lev - 1) * PQ_MAXT + u]);
+          c += sb >= (T * T) * sa ? 1 : 0;
+        }
+        L.cell[t][cell_off + j] = static_cast<uint8_t>(c);
+        nxt[t * half + j] = sa + sb;
+      }
+      __syncthreads();
+      double* tmp = cur;
+      cur = nxt;
+      nxt = tmp;
+      cell_off += half;
+      width = half;
+    }
+    // stream: level 1 cells (4 bits each), then 2-bit cells of levels 2..7
+    for (int e = tid; e < TK * PQ_WORDS; e += NT) {
+      const int t = e / PQ_WORDS, w = e % PQ_WORDS;
+      if (t >= nk) continue;
+      uint32_t word = 0;
+      for (int p = 0; p < 32; ++p) {
+        const int b = 32 * w + p;
+        uint32_t bit = 0;
+        if (b < (D / 2) * 4) {
+          bit = (static_cast<uint32_t>(L.cell[t][b / 4]) >> (b % 4)) & 1u;
+        } else if (b < (D / 2) * 4 + (D / 2 - 1) * 2) {
+          const int b2 = b - (D / 2) * 4;
+          bit = (static_cast<uint32_t>(L.cell[t][D / 2 + b2 / 2]) >> (b2 % 2)) & 1u;
+        }
+        word |= bit << p;
+      }
+      const int64_t row = dest_row(a.r0 + row0 + t, static_cast<uint32_t>(a.n), a.cap, a.pos);
+      a.pq_codes[row * PQ_WORDS + w] = word;
+    }
+    if (tid < nk) {
+      const int64_t row = dest_row(a.r0 + row0 + tid, static_cast<uint32_t>(a.n), a.cap, a.pos);
+      a.radii[row] = static_cast<float>(__builtin_sqrt(cur[tid]));
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// TurboQuant_prod scores: est_t = n_t (<Pi q, c[idx_t]> + sqrt(pi/2)/m g_t
+// <S^T Pi q, 2 bit_t - 1>) for every token t < N and query head
+// ---------------------------------------------------------------------------
+// A workgroup takes 256 tokens of one (batch, kv head); its prologue rotates
+// the G queries (fp32 FMAs), sketches them (S^T Pi q) and lays out, per head,
+// the products Pi q_i c_v for every coordinate and centroid; a thread then
+// scores one token with one LDS lookup per coordinate and one per sketch
+// coordinate.
+template <int G>
+__global__ __launch_bounds__(256) void tq_scores_kernel(
+    const float* __restrict__ q, const uint32_t* __restrict__ codes, const uint32_t* __restrict__ bits,
+    const float* __restrict__ norms, const float* __restrict__ gammas, const float* __restrict__ rot,
+    const uint16_t* __restrict__ s_il, const float* __restrict__ cents, int k, int H_kv, int N, int cap,
+    float coef, float* __restrict__ out) {
+  constexpr int CMAX = 8;
+  __shared__ float qs[G][D];            // q, then S^T Pi q
+  __shared__ float qr[G][D];            // Pi q
+  __shared__ float lut[G][D][CMAX];     // Pi q_i c_v
+  __shared__ float ssum[G];
+  const int tid = threadIdx.x;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = static_cast<int64_t>(b) * H_kv + kvh;
+  const int L2 = 1 << k;
+  for (int e = tid; e < G * D; e += 256) qs[e / D][e % D] = q[(bh * G) * D + e];
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, i = e % D;
+    float acc = 0.f;
+    for (int j = 0; j < D; ++j) acc = __builtin_fmaf(rot[i * D + j], qs[h][j], acc);
+    qr[h][i] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, l = e % D;
+    float acc = 0.f;
+    for (int i = 0; i < D; ++i)
+      acc = __builtin_fmaf(__uint_as_float(static_cast<uint32_t>(s_il[i * D + l]) << 16), qr[h][i], acc);
+    qs[h][l] = acc;
+  }
+  for (int e = tid; e < G * D * CMAX; e += 256) {
+    const int h = e / (D * CMAX), i = (e / CMAX) % D, v = e % CMAX;
+    lut[h][i][v] = v < L2 ? qr[h][i] * cents[v] : 0.f;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float s2 = 0.f;
+    for (int l = 0; l < D; ++l) s2 += qs[tid][l];
+    ssum[tid] = s2;
+  }
+  __syncthreads();
+  const int t = blockIdx.x * 256 + tid;
+  if (t >= N) return;
+  const int cw = D * k / 32;
+  const int64_t row = bh * cap + t;
+  uint32_t cwd[12], bw[4];
+  for (int w = 0; w < cw; ++w) cwd[w] = codes[row * cw + w];
+  for (int w = 0; w < 4; ++w) bw[w] = bits[row * 4 + w];
+  const float n = norms[row], g = gammas[row];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mse = 0.f;
+    for (int i = 0; i < D; ++i) {
+      const int bpos = i * k;
+      uint32_t idx = cwd[bpos >> 5] >> (bpos & 31);
+      if ((bpos & 31) + k > 32) idx |= cwd[(bpos >> 5) + 1] << (32 - (bpos & 31));
+      mse += lut[h][i][idx & (L2 - 1)];
+    }
+    float pos = 0.f;
+    for (int l = 0; l < D; ++l) pos += (bw[l >> 5] >> (l & 31)) & 1u ? qs[h][l] : 0.f;
+    out[((bh * G + h) * static_cast<int64_t>(N)) + t] = n * (mse + coef * g * (2.f * pos - ssum[h]));
+  }
+}
+
+}  // namespace
+
+int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys, int B, int H_kv, int n,
+                       uint32_t* codes, uint32_t* bits, float* norms, float* gammas, int cap, int pos,
+                       int margin_log2, void* stream) {
+  const int64_t R = static_cast<int64_t>(B) * H_kv * n;
+  if (R == 0) return hipSuccess;
+  RotqArgs a{};
+  a.keys = static_cast<const uint16_t*>(keys);
+  a.R = static_cast<int>(R);
+  a.n = n;
+  a.cap = cap;
+  a.pos = pos;
+  a.r0 = 0;
+  a.rotT = tb.rotT;
+  a.rot = tb.rot;
+  a.rot_row_max = tb.rot_row_max;
+  a.s_il = tb.s_il;
+  a.s_col_max = tb.s_col_max;
+  a.k = k;
+  a.cents = method == 0 ? tb.tq_cents + 8 * (k - 1) : nullptr;
+  a.pq_thr = tb.pq_thr;
+  a.margin_log2 = margin_log2;
+  if (method == 0) {
+    a.codes = codes;
+    a.bits = bits;
+    a.norms = norms;
+    a.gammas = gammas;
+  } else {
+    a.pq_codes = codes;
+    a.radii = norms;
+  }
+  const int tiles = static_cast<int>((R + TK - 1) / TK);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int grid = tiles < cus ? tiles : cus;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (method == 0) hipLaunchKernelGGL(tq_encode_kernel, dim3(grid), dim3(NT), 0, st, a, tiles);
+  else hipLaunchKernelGGL(pq_encode_kernel, dim3(grid), dim3(NT), 0, st, a, tiles);
+  return hipGetLastError();
+}
+
+int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t* codes,
+                     const uint32_t* bits, const float* norms, const float* gammas, int B, int H_q,
+                     int H_kv, int N, int cap, float* out, void* stream) {
+  const int G = H_q / H_kv;
+  // sqrt(pi/2) / m with m = d
+  const float coef = static_cast<float>(1.2533141373155002512 / D);
+  dim3 grid((N + 255) / 256, H_kv, B);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float* cents = tb.tq_cents + 8 * (k - 1);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(tq_scores_kernel<1>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
+    case 2: hipLaunchKernelGGL(tq_scores_kernel<2>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
+    case 4: hipLaunchKernelGGL(tq_scores_kernel<4>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
+    case 8: hipLaunchKernelGGL(tq_scores_kernel<8>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qjl

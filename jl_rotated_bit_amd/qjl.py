@@ -13,6 +13,8 @@ Names and semantics follow the C entry points:
 * ``decode_step(q, new_keys, new_values, signs, norms, values, pos, seed, m)`` -> qjl_decode_step
 * ``decode_attention_noalloc(q, signs, norms, values, N, seed, m, out)``  -> qjl_decode_attention_noalloc
 * ``baseline_decode_attention_bf16(q, keys, values, N)`` -> qjl_baseline_decode_attention_bf16
+* ``tq_encode_keys`` / ``tq_scores`` / ``pq_encode_keys`` -> qjl_tq_encode_keys / qjl_tq_scores /
+  qjl_pq_encode_keys; ``rotation_host`` / ``tq_codebook_host`` / ``pq_codebook_host``
 * ``decode_workspace_bytes`` / ``decode_num_splits`` / ``release_cache``
 * ``testing_set_encode_small_max`` -> qjl_testing_set_encode_small_max (a
   per-thread test hook, not part of the public header)
@@ -90,6 +92,17 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.qjl_baseline_decode_attention_bf16.argtypes = [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                                            c_int, c_int, ctypes.c_float, c_vp, c_vp,
                                                            c_sz, c_vp]
+        lib.qjl_tq_encode_keys.restype = c_int
+        lib.qjl_tq_encode_keys.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, c_u64, c_vp, c_vp,
+                                           c_vp, c_vp, c_int, c_int, c_vp]
+        lib.qjl_pq_encode_keys.restype = c_int
+        lib.qjl_pq_encode_keys.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_u64, c_vp, c_vp, c_int,
+                                           c_int, c_vp]
+        lib.qjl_tq_scores.restype = c_int
+        lib.qjl_tq_scores.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
+                                      c_int, c_int, c_u64, c_vp, c_vp]
+        lib.qjl_testing_set_rotq_margin.restype = c_int
+        lib.qjl_testing_set_rotq_margin.argtypes = [c_int]
         lib.qjl_release_cache.restype = c_int
         lib.qjl_release_cache.argtypes = []
         lib.qjl_testing_set_encode_small_max.restype = c_int
@@ -288,6 +301,56 @@ def baseline_decode_attention_bf16(q, keys, values, N: int, scale: float | None 
         0.0 if scale is None else float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), s.cuda_stream))
     return out
+
+
+def tq_encode_keys(keys, codes, bits, norms, gammas, pos: int, seed: int, k: int, stream=None):
+    """qjl_tq_encode_keys: keys [B][H_kv][n][d] bf16 bits -> rows [pos, pos + n)
+    of codes int32 [B][H_kv][cap][d k/32], bits int32 [B][H_kv][cap][d/32],
+    norms and gammas fp32 [B][H_kv][cap]."""
+    B, H, n, d = keys.shape
+    cap = norms.shape[2]
+    for t in (keys, codes, bits, norms, gammas):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if tuple(codes.shape) != (B, H, cap, d * k // 32) or tuple(bits.shape) != (B, H, cap, d // 32) \
+            or tuple(gammas.shape) != (B, H, cap):
+        raise ValueError("cache shapes do not match")
+    _check(load().qjl_tq_encode_keys(_ptr(keys), B, H, n, d, k, seed & (2 ** 64 - 1), _ptr(codes),
+                                     _ptr(bits), _ptr(norms), _ptr(gammas), cap, pos,
+                                     _stream_handle(stream)))
+
+
+def tq_scores(q, codes, bits, norms, gammas, N: int, seed: int, k: int, out=None, stream=None):
+    """qjl_tq_scores: estimated <q, k_t> -> fp32 [B][H_q][N]."""
+    import torch
+    B, H_q, d = q.shape
+    _, H_kv, cap = norms.shape
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp32 [B][H_q][d]")
+    s = _resolve_stream(stream)
+    if out is None:
+        with torch.cuda.stream(s):
+            out = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device)
+    _check(load().qjl_tq_scores(_ptr(q), _ptr(codes), _ptr(bits), _ptr(norms), _ptr(gammas), B, H_q,
+                                H_kv, N, cap, d, k, seed & (2 ** 64 - 1), _ptr(out), s.cuda_stream))
+    return out
+
+
+def pq_encode_keys(keys, codes, radii, pos: int, seed: int, stream=None):
+    """qjl_pq_encode_keys: keys [B][H_kv][n][d] -> rows [pos, pos + n) of codes
+    int32 [B][H_kv][cap][12] and radii fp32 [B][H_kv][cap]."""
+    B, H, n, d = keys.shape
+    cap = radii.shape[2]
+    if tuple(codes.shape) != (B, H, cap, 12):
+        raise ValueError("codes must be [B][H_kv][cap][12]")
+    _check(load().qjl_pq_encode_keys(_ptr(keys), B, H, n, d, seed & (2 ** 64 - 1), _ptr(codes),
+                                     _ptr(radii), cap, pos, _stream_handle(stream)))
+
+
+def testing_set_rotq_margin(log2_factor: int) -> int:
+    """Test hook (csrc/qjl_testing.h): widen the rotate-then-quantize
+    certificates of the calling thread by 2^log2_factor; returns the previous value."""
+    return load().qjl_testing_set_rotq_margin(log2_factor)
 
 
 def decode_attention_noalloc(q, signs, norms, values, N: int, seed: int, m: int, out,

@@ -35,7 +35,7 @@ def declared_functions(header=HEADER):
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     testing = declared_functions(TESTING_HEADER)
-    assert testing == ["qjl_testing_set_encode_small_max"]
+    assert testing == ["qjl_testing_set_encode_small_max", "qjl_testing_set_rotq_margin"]
     for name in names + testing:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", qjl.LIB_PATH], capture_output=True,
