@@ -29,7 +29,12 @@ other workload, each measured the same way in the same run:
                  head, then the decode over all tokens): per-step median,
                  total and HBM fraction;
 * ``mha16k``   - 40 heads, batch 8, 16384 tokens: decode time and HBM
-                 fraction (and the encode of its 5.2 M keys).
+                 fraction (and the encode of its 5.2 M keys);
+* ``rotq``     - TurboQuant_prod and PolarQuant encodes of the 32K workload's
+                 keys and TurboQuant scores over them.
+
+The headline also times the fused decode step (one launch that appends a
+token and decodes) and the uncompressed bf16-KV baseline at equal context.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -47,6 +52,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
+FP64_PEAK_TFLOPS = 78.6         # MI355X fp64 (vector and matrix)
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 SEED = 42
 RING_BYTES = 600 * 2 ** 20      # > 2 x 256 MB last-level cache, per timed loop
@@ -511,6 +517,73 @@ def bench_mha16k(qjl, w, args, T):
             "ring_sets": n_sets}
 
 
+def bench_rotq(qjl, w, args, T):
+    """TurboQuant_prod (k = 2: 3 bits per coordinate) and PolarQuant encodes of
+    the 32K GQA workload's keys, and TurboQuant scores of its 32 query heads
+    over them.  The encodes run their rotation (and TurboQuant's residual
+    sketch) in fp64, so they are priced against the fp64 peak; the scores
+    kernel reads 56 bytes per (token, kv head) and is bound by its LDS
+    lookups (reported against HBM for reference)."""
+    import torch
+    B, Hq, Hkv, N, d = w.B, w.H_q, w.H_kv, w.N, w.d
+    k = 2
+    R = B * Hkv * N
+    tq_bytes = R * (2 * d + d * k // 8 + d // 8 + 8)
+    n_sets = ring_sets(tq_bytes)
+    sets = []
+    for _ in range(n_sets):
+        sets.append(dict(
+            keys=dev(w.keys[:, :, :N]),
+            codes=torch.zeros((B, Hkv, N, d * k // 32), dtype=torch.int32, device="cuda"),
+            bits=torch.zeros((B, Hkv, N, d // 32), dtype=torch.int32, device="cuda"),
+            norms=torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda"),
+            gammas=torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda"),
+            pq=torch.zeros((B, Hkv, N, 12), dtype=torch.int32, device="cuda"),
+            radii=torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda"),
+            q=dev(w.q), scores=torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")))
+
+    def tq(i):
+        s = sets[i % n_sets]
+        qjl.tq_encode_keys(s["keys"], s["codes"], s["bits"], s["norms"], s["gammas"], 0, SEED, k)
+
+    def pq(i):
+        s = sets[i % n_sets]
+        qjl.pq_encode_keys(s["keys"], s["pq"], s["radii"], 0, SEED)
+
+    def sc(i):
+        s = sets[i % n_sets]
+        qjl.tq_scores(s["q"], s["codes"], s["bits"], s["norms"], s["gammas"], N, SEED, k, out=s["scores"])
+    for i in range(n_sets):
+        tq(i)
+        pq(i)
+        sc(i)
+    reps = max(4, args.steps // 2)
+    tq_ms = T.b2b(tq, reps)
+    pq_ms = T.b2b(pq, reps)
+    sc_ms = T.b2b(sc, reps)
+    log(f"[bench] rotq (32K GQA keys): TurboQuant encode {tq_ms * 1e3:.1f} us, PolarQuant encode "
+        f"{pq_ms * 1e3:.1f} us, TurboQuant scores {sc_ms * 1e3:.1f} us")
+    del sets
+    torch.cuda.empty_cache()
+    tq_flops = R * 2.0 * (2 * d * d)            # rotation + residual sketch (m = d)
+    pq_flops = R * 2.0 * d * d                  # rotation
+    sc_bytes = R * (d * k // 8 + d // 8 + 8) + B * Hq * N * 4
+    fp64 = lambda fl, ms: {"bound": "fp64", "achieved": round(fl / (ms / 1e3) / 1e12, 2),
+                           "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(fl / (ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS, 4),
+                           "flops_per_launch": int(fl)}
+    return {"workload": "the 262144 keys and 32 query heads of the 32K GQA workload; TurboQuant_prod at "
+                        "3 bits per coordinate (2-bit codes + 1-bit QJL of the residual), PolarQuant "
+                        "4/2-bit levels",
+            "tq_encode_us": round(tq_ms * 1e3, 3), "tq_encode_keys_per_s": round(R / (tq_ms / 1e3), 1),
+            "tq_encode_roofline": fp64(tq_flops, tq_ms),
+            "pq_encode_us": round(pq_ms * 1e3, 3), "pq_encode_keys_per_s": round(R / (pq_ms / 1e3), 1),
+            "pq_encode_roofline": fp64(pq_flops, pq_ms),
+            "tq_scores_us": round(sc_ms * 1e3, 3),
+            "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, None, "tq_scores_kernel", sc_bytes),
+            "ring_sets": n_sets}
+
+
 # ----------------------------------------------------------------------------
 # the oracle on the host (cpu_baseline)
 # ----------------------------------------------------------------------------
@@ -567,7 +640,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="all", choices=["all", *sorted(DESCRIPTIONS)],
+    ap.add_argument("--workload", default="all", choices=["all", "rotq", *sorted(DESCRIPTIONS)],
                     help="all (default): the gqa32k headline plus every other workload in `configs`; "
                          "a name: that workload alone (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -592,11 +665,11 @@ def main():
     T = Timer()
 
     runners = {"small": bench_small, "prefill": bench_prefill, "long64k": bench_long64k,
-               "mha16k": bench_mha16k}
+               "mha16k": bench_mha16k, "rotq": bench_rotq}
     if args.workload not in ("all", "gqa32k"):
         name = args.workload
         log(f"[bench] generating workload {name}")
-        res = runners[name](qjl, wl.WORKLOADS[name](), args, T)
+        res = runners[name](qjl, wl.WORKLOADS["gqa32k" if name == "rotq" else name](), args, T)
         if args.copy_calibration:
             a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
             b = torch.empty_like(a)
@@ -618,6 +691,7 @@ def main():
             log(f"[bench] {name} generated in {time.perf_counter() - t0:.1f} s")
             configs[name] = runners[name](qjl, wk, args, T)
             del wk
+        configs["rotq"] = bench_rotq(qjl, w, args, T)
     line = {
         "metric": METRIC,
         "value": head.pop("value"),

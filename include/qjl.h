@@ -131,8 +131,8 @@ QJL_API qjl_status qjl_pq_codebook_host(int32_t level, int32_t bits, float *cent
  *          of the row's bit stream (least significant bit first);
  *   bits   uint32 [B][H_kv][cap][d / 32] (as QJL sign words);
  *   norms, gammas fp32 [B][H_kv][cap].
- * keys_bf16 [B][H_kv][n][d]; d == 128; k in {1, 2, 3}; pointers 4-byte
- * aligned.  Other sizes as for qjl_encode_keys.  The first call for a seed
+ * keys_bf16 [B][H_kv][n][d], 16-byte aligned; d == 128; k in {1, 2, 3};
+ * the other pointers 4-byte aligned.  Other sizes as for qjl_encode_keys.  The first call for a seed
  * on a device uploads its tables (~100 KB).  Returns QJL_OK, QJL_EINVAL,
  * QJL_EUNSUPPORTED, QJL_ENOMEM or QJL_EHIP. */
 QJL_API qjl_status qjl_tq_encode_keys(const void *keys_bf16, int32_t B, int32_t H_kv, int32_t n,

@@ -542,8 +542,8 @@ QJL_API qjl_status qjl_tq_encode_keys(const void* keys_bf16, int32_t B, int32_t 
   if (st != QJL_OK || n == 0) return st;
   if (keys_bf16 == nullptr || codes == nullptr || bits == nullptr || norms == nullptr || gammas == nullptr)
     return fail(QJL_EINVAL, "%s: NULL pointer", fn);
-  if (!aligned(keys_bf16, 4) || !aligned(codes, 4) || !aligned(bits, 4) || !aligned(norms, 4) || !aligned(gammas, 4))
-    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+  if (!aligned(keys_bf16, 16) || !aligned(codes, 4) || !aligned(bits, 4) || !aligned(norms, 4) || !aligned(gammas, 4))
+    return fail(QJL_EINVAL, "%s: misaligned pointer (keys need 16 B, the rest 4 B)", fn);
   qjl::RotqTables tb;
   st = get_rotq(seed, &tb);
   if (st != QJL_OK) return st;
@@ -562,8 +562,8 @@ QJL_API qjl_status qjl_pq_encode_keys(const void* keys_bf16, int32_t B, int32_t 
   qjl_status st = check_rows(fn, B, H_kv, n, cap, pos);
   if (st != QJL_OK || n == 0) return st;
   if (keys_bf16 == nullptr || codes == nullptr || radii == nullptr) return fail(QJL_EINVAL, "%s: NULL pointer", fn);
-  if (!aligned(keys_bf16, 4) || !aligned(codes, 4) || !aligned(radii, 4))
-    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+  if (!aligned(keys_bf16, 16) || !aligned(codes, 4) || !aligned(radii, 4))
+    return fail(QJL_EINVAL, "%s: misaligned pointer (keys need 16 B, the rest 4 B)", fn);
   qjl::RotqTables tb;
   st = get_rotq(seed, &tb);
   if (st != QJL_OK) return st;

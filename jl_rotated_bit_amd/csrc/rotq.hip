@@ -51,7 +51,10 @@ namespace {
 
 constexpr int D = kHeadDim;      // 128
 constexpr int TK = 32;           // keys per tile
-constexpr int NT = 256;          // threads per workgroup
+constexpr int TKP = TK + 1;      // LDS row stride of the [channel][key] tile (odd: spreads banks)
+constexpr int NT = 512;          // threads per workgroup (two waves per SIMD)
+constexpr int NW = NT / 64;      // waves
+constexpr int CB = D / 16 / (NW / 2);  // 16-column result blocks per wave (2)
 constexpr int PQ_LEVELS = 7;     // log2(128)
 constexpr int PQ_WORDS = 12;     // 64 * 4 + 63 * 2 = 382 bits
 constexpr int PQ_MAXT = 8;       // thresholds per level (<= 2^3 - 1 or 2^bits/4 - 1)
@@ -149,68 +152,126 @@ __device__ __forceinline__ int64_t dest_row(uint32_t r, uint32_t un, int cap, in
 struct RotqLds {
   float rotT[D * D];               // 64 KB
   uint16_t s_il[D * D];            // 32 KB (TurboQuant)
-  double kt[D * TK];               // keys (then residuals), [j][t]: 32 KB
+  double kt[D * TKP];              // keys (then residuals), [j][t]: 33 KB
   float y[TK][D + 1];              // rotated keys
   double nsq[TK];                  // fp64 sums of squares
   float nrm[TK];
   uint8_t cell[TK][D];             // codes / level cells
   uint32_t qwords[TK][4];          // TurboQuant sign words
   uint32_t scratch[NT / 64][2 * ACC_WORDS];
+  float thr[PQ_LEVELS * PQ_MAXT];  // PolarQuant thresholds
 };
 
-// Stage A: y = RN32(exact Pi k) for the tile's keys (rows t < nk valid).
-__device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk) {
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// The tile's fp64 product on the matrix cores (v_mfma_f64_16x16x4_f64):
+// out[key][col] = sum_k x[k][key] col(k, col) over the d channels, for 32
+// keys x 128 columns.  Wave w takes keys 16 (w & 1) .. +15 and columns
+// 32 (w >> 1) .. +31 as two 16 x 16 blocks.  Operand lanes: A (16 keys x 4
+// channels) lane l = key l % 16, channel l / 16; B (4 channels x 16 columns)
+// lane l = channel l / 16, column l % 16.  Result: acc[c][r] of lane l is
+// key 16 (w & 1) + l / 16 + 4 r, column 16 (2 (w >> 1) + c) + l % 16 (the
+// result rows of this instruction are interleaved by register; the operand
+// and result layouts were checked on the GPU with a one-hot probe).
+// Each product of two values exact in fp64 (a bf16 key or an fp32 residual
+// times an fp32 rotation entry or a bf16 sketch entry) is exact; the sums
+// carry at most d roundings, whatever order the unit adds in.
+template <class Col>
+__device__ __forceinline__ void mfma_tile(const Col& col, const double* x, int wave, int lane,
+                                          f64x4_t (&acc)[CB]) {
+  const int kb = wave & 1, cg = wave >> 1;
+  const int lr = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < CB; ++c) acc[c] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int s = 0; s < D / 4; ++s) {
+    const int kk = 4 * s + lk;
+    const double av = x[kk * TKP + 16 * kb + lr];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, col(kk, 16 * (CB * cg + c) + lr), acc[c], 0, 0, 0);
+  }
+}
+
+// fp64 sum of squares of x[j][t] over j in order (the exact definition the
+// codes use), loads batched 16 at a time
+__device__ __forceinline__ double ordered_sumsq(const double* x, int t) {
+  double s = 0.0;
+  for (int j0 = 0; j0 < D; j0 += 16) {
+    double v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = x[(j0 + u) * TKP + t];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s = s + v[u] * v[u];
+  }
+  return s;
+}
+
+// A tile's keys: thread tid holds 16-byte chunks tid + NT r of the tile (row
+// = chunk / 16, channels 8 (chunk % 16) .. +7); rows past nk are 0.
+constexpr int KCH = TK * D / 8 / NT;   // chunks per thread (1)
+struct KeyRegs {
+  uint4 c[KCH];
+};
+__device__ __forceinline__ void load_key_regs(KeyRegs& kr, const RotqArgs& a, int row0, int nk) {
+#pragma unroll
+  for (int r = 0; r < KCH; ++r) {
+    const int e = threadIdx.x + NT * r;
+    const int t = e >> 4;
+    kr.c[r] = t < nk ? reinterpret_cast<const uint4*>(a.keys + static_cast<int64_t>(row0 + t) * D)[e & 15]
+                     : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Stage A: y = RN32(exact Pi k) for the tile's keys (rows t < nk valid), from
+// the keys already in kr.
+__device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk, const KeyRegs& kr) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  // keys -> LDS as fp64, transposed ([j][t]); missing rows are zero
-  for (int e = tid; e < TK * D / 2; e += NT) {
-    const int t = e / (D / 2), jp = e % (D / 2);
-    uint32_t pair = 0;
-    if (t < nk) pair = reinterpret_cast<const uint32_t*>(a.keys + static_cast<int64_t>(row0 + t) * D)[jp];
-    L.kt[(2 * jp) * TK + t] = static_cast<double>(__uint_as_float(pair << 16));
-    L.kt[(2 * jp + 1) * TK + t] = static_cast<double>(__uint_as_float(pair & 0xFFFF0000u));
+  // keys -> LDS as fp64, transposed ([j][t])
+#pragma unroll
+  for (int r = 0; r < KCH; ++r) {
+    const int e = tid + NT * r;
+    const int t = e >> 4, j0 = 8 * (e & 15);
+    const uint32_t w[4] = {kr.c[r].x, kr.c[r].y, kr.c[r].z, kr.c[r].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      L.kt[(j0 + 2 * q) * TKP + t] = static_cast<double>(__uint_as_float(w[q] << 16));
+      L.kt[(j0 + 2 * q + 1) * TKP + t] = static_cast<double>(__uint_as_float(w[q] & 0xFFFF0000u));
+    }
   }
   __syncthreads();
   // ||k||^2 in channel order (one thread per key)
   if (tid < TK) {
-    double s = 0.0;
-    for (int j = 0; j < D; ++j) {
-      const double v = L.kt[j * TK + tid];
-      s = s + v * v;
-    }
+    const double s = ordered_sumsq(L.kt, tid);
     L.nsq[tid] = s;
     L.nrm[tid] = static_cast<float>(__builtin_sqrt(s));
   }
-  // the fp64 product
-  const int i = tid & (D - 1), h = tid >> 7;
-  double acc[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) acc[u] = 0.0;
-#pragma unroll 4
-  for (int j = 0; j < D; ++j) {
-    const double p = static_cast<double>(L.rotT[j * D + i]);
-    const double2* kv = reinterpret_cast<const double2*>(&L.kt[j * TK + 16 * h]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const double2 k2 = kv[u];
-      acc[2 * u] = __builtin_fma(k2.x, p, acc[2 * u]);
-      acc[2 * u + 1] = __builtin_fma(k2.y, p, acc[2 * u + 1]);
-    }
-  }
+  // the fp64 product y = K Pi^T on the matrix cores
+  f64x4_t acc[CB];
+  mfma_tile([&](int j, int col) { return static_cast<double>(L.rotT[j * D + col]); }, L.kt, wave, lane, acc);
   __syncthreads();   // nsq ready
   // certify the fp32 rounding: |v - exact| <= 2 d 2^-53 ||k|| ||Pi_i||
   const double wide = __builtin_ldexp(1.0, a.margin_log2);
+  const int t_base = 16 * (wave & 1) + (lane >> 4);
+  const int i_base = 16 * CB * (wave >> 1) + (lane & 15);
   uint32_t open = 0;
+  double Er[4];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int t = 16 * h + u;
-    const double kn = __builtin_sqrt(L.nsq[t]) * (1.0 + 0x1.0p-40);
-    const double E = 2.0 * D * 0x1.0p-53 * kn * static_cast<double>(a.rot_row_max) * wide + 0x1.0p-1060;
-    const float lo = static_cast<float>(acc[u] - E);
-    const float hi = static_cast<float>(acc[u] + E);
-    L.y[t][i] = hi;
-    if (lo != hi && t < nk) open |= 1u << u;
-  }
+  for (int r = 0; r < 4; ++r)
+    Er[r] = 2.0 * D * 0x1.0p-53 * (__builtin_sqrt(L.nsq[t_base + 4 * r]) * (1.0 + 0x1.0p-40)) *
+                static_cast<double>(a.rot_row_max) * wide + 0x1.0p-1060;
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t_base + 4 * r, i = i_base + 16 * c;
+      const double E = Er[r];
+      const float lo = static_cast<float>(acc[c][r] - E);
+      const float hi = static_cast<float>(acc[c][r] + E);
+      L.y[t][i] = hi;
+      if (lo != hi && t < nk) open |= 1u << (4 * c + r);
+    }
   // exact sums for the uncertified values (about one in 10^5): the lanes
   // of a wave take turns with the wave's integer accumulator
   for (uint64_t any = __ballot(open != 0); any != 0; any = __ballot(open != 0)) {
@@ -219,7 +280,8 @@ __device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk) {
       uint32_t* pos = L.scratch[wave];
       uint32_t* neg = pos + ACC_WORDS;
       for (uint32_t o = open; o; o &= o - 1) {
-        const int t = 16 * h + __builtin_ctz(o);
+        const int u = __builtin_ctz(o);
+        const int t = t_base + 4 * (u & 3), i = i_base + 16 * (u >> 2);
         long_clear(pos);
         const uint16_t* krow = a.keys + static_cast<int64_t>(row0 + t) * D;
         for (int j = 0; j < D; ++j) add_product(pos, neg, krow[j], a.rot[i * D + j]);
@@ -250,14 +312,19 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
   const double wide = __builtin_ldexp(1.0, a.margin_log2);
   __syncthreads();
 
+  KeyRegs kr;
+  if (blockIdx.x < tiles) load_key_regs(kr, a, blockIdx.x * TK, min(TK, a.R - static_cast<int>(blockIdx.x) * TK));
   for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int row0 = tile * TK;
     const int nk = min(TK, a.R - row0);
-    rotate_tile(L, a, row0, nk);
+    rotate_tile(L, a, row0, nk, kr);
+    // the next tile's keys load while this one is encoded
+    const int next = tile + gridDim.x;
+    if (next < tiles) load_key_regs(kr, a, next * TK, min(TK, a.R - next * TK));
     // u, codes, residual (thread per (coordinate, key half))
-    const int i = tid & (D - 1), h = tid >> 7;
-    for (int u8 = 0; u8 < 16; ++u8) {
-      const int t = 16 * h + u8;
+    const int i = tid & (D - 1), h = tid >> 7;   // h < NT / D
+    for (int u8 = 0; u8 < TK * D / NT; ++u8) {
+      const int t = (TK * D / NT) * h + u8;
       const float n = L.nrm[t];
       const float u = n > 0.f ? L.y[t][i] / n : 0.f;
       int idx = 0;
@@ -272,42 +339,29 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
     // residuals -> fp64 [i][t]; g in coordinate order
     for (int e = tid; e < TK * D; e += NT) {
       const int t = e / D, ii = e % D;
-      L.kt[ii * TK + t] = static_cast<double>(L.y[t][ii]);
+      L.kt[ii * TKP + t] = static_cast<double>(L.y[t][ii]);
     }
     __syncthreads();
-    if (tid < TK) {
-      double s = 0.0;
-      for (int ii = 0; ii < D; ++ii) {
-        const double v = L.kt[ii * TK + tid];
-        s = s + v * v;
-      }
-      L.nsq[tid] = s;
-    }
-    // z = S^T r (thread per (sketch row l, key half))
-    const int l = i;
-    double acc[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) acc[u] = 0.0;
-#pragma unroll 4
-    for (int ii = 0; ii < D; ++ii) {
-      const double s = static_cast<double>(__uint_as_float(static_cast<uint32_t>(L.s_il[ii * D + l]) << 16));
-      const double2* rv = reinterpret_cast<const double2*>(&L.kt[ii * TK + 16 * h]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const double2 r2 = rv[u];
-        acc[2 * u] = __builtin_fma(r2.x, s, acc[2 * u]);
-        acc[2 * u + 1] = __builtin_fma(r2.y, s, acc[2 * u + 1]);
-      }
-    }
+    if (tid < TK) L.nsq[tid] = ordered_sumsq(L.kt, tid);
+    // z = S^T r on the matrix cores (columns = sketch coordinates)
+    f64x4_t acc[CB];
+    mfma_tile([&](int ii, int col) {
+      return static_cast<double>(__uint_as_float(static_cast<uint32_t>(L.s_il[ii * D + col]) << 16));
+    }, L.kt, wave, lane, acc);
     __syncthreads();   // nsq (residual) ready
+    const int t_base = 16 * (wave & 1) + (lane >> 4);
+    const int l_base = 16 * CB * (wave >> 1) + (lane & 15);
     uint32_t open = 0;
+    double Er[4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int t = 16 * h + u;
-      const double rn = __builtin_sqrt(L.nsq[t]) * (1.0 + 0x1.0p-40);
-      const double E = 2.0 * D * 0x1.0p-53 * rn * static_cast<double>(a.s_col_max) * wide + 0x1.0p-1060;
-      if (!(__builtin_fabs(acc[u]) > E) && t < nk) open |= 1u << u;
-    }
+    for (int r = 0; r < 4; ++r)
+      Er[r] = 2.0 * D * 0x1.0p-53 * (__builtin_sqrt(L.nsq[t_base + 4 * r]) * (1.0 + 0x1.0p-40)) *
+                  static_cast<double>(a.s_col_max) * wide + 0x1.0p-1060;
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!(__builtin_fabs(acc[c][r]) > Er[r]) && t_base + 4 * r < nk) open |= 1u << (4 * c + r);
     // exact signs for the uncertified sums (rare): lanes take turns with the
     // wave's integer accumulator
     for (uint64_t any = __ballot(open != 0); any != 0; any = __ballot(open != 0)) {
@@ -317,24 +371,28 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
         uint32_t* neg = pos + ACC_WORDS;
         for (uint32_t o = open; o; o &= o - 1) {
           const int u = __builtin_ctz(o);
-          const int t = 16 * h + u;
+          const int t = t_base + 4 * (u & 3), lc = l_base + 16 * (u >> 2);
           long_clear(pos);
-          for (int ii = 0; ii < D; ++ii) add_product(pos, neg, L.s_il[ii * D + l], L.y[t][ii]);
-          acc[u] = long_sign(pos, neg) ? 1.0 : -1.0;
+          for (int ii = 0; ii < D; ++ii) add_product(pos, neg, L.s_il[ii * D + lc], L.y[t][ii]);
+          acc[u >> 2][u & 3] = long_sign(pos, neg) ? 1.0 : -1.0;
         }
         open = 0;
       }
     }
-    // sign words: wave (l / 64, h) holds coordinates 64 (wave & 1) .. +63
+    // sign words: ballot bit l of register (c, r) is key 16 (wave & 1) +
+    // l / 16 + 4 r, coordinate 16 (CB (wave >> 1) + c) + l % 16; each 16-lane
+    // group fills one half-word of its key's row
+    uint16_t* qh = reinterpret_cast<uint16_t*>(&L.qwords[0][0]);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint64_t m = __ballot(acc[u] >= 0.0);
-      if (lane == 0) {
-        const int t = 16 * h + u;
-        L.qwords[t][2 * (wave & 1)] = static_cast<uint32_t>(m);
-        L.qwords[t][2 * (wave & 1) + 1] = static_cast<uint32_t>(m >> 32);
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint64_t m = __ballot(acc[c][r] >= 0.0);
+        if (lane < 4) {
+          const int t = 16 * (wave & 1) + lane + 4 * r;
+          qh[t * 8 + CB * (wave >> 1) + c] = static_cast<uint16_t>(m >> (16 * lane));
+        }
       }
-    }
     __syncthreads();
     // stores: codes (bit stream, k bits per coordinate), sign words, n, g
     const int cw = D * K / 32;
@@ -344,9 +402,18 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
       const int64_t row = dest_row(a.r0 + row0 + t, static_cast<uint32_t>(a.n), a.cap, a.pos);
       if (w < cw) {
         uint32_t word = 0;
-        for (int p = 0; p < 32; ++p) {
-          const int b = 32 * w + p;
-          word |= ((static_cast<uint32_t>(L.cell[t][b / K]) >> (b % K)) & 1u) << p;
+        if (K == 2) {   // coordinates 16 w .. 16 w + 15, two bits each
+          const uint4 c4 = *reinterpret_cast<const uint4*>(&L.cell[t][16 * w]);
+          const uint32_t cb[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) word |= ((cb[q] >> (8 * bb)) & 3u) << (2 * (4 * q + bb));
+        } else {
+          for (int p = 0; p < 32; ++p) {
+            const int b = 32 * w + p;
+            word |= ((static_cast<uint32_t>(L.cell[t][b / K]) >> (b % K)) & 1u) << p;
+          }
         }
         a.codes[row * cw + w] = word;
       } else {
@@ -371,14 +438,19 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
   const int tid = threadIdx.x;
   for (int e = tid; e < D * D / 4; e += NT)
     reinterpret_cast<float4*>(L.rotT)[e] = reinterpret_cast<const float4*>(a.rotT)[e];
+  if (tid < PQ_LEVELS * PQ_MAXT) L.thr[tid] = a.pq_thr[tid];
   __syncthreads();
   // bits per level: 4, then 2; thresholds per level: 3 (level 1), 3
   constexpr int kBits[PQ_LEVELS] = {4, 2, 2, 2, 2, 2, 2};
 
+  KeyRegs kr;
+  if (blockIdx.x < tiles) load_key_regs(kr, a, blockIdx.x * TK, min(TK, a.R - static_cast<int>(blockIdx.x) * TK));
   for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int row0 = tile * TK;
     const int nk = min(TK, a.R - row0);
-    rotate_tile(L, a, row0, nk);
+    rotate_tile(L, a, row0, nk, kr);
+    const int next = tile + gridDim.x;
+    if (next < tiles) load_key_regs(kr, a, next * TK, min(TK, a.R - next * TK));
     // level 1: pair cells and the pairs' sums of squares
     for (int e = tid; e < TK * (D / 2); e += NT) {
       const int t = e / (D / 2), j = e % (D / 2);
@@ -397,7 +469,7 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
       bp = q == 0 ? bv : (q == 1 ? -av : (q == 2 ? -bv : av));
       int within = 0;
       for (int u = 0; u < (1 << kBits[0]) / 4 - 1; ++u) {
-        const double T = static_cast<double>(a.pq_thr[u]);
+        const double T = static_cast<double>(L.thr[u]);
         within += bp >= T * ap ? 1 : 0;
       }
       if (ap == 0.0 && bp == 0.0) within = 0;
@@ -419,7 +491,7 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
         const double sa = cur[t * width + 2 * j], sb = cur[t * width + 2 * j + 1];
         int c = 0;
         for (int u = 0; u < nthr; ++u) {
-          const double T = static_cast<double>(a.pq_thr[(lev - 1) * PQ_MAXT + u]);
+          const double T = static_cast<double>(L.thr[(lev - 1) * PQ_MAXT + u]);
           c += sb >= (T * T) * sa ? 1 : 0;
         }
         L.cell[t][cell_off + j] = static_cast<uint8_t>(c);
@@ -436,17 +508,25 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
     for (int e = tid; e < TK * PQ_WORDS; e += NT) {
       const int t = e / PQ_WORDS, w = e % PQ_WORDS;
       if (t >= nk) continue;
+      // words 0..7: eight 4-bit level-1 cells each; words 8..11: sixteen
+      // 2-bit cells of levels 2..7 each (cell 127 does not exist: its bits,
+      // the top two of word 11, stay zero)
       uint32_t word = 0;
-      for (int p = 0; p < 32; ++p) {
-        const int b = 32 * w + p;
-        uint32_t bit = 0;
-        if (b < (D / 2) * 4) {
-          bit = (static_cast<uint32_t>(L.cell[t][b / 4]) >> (b % 4)) & 1u;
-        } else if (b < (D / 2) * 4 + (D / 2 - 1) * 2) {
-          const int b2 = b - (D / 2) * 4;
-          bit = (static_cast<uint32_t>(L.cell[t][D / 2 + b2 / 2]) >> (b2 % 2)) & 1u;
-        }
-        word |= bit << p;
+      if (w < 8) {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(&L.cell[t][8 * w]);
+        const uint32_t cb[2] = {c8.x, c8.y};
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) word |= ((cb[q] >> (8 * bb)) & 15u) << (4 * (4 * q + bb));
+      } else {
+        const uint4 c16 = *reinterpret_cast<const uint4*>(&L.cell[t][D / 2 + 16 * (w - 8)]);
+        const uint32_t cb[4] = {c16.x, c16.y, c16.z, c16.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) word |= ((cb[q] >> (8 * bb)) & 3u) << (2 * (4 * q + bb));
+        if (w == PQ_WORDS - 1) word &= 0x3FFFFFFFu;
       }
       const int64_t row = dest_row(a.r0 + row0 + t, static_cast<uint32_t>(a.n), a.cap, a.pos);
       a.pq_codes[row * PQ_WORDS + w] = word;
@@ -464,25 +544,32 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
 // <S^T Pi q, 2 bit_t - 1>) for every token t < N and query head
 // ---------------------------------------------------------------------------
 // A workgroup takes 256 tokens of one (batch, kv head); its prologue rotates
-// the G queries (fp32 FMAs), sketches them (S^T Pi q) and lays out, per head,
-// the products Pi q_i c_v for every coordinate and centroid; a thread then
-// scores one token with one LDS lookup per coordinate and one per sketch
-// coordinate.
-template <int G>
+// the G queries (fp32 FMAs), sketches them (S^T Pi q) and builds, per head,
+// nibble tables in LDS: for the sign words, the sum of S^T Pi q over the set
+// bits of every 4-bit group; for the codes, <Pi q, c[idx]> over the
+// coordinates of a 4-bit group (4 coordinates at k = 1, 2 at k = 2; at k = 3
+// one table row per coordinate).  A thread then scores one token with one
+// LDS lookup per nibble (32 + 64 at k = 2).
+template <int G, int K>
 __global__ __launch_bounds__(256) void tq_scores_kernel(
     const float* __restrict__ q, const uint32_t* __restrict__ codes, const uint32_t* __restrict__ bits,
     const float* __restrict__ norms, const float* __restrict__ gammas, const float* __restrict__ rot,
-    const uint16_t* __restrict__ s_il, const float* __restrict__ cents, int k, int H_kv, int N, int cap,
+    const uint16_t* __restrict__ s_il, const float* __restrict__ cents, int H_kv, int N, int cap,
     float coef, float* __restrict__ out) {
-  constexpr int CMAX = 8;
+  constexpr int CW = D * K / 32;                       // code words per token
+  constexpr int CROWS = K == 3 ? D : D * K / 4;        // code-table rows
+  constexpr int CCOLS = K == 3 ? 8 : 16;
   __shared__ float qs[G][D];            // q, then S^T Pi q
   __shared__ float qr[G][D];            // Pi q
-  __shared__ float lut[G][D][CMAX];     // Pi q_i c_v
+  __shared__ float lb[G][D / 4][16];    // sign-word nibbles
+  __shared__ float lc[G][CROWS][CCOLS]; // code nibbles
   __shared__ float ssum[G];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int64_t bh = static_cast<int64_t>(b) * H_kv + kvh;
-  const int L2 = 1 << k;
+  float c[1 << K];
+#pragma unroll
+  for (int v = 0; v < (1 << K); ++v) c[v] = cents[v];
   for (int e = tid; e < G * D; e += 256) qs[e / D][e % D] = q[(bh * G) * D + e];
   __syncthreads();
   for (int e = tid; e < G * D; e += 256) {
@@ -499,11 +586,28 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
       acc = __builtin_fmaf(__uint_as_float(static_cast<uint32_t>(s_il[i * D + l]) << 16), qr[h][i], acc);
     qs[h][l] = acc;
   }
-  for (int e = tid; e < G * D * CMAX; e += 256) {
-    const int h = e / (D * CMAX), i = (e / CMAX) % D, v = e % CMAX;
-    lut[h][i][v] = v < L2 ? qr[h][i] * cents[v] : 0.f;
-  }
   __syncthreads();
+  for (int e = tid; e < G * (D / 4) * 16; e += 256) {
+    const int h = e / (D * 4), g4 = (e / 16) % (D / 4), nib = e % 16;
+    float v = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) v += (nib >> bb) & 1 ? qs[h][4 * g4 + bb] : 0.f;
+    lb[h][g4][nib] = v;
+  }
+  for (int e = tid; e < G * CROWS * CCOLS; e += 256) {
+    const int h = e / (CROWS * CCOLS), row = (e / CCOLS) % CROWS, col = e % CCOLS;
+    float v;
+    if constexpr (K == 1) {
+      v = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) v += qr[h][4 * row + bb] * c[(col >> bb) & 1];
+    } else if constexpr (K == 2) {
+      v = qr[h][2 * row] * c[col & 3] + qr[h][2 * row + 1] * c[col >> 2];
+    } else {
+      v = qr[h][row] * c[col];
+    }
+    lc[h][row][col] = v;
+  }
   if (tid < G) {
     float s2 = 0.f;
     for (int l = 0; l < D; ++l) s2 += qs[tid][l];
@@ -512,23 +616,31 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
   __syncthreads();
   const int t = blockIdx.x * 256 + tid;
   if (t >= N) return;
-  const int cw = D * k / 32;
   const int64_t row = bh * cap + t;
-  uint32_t cwd[12], bw[4];
-  for (int w = 0; w < cw; ++w) cwd[w] = codes[row * cw + w];
+  uint32_t cwd[CW], bw[4];
+#pragma unroll
+  for (int w = 0; w < CW; ++w) cwd[w] = codes[row * CW + w];
+#pragma unroll
   for (int w = 0; w < 4; ++w) bw[w] = bits[row * 4 + w];
   const float n = norms[row], g = gammas[row];
-#pragma unroll
+#pragma unroll 1
   for (int h = 0; h < G; ++h) {
     float mse = 0.f;
-    for (int i = 0; i < D; ++i) {
-      const int bpos = i * k;
-      uint32_t idx = cwd[bpos >> 5] >> (bpos & 31);
-      if ((bpos & 31) + k > 32) idx |= cwd[(bpos >> 5) + 1] << (32 - (bpos & 31));
-      mse += lut[h][i][idx & (L2 - 1)];
+    if constexpr (K == 3) {
+#pragma unroll 8
+      for (int i = 0; i < D; ++i) {
+        const int bpos = 3 * i;
+        uint32_t idx = cwd[bpos >> 5] >> (bpos & 31);
+        if ((bpos & 31) > 29) idx |= cwd[(bpos >> 5) + 1] << (32 - (bpos & 31));
+        mse += lc[h][i][idx & 7];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < CROWS; ++r) mse += lc[h][r][(cwd[r >> 3] >> (4 * (r & 7))) & 15];
     }
     float pos = 0.f;
-    for (int l = 0; l < D; ++l) pos += (bw[l >> 5] >> (l & 31)) & 1u ? qs[h][l] : 0.f;
+#pragma unroll
+    for (int r = 0; r < D / 4; ++r) pos += lb[h][r][(bw[r >> 3] >> (4 * (r & 7))) & 15];
     out[((bh * G + h) * static_cast<int64_t>(N)) + t] = n * (mse + coef * g * (2.f * pos - ssum[h]));
   }
 }
@@ -584,13 +696,25 @@ int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t
   dim3 grid((N + 255) / 256, H_kv, B);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float* cents = tb.tq_cents + 8 * (k - 1);
+#define QJL_TQ_SCORES(GG, KK)                                                                     \
+  hipLaunchKernelGGL((tq_scores_kernel<GG, KK>), grid, dim3(256), 0, st, q, codes, bits, norms, gammas, \
+                     tb.rot, tb.s_il, cents, H_kv, N, cap, coef, out)
+#define QJL_TQ_SCORES_K(GG)            \
+  switch (k) {                         \
+    case 1: QJL_TQ_SCORES(GG, 1); break; \
+    case 2: QJL_TQ_SCORES(GG, 2); break; \
+    case 3: QJL_TQ_SCORES(GG, 3); break; \
+    default: return hipErrorInvalidValue; \
+  }
   switch (G) {
-    case 1: hipLaunchKernelGGL(tq_scores_kernel<1>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
-    case 2: hipLaunchKernelGGL(tq_scores_kernel<2>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
-    case 4: hipLaunchKernelGGL(tq_scores_kernel<4>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
-    case 8: hipLaunchKernelGGL(tq_scores_kernel<8>, grid, dim3(256), 0, st, q, codes, bits, norms, gammas, tb.rot, tb.s_il, cents, k, H_kv, N, cap, coef, out); break;
+    case 1: QJL_TQ_SCORES_K(1); break;
+    case 2: QJL_TQ_SCORES_K(2); break;
+    case 4: QJL_TQ_SCORES_K(4); break;
+    case 8: QJL_TQ_SCORES_K(8); break;
     default: return hipErrorInvalidValue;
   }
+#undef QJL_TQ_SCORES_K
+#undef QJL_TQ_SCORES
   return hipGetLastError();
 }
 

@@ -291,3 +291,47 @@ def test_host_table_errors(lib):
     assert lib.qjl_tq_codebook_host(128, 5, buf.ctypes.data) == EINVAL
     assert lib.qjl_pq_codebook_host(1, 1, buf.ctypes.data, buf.ctypes.data) == EINVAL
     assert lib.qjl_pq_codebook_host(0, 2, buf.ctypes.data, buf.ctypes.data) == EINVAL
+
+
+def tqe(lib, keys=A16, B=1, H=1, n=4, d=128, k=2, codes=A16, bits=A16, norms=A16, gammas=A16, cap=8, pos=0):
+    return lib.qjl_tq_encode_keys(keys, B, H, n, d, k, 7, codes, bits, norms, gammas, cap, pos, None)
+
+
+def pqe(lib, keys=A16, B=1, H=1, n=4, d=128, codes=A16, radii=A16, cap=8, pos=0):
+    return lib.qjl_pq_encode_keys(keys, B, H, n, d, 7, codes, radii, cap, pos, None)
+
+
+def tqs(lib, q=A16, codes=A16, bits=A16, norms=A16, gammas=A16, B=1, Hq=4, Hkv=1, N=8, cap=8, d=128, k=2,
+        out=A16):
+    return lib.qjl_tq_scores(q, codes, bits, norms, gammas, B, Hq, Hkv, N, cap, d, k, 7, out, None)
+
+
+def test_rotq_entry_point_validation(lib):
+    """Argument errors of the rotate-then-quantize entry points are caught on
+    the host, before any table upload or launch."""
+    assert tqe(lib, d=64) == EUNSUP
+    assert tqe(lib, k=0) == EUNSUP and tqe(lib, k=4) == EUNSUP
+    assert tqe(lib, B=0) == EINVAL
+    assert tqe(lib, n=5, pos=4, cap=8) == EINVAL
+    assert "exceeds cap" in qjl.last_error()
+    for name in ("keys", "codes", "bits", "norms", "gammas"):
+        assert tqe(lib, **{name: None}) == EINVAL, name
+    assert tqe(lib, keys=A16 + 4) == EINVAL            # keys need 16 B
+    assert "misaligned" in qjl.last_error()
+    assert tqe(lib, gammas=A16 + 2) == EINVAL
+    assert tqe(lib, n=0, keys=None, codes=None, bits=None, norms=None, gammas=None) == 0
+    assert pqe(lib, d=256) == EUNSUP
+    assert pqe(lib, pos=-1) == EINVAL
+    for name in ("keys", "codes", "radii"):
+        assert pqe(lib, **{name: None}) == EINVAL, name
+    assert pqe(lib, keys=A16 + 8) == EINVAL
+    assert pqe(lib, radii=A16 + 1) == EINVAL
+    assert pqe(lib, n=0, keys=None, codes=None, radii=None) == 0
+    assert tqs(lib, k=5) == EUNSUP
+    assert tqs(lib, Hq=6, Hkv=2) == EUNSUP             # G = 3
+    assert tqs(lib, Hq=6, Hkv=4) == EINVAL             # not a multiple
+    assert tqs(lib, N=0) == EINVAL and tqs(lib, N=9, cap=8) == EINVAL
+    for name in ("q", "codes", "bits", "norms", "gammas", "out"):
+        assert tqs(lib, **{name: None}) == EINVAL, name
+    assert tqs(lib, out=A16 + 2) == EINVAL
+    assert "misaligned" in qjl.last_error()
