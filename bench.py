@@ -128,6 +128,10 @@ def roofline(achieved_gbs, traffic, kernel, alg_bytes):
             "kernel": kernel, "algorithmic_bytes_per_launch": int(alg_bytes)}
 
 
+# GPU clock cycles of hold per queued call (~150 us at 2.4 GHz)
+HOLD_CYCLES_PER_CALL = 360_000
+
+
 class Timer:
     """HIP events on the launch stream (torch's current stream, which is
     the stream every call below is issued on)."""
@@ -138,16 +142,32 @@ class Timer:
         self.stream = torch.cuda.current_stream()
 
     def b2b(self, fn, reps):
-        """fn(i) for i < reps issued back to back between two events; ms per call."""
+        """fn(i) for i < reps issued back to back between two events; ms per call.
+
+        A spin kernel queued ahead of the first event holds the GPU while the
+        host issues the reps calls (Python and ctypes take ~10-30 us a call),
+        so the events time the kernels back to back, not the launch rate; the
+        host's issue time is compared with the hold and a shortfall logged.
+        """
+        import time
         torch = self.torch
         torch.cuda.synchronize()
+        h0 = torch.cuda.Event(enable_timing=True)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        h0.record(self.stream)
+        torch.cuda._sleep(int(reps * HOLD_CYCLES_PER_CALL))
         e0.record(self.stream)
+        t0 = time.perf_counter()
         for i in range(reps):
             fn(i)
+        host_ms = (time.perf_counter() - t0) * 1e3
         e1.record(self.stream)
         torch.cuda.synchronize()
+        hold_ms = h0.elapsed_time(e0)
+        if host_ms > hold_ms:
+            log(f"[bench] note: host issue {host_ms:.2f} ms outlasted the {hold_ms:.2f} ms hold "
+                f"(the timing below is partly launch-bound)")
         return e0.elapsed_time(e1) / reps
 
     def each(self, fn, reps):
@@ -580,7 +600,7 @@ def bench_rotq(qjl, w, args, T):
             "pq_encode_us": round(pq_ms * 1e3, 3), "pq_encode_keys_per_s": round(R / (pq_ms / 1e3), 1),
             "pq_encode_roofline": fp64(pq_flops, pq_ms),
             "tq_scores_us": round(sc_ms * 1e3, 3),
-            "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, None, "tq_scores_kernel", sc_bytes),
+            "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, None, "tq_query_kernel + tq_scores_kernel", sc_bytes),
             "ring_sets": n_sets}
 
 

@@ -140,20 +140,30 @@ QJL_API qjl_status qjl_tq_encode_keys(const void *keys_bf16, int32_t B, int32_t 
                                       uint32_t *bits, float *norms, float *gammas, int32_t cap,
                                       int32_t pos, void *stream);
 
+/* Workspace bytes of qjl_tq_scores: the prepared queries (Pi q and
+ * S^T Pi q, fp32) of the B * H_q heads.  0 for invalid sizes.  Pure host
+ * code. */
+QJL_API size_t qjl_tq_scores_workspace_bytes(int32_t B, int32_t H_q, int32_t d);
+
 /* TurboQuant_prod scores: the estimate of <q, k_t> for every query head and
  * cached token t < N (same section: the reconstruction's inner product plus
  * the QJL estimate of the residual's, unbiased):
  *   scores[b][h][t] = norm_t (<Pi q, c[idx_t]> + sqrt(pi/2)/d gamma_t
  *                     <S^T Pi q, 2 bit_t - 1>),  kv head h / (H_q / H_kv).
  * q fp32 [B][H_q][d]; caches as written by qjl_tq_encode_keys (same k,
- * seed); scores fp32 [B][H_q][N].  G = H_q / H_kv in {1, 2, 4, 8};
- * 1 <= N <= cap.  fp32 arithmetic (relative error ~1e-6 of the score
- * scale).  Returns QJL_OK, QJL_EINVAL, QJL_EUNSUPPORTED, QJL_ENOMEM or
- * QJL_EHIP. */
+ * seed), codes and bits 16-byte aligned, the rest 4-byte aligned; scores
+ * fp32 [B][H_q][N].  G = H_q / H_kv in {1, 2, 4, 8}; 1 <= N <= cap;
+ * B, H_kv <= 65535.  workspace: device, 256-byte aligned, at least
+ * qjl_tq_scores_workspace_bytes(B, H_q, d) bytes; its contents are
+ * overwritten (no zero-fill needed, and a workspace shared with
+ * qjl_decode_attention must be zero-filled again before that call).  fp32
+ * arithmetic (relative error ~1e-6 of the score scale).  Returns QJL_OK,
+ * QJL_EINVAL, QJL_EWORKSPACE, QJL_EUNSUPPORTED, QJL_ENOMEM or QJL_EHIP. */
 QJL_API qjl_status qjl_tq_scores(const float *q, const uint32_t *codes, const uint32_t *bits,
                                  const float *norms, const float *gammas, int32_t B, int32_t H_q,
                                  int32_t H_kv, int32_t N, int32_t cap, int32_t d, int32_t k,
-                                 uint64_t seed, float *scores, void *stream);
+                                 uint64_t seed, float *scores, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /* PolarQuant encode ("The Geometry of Forgetting", section "PolarQuant:
  * skipping Cartesian altogether"): the rotated key y (as for

@@ -117,8 +117,10 @@ constexpr int kPqBits[7] = {4, 2, 2, 2, 2, 2, 2};   // PolarQuant bits per level
 int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys, int B, int H_kv, int n,
                        uint32_t* codes, uint32_t* bits, float* norms, float* gammas, int cap, int pos,
                        int margin_log2, void* stream);
+// the scores' workspace: the prepared queries (Pi q, S^T Pi q), fp32
+size_t tq_scores_workspace_bytes(int B, int H_q);
 int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t* codes,
                      const uint32_t* bits, const float* norms, const float* gammas, int B, int H_q,
-                     int H_kv, int N, int cap, float* out, void* stream);
+                     int H_kv, int N, int cap, float* out, void* workspace, void* stream);
 
 }  // namespace qjl

@@ -32,7 +32,7 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 thread_local std::string g_last_error;
 
@@ -573,10 +573,16 @@ QJL_API qjl_status qjl_pq_encode_keys(const void* keys_bf16, int32_t B, int32_t 
   return QJL_OK;
 }
 
+QJL_API size_t qjl_tq_scores_workspace_bytes(int32_t B, int32_t H_q, int32_t d) {
+  if (B <= 0 || H_q <= 0 || d != qjl::kHeadDim) return 0;
+  return qjl::tq_scores_workspace_bytes(B, H_q);
+}
+
 QJL_API qjl_status qjl_tq_scores(const float* q, const uint32_t* codes, const uint32_t* bits,
                                  const float* norms, const float* gammas, int32_t B, int32_t H_q,
                                  int32_t H_kv, int32_t N, int32_t cap, int32_t d, int32_t k,
-                                 uint64_t seed, float* scores, void* stream) {
+                                 uint64_t seed, float* scores, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   const char* fn = "qjl_tq_scores";
   g_last_error.clear();
   if (d != qjl::kHeadDim || k < 1 || k > 3)
@@ -589,15 +595,22 @@ QJL_API qjl_status qjl_tq_scores(const float* q, const uint32_t* codes, const ui
     return fail(QJL_EUNSUPPORTED, "%s: G=H_q/H_kv=%d unsupported (1, 2, 4, 8)", fn, G);
   if (static_cast<int64_t>(B) * H_kv * cap > (int64_t{1} << 40)) return fail(QJL_EINVAL, "%s: cache too large", fn);
   if (static_cast<int64_t>(B) * H_q * N > (int64_t{1} << 40)) return fail(QJL_EINVAL, "%s: output too large", fn);
+  if (B > 65535 || H_kv > 65535) return fail(QJL_EINVAL, "%s: B=%d or H_kv=%d above 65535", fn, B, H_kv);
   if (q == nullptr || codes == nullptr || bits == nullptr || norms == nullptr || gammas == nullptr || scores == nullptr)
     return fail(QJL_EINVAL, "%s: NULL pointer", fn);
-  if (!aligned(q, 4) || !aligned(codes, 4) || !aligned(bits, 4) || !aligned(norms, 4) || !aligned(gammas, 4) ||
+  if (!aligned(q, 4) || !aligned(codes, 16) || !aligned(bits, 16) || !aligned(norms, 4) || !aligned(gammas, 4) ||
       !aligned(scores, 4))
-    return fail(QJL_EINVAL, "%s: misaligned pointer", fn);
+    return fail(QJL_EINVAL, "%s: misaligned pointer (codes and bits need 16 B, the rest 4 B)", fn);
+  if (workspace == nullptr || !aligned(workspace, 256))
+    return fail(QJL_EWORKSPACE, "%s: workspace NULL or not 256-byte aligned", fn);
+  const size_t need = qjl::tq_scores_workspace_bytes(B, H_q);
+  if (workspace_bytes < need)
+    return fail(QJL_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
   qjl::RotqTables tb;
   qjl_status st = get_rotq(seed, &tb);
   if (st != QJL_OK) return st;
-  const int e = qjl::launch_tq_scores(tb, k, q, codes, bits, norms, gammas, B, H_q, H_kv, N, cap, scores, stream);
+  const int e = qjl::launch_tq_scores(tb, k, q, codes, bits, norms, gammas, B, H_q, H_kv, N, cap, scores,
+                                      workspace, stream);
   if (e != hipSuccess) return fail(QJL_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(static_cast<hipError_t>(e)));
   return QJL_OK;
 }

@@ -543,59 +543,173 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
 // TurboQuant_prod scores: est_t = n_t (<Pi q, c[idx_t]> + sqrt(pi/2)/m g_t
 // <S^T Pi q, 2 bit_t - 1>) for every token t < N and query head
 // ---------------------------------------------------------------------------
-// A workgroup takes 256 tokens of one (batch, kv head); its prologue rotates
-// the G queries (fp32 FMAs), sketches them (S^T Pi q) and builds, per head,
-// nibble tables in LDS: for the sign words, the sum of S^T Pi q over the set
-// bits of every 4-bit group; for the codes, <Pi q, c[idx]> over the
-// coordinates of a 4-bit group (4 coordinates at k = 1, 2 at k = 2; at k = 3
-// one table row per coordinate).  A thread then scores one token with one
-// LDS lookup per nibble (32 + 64 at k = 2).
+// Two kernels.  tq_query_kernel prepares each query head once: Pi q and
+// S^T Pi q (fp32 FMAs, coalesced reads of the transposed rotation and of S)
+// into the workspace.  tq_scores_kernel takes a range of tokens of one
+// (batch, kv head); its prologue builds nibble tables in LDS from the
+// prepared queries of the kv head's G query heads, the G heads' values of one
+// table entry side by side (so one 16-byte LDS read serves four heads): for
+// the sign words, the sum of S^T Pi q over the set bits of every 4-bit group;
+// for the codes, <Pi q, c[idx]> over the coordinates of a 4-bit group (4
+// coordinates at k = 1, 2 at k = 2; at k = 3 one table row per coordinate).
+// A thread then scores its tokens with one table read per nibble (per four
+// heads): 32 sign nibbles and 32, 64 or 128 code lookups at k = 1, 2, 3.
+
+// prepared query of head hq: [hq][0][D] = Pi q, [hq][1][D] = S^T Pi q
+constexpr int kQPrepFloats = 2 * D;
+
+// 256 threads per query head: thread (jp, i4) sums the products of 16
+// channels j (part jp of 8) for coordinates 4 i4 .. 4 i4 + 3 (one 16-byte
+// read of a row of the transposed rotation, or 8 bytes of S, per channel);
+// the 8 partial sums of a coordinate are then added in part order.
+constexpr int kQueryThreads = 256;
+__global__ __launch_bounds__(kQueryThreads) void tq_query_kernel(const float* __restrict__ q,
+                                                                 const float* __restrict__ rotT,
+                                                                 const uint16_t* __restrict__ s_il,
+                                                                 float* __restrict__ prep) {
+  constexpr int PARTS = kQueryThreads / (D / 4);   // 8
+  constexpr int JP = D / PARTS;                    // 16 channels per part
+  __shared__ float qs[D], qr[D];
+  __shared__ __attribute__((aligned(16))) float part[PARTS][D];
+  const int tid = threadIdx.x;
+  const int i4 = tid % (D / 4), jp = tid / (D / 4);
+  const int64_t hq = blockIdx.x;
+  // every global read is issued up front (the matrices do not depend on q)
+  float4 r[JP];
+  uint2 w[JP];
+#pragma unroll
+  for (int u = 0; u < JP; ++u) r[u] = reinterpret_cast<const float4*>(rotT + (jp * JP + u) * D)[i4];
+#pragma unroll
+  for (int u = 0; u < JP; ++u) w[u] = reinterpret_cast<const uint2*>(s_il + (jp * JP + u) * D)[i4];
+  if (tid < D) qs[tid] = q[hq * D + tid];
+  __syncthreads();
+  // (Pi q)_i = sum_j Pi[i][j] q_j; the transposed table puts Pi[i][j] at [j][i]
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < JP; ++u) {
+    const float qj = qs[jp * JP + u];
+    acc.x = __builtin_fmaf(r[u].x, qj, acc.x);
+    acc.y = __builtin_fmaf(r[u].y, qj, acc.y);
+    acc.z = __builtin_fmaf(r[u].z, qj, acc.z);
+    acc.w = __builtin_fmaf(r[u].w, qj, acc.w);
+  }
+  reinterpret_cast<float4*>(part[jp])[i4] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float v = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < PARTS; ++p2) v += part[p2][tid];
+    qr[tid] = v;
+    prep[hq * kQPrepFloats + tid] = v;
+  }
+  __syncthreads();
+  // (S^T Pi q)_l = sum_i S[i][l] (Pi q)_i, S stored [i][l]
+  acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < JP; ++u) {
+    const float qi = qr[jp * JP + u];
+    acc.x = __builtin_fmaf(__uint_as_float(w[u].x << 16), qi, acc.x);
+    acc.y = __builtin_fmaf(__uint_as_float(w[u].x & 0xFFFF0000u), qi, acc.y);
+    acc.z = __builtin_fmaf(__uint_as_float(w[u].y << 16), qi, acc.z);
+    acc.w = __builtin_fmaf(__uint_as_float(w[u].y & 0xFFFF0000u), qi, acc.w);
+  }
+  reinterpret_cast<float4*>(part[jp])[i4] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float v = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < PARTS; ++p2) v += part[p2][tid];
+    prep[hq * kQPrepFloats + D + tid] = v;
+  }
+}
+
+// acc[h] += entry[h] for GH (<= 4) heads of one table entry, one LDS read
+template <int GH>
+__device__ __forceinline__ void add_entry(const float* e, float (&acc)[GH]) {
+  if constexpr (GH == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(e);
+    acc[0] += v.x;
+    acc[1] += v.y;
+    acc[2] += v.z;
+    acc[3] += v.w;
+  } else if constexpr (GH == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(e);
+    acc[0] += v.x;
+    acc[1] += v.y;
+  } else {
+    acc[0] += e[0];
+  }
+}
+
+// one token's cache row: code words, sign words, norm and gamma
+template <int K>
+struct TqRow {
+  uint32_t cw[D * K / 32];
+  uint32_t bw[4];
+  float n, g;
+};
+template <int K>
+__device__ __forceinline__ void load_tq_row(TqRow<K>& r, const uint32_t* __restrict__ codes,
+                                            const uint32_t* __restrict__ bits, const float* __restrict__ norms,
+                                            const float* __restrict__ gammas, int64_t row) {
+  constexpr int CW = D * K / 32;   // 4, 8 or 12: whole 16-byte chunks
+#pragma unroll
+  for (int w4 = 0; w4 < CW / 4; ++w4) {
+    const uint4 v = reinterpret_cast<const uint4*>(codes + row * CW)[w4];
+    r.cw[4 * w4] = v.x;
+    r.cw[4 * w4 + 1] = v.y;
+    r.cw[4 * w4 + 2] = v.z;
+    r.cw[4 * w4 + 3] = v.w;
+  }
+  const uint4 v = reinterpret_cast<const uint4*>(bits + row * 4)[0];
+  r.bw[0] = v.x;
+  r.bw[1] = v.y;
+  r.bw[2] = v.z;
+  r.bw[3] = v.w;
+  r.n = norms[row];
+  r.g = gammas[row];
+}
+
 template <int G, int K>
 __global__ __launch_bounds__(256) void tq_scores_kernel(
-    const float* __restrict__ q, const uint32_t* __restrict__ codes, const uint32_t* __restrict__ bits,
-    const float* __restrict__ norms, const float* __restrict__ gammas, const float* __restrict__ rot,
-    const uint16_t* __restrict__ s_il, const float* __restrict__ cents, int H_kv, int N, int cap,
-    float coef, float* __restrict__ out) {
+    const float* __restrict__ prep, const uint32_t* __restrict__ codes, const uint32_t* __restrict__ bits,
+    const float* __restrict__ norms, const float* __restrict__ gammas, const float* __restrict__ cents, int H_kv,
+    int N, int cap, int tpw, float coef, float* __restrict__ out) {
   constexpr int CW = D * K / 32;                       // code words per token
   constexpr int CROWS = K == 3 ? D : D * K / 4;        // code-table rows
   constexpr int CCOLS = K == 3 ? 8 : 16;
-  __shared__ float qs[G][D];            // q, then S^T Pi q
-  __shared__ float qr[G][D];            // Pi q
-  __shared__ float lb[G][D / 4][16];    // sign-word nibbles
-  __shared__ float lc[G][CROWS][CCOLS]; // code nibbles
+  __shared__ float qr[G][D];                           // Pi q
+  __shared__ float qs[G][D];                           // S^T Pi q
+  __shared__ __attribute__((aligned(16))) float lb[D / 4][16][G];   // sign-word nibbles
+  __shared__ __attribute__((aligned(16))) float lc[CROWS][CCOLS][G];  // code nibbles
   __shared__ float ssum[G];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int64_t bh = static_cast<int64_t>(b) * H_kv + kvh;
+  const int t_end = min(N, (static_cast<int>(blockIdx.x) + 1) * tpw);
+  // the first token's row is in flight while the tables are built
+  int t = blockIdx.x * tpw + tid;
+  TqRow<K> cur;
+  if (t < t_end) load_tq_row<K>(cur, codes, bits, norms, gammas, bh * cap + t);
   float c[1 << K];
 #pragma unroll
   for (int v = 0; v < (1 << K); ++v) c[v] = cents[v];
-  for (int e = tid; e < G * D; e += 256) qs[e / D][e % D] = q[(bh * G) * D + e];
-  __syncthreads();
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, i = e % D;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) acc = __builtin_fmaf(rot[i * D + j], qs[h][j], acc);
-    qr[h][i] = acc;
+    const float* p = prep + (bh * G + h) * kQPrepFloats;
+    qr[h][i] = p[i];
+    qs[h][i] = p[D + i];
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += 256) {
-    const int h = e / D, l = e % D;
-    float acc = 0.f;
-    for (int i = 0; i < D; ++i)
-      acc = __builtin_fmaf(__uint_as_float(static_cast<uint32_t>(s_il[i * D + l]) << 16), qr[h][i], acc);
-    qs[h][l] = acc;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * (D / 4) * 16; e += 256) {
-    const int h = e / (D * 4), g4 = (e / 16) % (D / 4), nib = e % 16;
+  for (int e = tid; e < (D / 4) * 16 * G; e += 256) {
+    const int h = e % G, nib = (e / G) % 16, g4 = e / (16 * G);
     float v = 0.f;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) v += (nib >> bb) & 1 ? qs[h][4 * g4 + bb] : 0.f;
-    lb[h][g4][nib] = v;
+    lb[g4][nib][h] = v;
   }
-  for (int e = tid; e < G * CROWS * CCOLS; e += 256) {
-    const int h = e / (CROWS * CCOLS), row = (e / CCOLS) % CROWS, col = e % CCOLS;
+  for (int e = tid; e < CROWS * CCOLS * G; e += 256) {
+    const int h = e % G, col = (e / G) % CCOLS, row = e / (G * CCOLS);
     float v;
     if constexpr (K == 1) {
       v = 0.f;
@@ -606,7 +720,7 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
     } else {
       v = qr[h][row] * c[col];
     }
-    lc[h][row][col] = v;
+    lc[row][col][h] = v;
   }
   if (tid < G) {
     float s2 = 0.f;
@@ -614,34 +728,58 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
     ssum[tid] = s2;
   }
   __syncthreads();
-  const int t = blockIdx.x * 256 + tid;
-  if (t >= N) return;
-  const int64_t row = bh * cap + t;
-  uint32_t cwd[CW], bw[4];
-#pragma unroll
-  for (int w = 0; w < CW; ++w) cwd[w] = codes[row * CW + w];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) bw[w] = bits[row * 4 + w];
-  const float n = norms[row], g = gammas[row];
 #pragma unroll 1
-  for (int h = 0; h < G; ++h) {
-    float mse = 0.f;
-    if constexpr (K == 3) {
-#pragma unroll 8
-      for (int i = 0; i < D; ++i) {
-        const int bpos = 3 * i;
-        uint32_t idx = cwd[bpos >> 5] >> (bpos & 31);
-        if ((bpos & 31) > 29) idx |= cwd[(bpos >> 5) + 1] << (32 - (bpos & 31));
-        mse += lc[h][i][idx & 7];
+  for (; t < t_end; t += 256) {
+    // the next token's row loads while this one is scored
+    TqRow<K> nxt = cur;
+    if (t + 256 < t_end) load_tq_row<K>(nxt, codes, bits, norms, gammas, bh * cap + t + 256);
+    const uint32_t* cwd = cur.cw;
+    const uint32_t* bw = cur.bw;
+    const float n = cur.n, g = cur.g;
+    // heads in groups of up to four (one 16-byte table read per nibble)
+    constexpr int GH = G < 4 ? G : 4;
+#pragma unroll 1
+    for (int h0 = 0; h0 < G; h0 += GH) {
+      // the words pass through an empty asm per group, so the table
+      // addresses derived from them are recomputed in the loop, not held
+      // live across it (96 to 160 registers otherwise)
+      uint32_t cw2[CW], bw2[4];
+#pragma unroll
+      for (int w = 0; w < CW; ++w) {
+        cw2[w] = cwd[w];
+        asm volatile("" : "+v"(cw2[w]));
       }
-    } else {
 #pragma unroll
-      for (int r = 0; r < CROWS; ++r) mse += lc[h][r][(cwd[r >> 3] >> (4 * (r & 7))) & 15];
+      for (int w = 0; w < 4; ++w) {
+        bw2[w] = bw[w];
+        asm volatile("" : "+v"(bw2[w]));
+      }
+      float mse[GH], pos[GH];
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        mse[h] = 0.f;
+        pos[h] = 0.f;
+      }
+      if constexpr (K == 3) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          const int bpos = 3 * i;
+          uint32_t idx = cw2[bpos >> 5] >> (bpos & 31);
+          if ((bpos & 31) > 29) idx |= cw2[(bpos >> 5) + 1] << (32 - (bpos & 31));
+          add_entry<GH>(&lc[i][idx & 7][h0], mse);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < CROWS; ++r) add_entry<GH>(&lc[r][(cw2[r >> 3] >> (4 * (r & 7))) & 15][h0], mse);
+      }
+#pragma unroll
+      for (int r = 0; r < D / 4; ++r) add_entry<GH>(&lb[r][(bw2[r >> 3] >> (4 * (r & 7))) & 15][h0], pos);
+#pragma unroll
+      for (int h = 0; h < GH; ++h)
+        out[((bh * G + h0 + h) * static_cast<int64_t>(N)) + t] =
+            n * (mse[h] + coef * g * (2.f * pos[h] - ssum[h0 + h]));
     }
-    float pos = 0.f;
-#pragma unroll
-    for (int r = 0; r < D / 4; ++r) pos += lb[h][r][(bw[r >> 3] >> (4 * (r & 7))) & 15];
-    out[((bh * G + h) * static_cast<int64_t>(N)) + t] = n * (mse + coef * g * (2.f * pos - ssum[h]));
+    cur = nxt;
   }
 }
 
@@ -687,18 +825,31 @@ int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys
   return hipGetLastError();
 }
 
+size_t tq_scores_workspace_bytes(int B, int H_q) {
+  return static_cast<size_t>(B) * H_q * kQPrepFloats * sizeof(float);
+}
+
 int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t* codes,
                      const uint32_t* bits, const float* norms, const float* gammas, int B, int H_q,
-                     int H_kv, int N, int cap, float* out, void* stream) {
+                     int H_kv, int N, int cap, float* out, void* workspace, void* stream) {
   const int G = H_q / H_kv;
   // sqrt(pi/2) / m with m = d
   const float coef = static_cast<float>(1.2533141373155002512 / D);
-  dim3 grid((N + 255) / 256, H_kv, B);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  float* prep = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(tq_query_kernel, dim3(B * H_q), dim3(kQueryThreads), 0, st, q, tb.rotT, tb.s_il, prep);
+  // about two workgroups per compute unit, each a multiple of 256 tokens
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t heads = static_cast<int64_t>(B) * H_kv;
+  const int64_t want = (2 * static_cast<int64_t>(cus) + heads - 1) / heads;
+  const int64_t per = (N + want - 1) / want;
+  const int tpw = static_cast<int>((per + 255) / 256 * 256);
+  dim3 grid((N + tpw - 1) / tpw, H_kv, B);
   const float* cents = tb.tq_cents + 8 * (k - 1);
-#define QJL_TQ_SCORES(GG, KK)                                                                     \
-  hipLaunchKernelGGL((tq_scores_kernel<GG, KK>), grid, dim3(256), 0, st, q, codes, bits, norms, gammas, \
-                     tb.rot, tb.s_il, cents, H_kv, N, cap, coef, out)
+#define QJL_TQ_SCORES(GG, KK)                                                                          \
+  hipLaunchKernelGGL((tq_scores_kernel<GG, KK>), grid, dim3(256), 0, st, prep, codes, bits, norms, gammas, \
+                     cents, H_kv, N, cap, tpw, coef, out)
 #define QJL_TQ_SCORES_K(GG)            \
   switch (k) {                         \
     case 1: QJL_TQ_SCORES(GG, 1); break; \

@@ -30,7 +30,7 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqjl.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {0: "QJL_OK", 1: "QJL_EINVAL", 2: "QJL_EUNSUPPORTED", 3: "QJL_EWORKSPACE",
           4: "QJL_EHIP", 5: "QJL_ENOMEM"}
@@ -100,7 +100,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                            c_int, c_vp]
         lib.qjl_tq_scores.restype = c_int
         lib.qjl_tq_scores.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
-                                      c_int, c_int, c_u64, c_vp, c_vp]
+                                      c_int, c_int, c_u64, c_vp, c_vp, c_sz, c_vp]
+        lib.qjl_tq_scores_workspace_bytes.restype = c_sz
+        lib.qjl_tq_scores_workspace_bytes.argtypes = [c_int, c_int, c_int]
         lib.qjl_testing_set_rotq_margin.restype = c_int
         lib.qjl_testing_set_rotq_margin.argtypes = [c_int]
         lib.qjl_release_cache.restype = c_int
@@ -192,18 +194,18 @@ def decode_workspace_bytes(B, H_q, H_kv, N, d, m) -> int:
     return load().qjl_decode_workspace_bytes(B, H_q, H_kv, N, d, m)
 
 
-def workspace_for(nbytes: int, device, stream=None):
+def workspace_for(nbytes: int, device, stream=None, tag: str = "decode"):
     """A zero-filled workspace of at least nbytes, cached per (device, stream).
 
     It is allocated and zero-filled on ``stream`` (default: the current
     stream), so it is ready for the kernels queued there, and the caching
     allocator keeps its memory for that stream.  Calls on one stream share
     it (each call returns its counters to zero); calls on other streams get
-    their own.
+    their own.  ``tag`` keeps workspaces of different entry points apart.
     """
     import torch
     s = _resolve_stream(stream)
-    key = (str(device), s.cuda_stream)
+    key = (str(device), s.cuda_stream, tag)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         with torch.cuda.stream(s):
@@ -320,8 +322,19 @@ def tq_encode_keys(keys, codes, bits, norms, gammas, pos: int, seed: int, k: int
                                      _stream_handle(stream)))
 
 
-def tq_scores(q, codes, bits, norms, gammas, N: int, seed: int, k: int, out=None, stream=None):
-    """qjl_tq_scores: estimated <q, k_t> -> fp32 [B][H_q][N]."""
+def tq_scores_workspace_bytes(B: int, H_q: int, d: int) -> int:
+    """qjl_tq_scores_workspace_bytes."""
+    return load().qjl_tq_scores_workspace_bytes(B, H_q, d)
+
+
+def tq_scores(q, codes, bits, norms, gammas, N: int, seed: int, k: int, out=None, workspace=None,
+              stream=None):
+    """qjl_tq_scores: estimated <q, k_t> -> fp32 [B][H_q][N].
+
+    The workspace (prepared queries, overwritten by every call) is cached per
+    (device, stream) apart from the decode workspace, whose counters must stay
+    zero between calls.
+    """
     import torch
     B, H_q, d = q.shape
     _, H_kv, cap = norms.shape
@@ -331,8 +344,12 @@ def tq_scores(q, codes, bits, norms, gammas, N: int, seed: int, k: int, out=None
     if out is None:
         with torch.cuda.stream(s):
             out = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device)
+    need = tq_scores_workspace_bytes(B, H_q, d)
+    if workspace is None:
+        workspace = workspace_for(need, q.device, s, tag="tq_scores")
     _check(load().qjl_tq_scores(_ptr(q), _ptr(codes), _ptr(bits), _ptr(norms), _ptr(gammas), B, H_q,
-                                H_kv, N, cap, d, k, seed & (2 ** 64 - 1), _ptr(out), s.cuda_stream))
+                                H_kv, N, cap, d, k, seed & (2 ** 64 - 1), _ptr(out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), s.cuda_stream))
     return out
 
 

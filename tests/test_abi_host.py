@@ -302,8 +302,9 @@ def pqe(lib, keys=A16, B=1, H=1, n=4, d=128, codes=A16, radii=A16, cap=8, pos=0)
 
 
 def tqs(lib, q=A16, codes=A16, bits=A16, norms=A16, gammas=A16, B=1, Hq=4, Hkv=1, N=8, cap=8, d=128, k=2,
-        out=A16):
-    return lib.qjl_tq_scores(q, codes, bits, norms, gammas, B, Hq, Hkv, N, cap, d, k, 7, out, None)
+        out=A16, ws=A16, ws_bytes=1 << 20):
+    return lib.qjl_tq_scores(q, codes, bits, norms, gammas, B, Hq, Hkv, N, cap, d, k, 7, out, ws, ws_bytes,
+                             None)
 
 
 def test_rotq_entry_point_validation(lib):
@@ -335,3 +336,14 @@ def test_rotq_entry_point_validation(lib):
         assert tqs(lib, **{name: None}) == EINVAL, name
     assert tqs(lib, out=A16 + 2) == EINVAL
     assert "misaligned" in qjl.last_error()
+    assert tqs(lib, codes=A16 + 4) == EINVAL and tqs(lib, bits=A16 + 8) == EINVAL   # 16 B
+    assert tqs(lib, B=70000, Hq=70000, Hkv=70000, N=1, cap=1) == EINVAL
+    # the workspace holds Pi q and S^T Pi q of every query head
+    need = lib.qjl_tq_scores_workspace_bytes(2, 8, 128)
+    assert need == 2 * 8 * 2 * 128 * 4
+    assert lib.qjl_tq_scores_workspace_bytes(0, 8, 128) == 0
+    assert lib.qjl_tq_scores_workspace_bytes(2, 8, 64) == 0
+    assert tqs(lib, B=2, Hq=8, Hkv=2, ws=None) == EWS
+    assert tqs(lib, B=2, Hq=8, Hkv=2, ws=A16 + 16) == EWS
+    assert tqs(lib, B=2, Hq=8, Hkv=2, ws_bytes=need - 4) == EWS
+    assert "workspace" in qjl.last_error()
