@@ -11,7 +11,9 @@ tokens.
 Headline ``value``: the decode step's effective HBM bandwidth, algorithmic
 bytes (sign words + norms + bf16 values + q + out) over the decode kernel's
 duration, timed with HIP events on the launch stream around K decode
-launches issued back to back.  The encode is timed the same way.
+launches issued back to back (a spin kernel ahead of the first event holds
+the GPU until the host has queued all K, so the events time the kernels, not
+the host's launch rate).  The encode is timed the same way.
 
 Every timed loop cycles through a ring of buffer sets whose bytes touched by
 the timed kernels (read and written) add up to more than 600 MiB, more than
@@ -128,8 +130,8 @@ def roofline(achieved_gbs, traffic, kernel, alg_bytes):
             "kernel": kernel, "algorithmic_bytes_per_launch": int(alg_bytes)}
 
 
-# GPU clock cycles of hold per queued call (~150 us at 2.4 GHz)
-HOLD_CYCLES_PER_CALL = 360_000
+# GPU clock cycles of hold per queued call (~250 us at 2.4 GHz)
+HOLD_CYCLES_PER_CALL = 600_000
 
 
 class Timer:
@@ -171,11 +173,13 @@ class Timer:
         return e0.elapsed_time(e1) / reps
 
     def each(self, fn, reps):
-        """fn(i) back to back with an event between consecutive calls; returns
-        the per-call durations (ms) and the total (ms)."""
+        """fn(i) back to back with an event between consecutive calls (the
+        GPU held as in b2b while the host queues them); returns the per-call
+        durations (ms) and the total (ms)."""
         torch = self.torch
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda._sleep(int(reps * HOLD_CYCLES_PER_CALL))
         ev[0].record(self.stream)
         for i in range(reps):
             fn(i)
@@ -458,8 +462,11 @@ def bench_long64k(qjl, w, args, T):
         qjl.decode_attention(qs[s], st["signs"], st["norms"], st["values"], N0 + s + 1, SEED, m,
                              out=st["out"], workspace=ws)
     T.each(step, steps)                           # warmup: the 64 steps once
-    per, total = T.each(step, steps)
-    per2, total2 = T.each(step2, steps)
+    per, _ = T.each(step, steps)                  # per-step times (events between the steps)
+    per2, _ = T.each(step2, steps)
+    # totals: the 64 steps back to back, no events between them
+    total = T.b2b(step, steps) * steps
+    total2 = T.b2b(step2, steps) * steps
     per = np.array(per)
     med = float(np.median(per))
     alg = np.array([decode_bytes(B, Hq, Hkv, N0 + s + 1, d, m) for s in range(steps)], dtype=np.float64)
@@ -487,7 +494,8 @@ def bench_long64k(qjl, w, args, T):
             "note": "a step = qjl_decode_step: the append of one token per kv head (key encoded, value "
                     "row copied) and the decode over all tokens, in one launch; two_call_* = "
                     "qjl_encode_keys of the new keys then qjl_decode_attention; step fraction = the "
-                    "step's decode bytes / the step's time"}
+                    "step's decode bytes / the step's time; per-step times carry an event between "
+                    "steps, the totals none"}
 
 
 def bench_mha16k(qjl, w, args, T):

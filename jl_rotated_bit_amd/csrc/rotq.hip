@@ -24,18 +24,23 @@
 //   b' >= T a'; level-l cells by s_b >= T^2 s_a on fp64 tree sums of
 //   squares; radius = fp32(sqrt(total)).
 //
-// Kernel design.  A workgroup (256 threads) keeps Pi^T (fp32, 64 KB) and, for
-// TurboQuant, S (bf16, 32 KB) in LDS for the whole launch and walks over
-// tiles of 32 keys.  The rotation is an fp64 product (each product of an fp32
-// and a bf16 value is exact in fp64; MI355X runs fp64 FMAs at its full fp64
-// rate on the vector units): thread (coordinate i, key half h) accumulates
-// 16 keys, reading Pi^T[j][i] (consecutive lanes, no bank conflicts) and the
-// 16 keys' channel j as a broadcast.  The fp32 rounding is certified: with
+// Kernel design.  A workgroup (eight waves, one per CU: the tables fill most
+// of the LDS) keeps Pi^T (fp32, 64 KB) and, for TurboQuant, S (bf16, 32 KB)
+// in LDS for the whole launch and walks over tiles of 32 keys; the next
+// tile's keys (one 16-byte chunk per thread) load into registers while the
+// current tile is encoded.  The rotation y = K Pi^T, and TurboQuant's
+// residual sketch S^T r, are fp64 products on the matrix cores
+// (v_mfma_f64_16x16x4f64): every product of a bf16 key value or an fp32
+// residual with an fp32 rotation entry or a bf16 sketch entry is exact in
+// fp64, so a sum carries at most d roundings in whatever order the unit adds.
+// Wave w computes keys 16 (w & 1) .. +15 against the 32 columns
+// 32 (w >> 1) .. +31.  The fp32 rounding is certified: with
 // E = 2 d 2^-53 ||k|| max_i ||Pi_i|| bounding the fp64 error, y = fp32(v + E)
-// when that equals fp32(v - E); otherwise (about one value in 10^5) the sum
-// is recomputed exactly in a 576-bit integer accumulator and rounded from
-// there.  The residual's QJL signs are certified the same way (the sign of
-// the fp64 sum when it exceeds its error bound, else the exact integer sum).
+// when that equals fp32(v - E); otherwise (about one value in 10^5) the lanes
+// of the wave take turns recomputing their open sums exactly in a 576-bit
+// integer accumulator and rounding from there.  The residual's QJL signs are
+// certified the same way (the sign of the fp64 sum when it exceeds its error
+// bound, else the exact integer sum).
 // This file is compiled with -ffp-contract=off: every fp64/fp32 operation
 // that feeds a decision rounds exactly as written.
 
