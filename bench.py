@@ -596,7 +596,7 @@ def bench_rotq(qjl, w, args, T):
     tq_flops = R * 2.0 * (2 * d * d)            # rotation + residual sketch (m = d)
     pq_flops = R * 2.0 * d * d                  # rotation
     sc_bytes = R * (d * k // 8 + d // 8 + 8) + B * Hq * N * 4
-    fp64 = lambda fl, ms: {"bound": "fp64", "achieved": round(fl / (ms / 1e3) / 1e12, 2),
+    fp64 = lambda fl, ms: {"bound": "mfma", "dtype": "f64", "achieved": round(fl / (ms / 1e3) / 1e12, 2),
                            "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(fl / (ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS, 4),
                            "flops_per_launch": int(fl)}

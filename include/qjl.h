@@ -40,6 +40,11 @@
  *   launched and no output has been written.
  * - All entry points are thread-safe.  Inputs with Inf or NaN give undefined
  *   (but memory-safe) results.
+ * - The library is silent unless the environment (read once per process)
+ *   says otherwise: QJL_LOG=1 prints every error to stderr ("[qjl] error
+ *   <status>: <message>"), QJL_LOG=2 also names every call; QJL_TRACE=1 wraps
+ *   every call in a roctx range (the ROCm tracer's marker API, loaded on
+ *   first use), visible under rocprofv3 --marker-trace.
  */
 #ifndef QJL_H
 #define QJL_H

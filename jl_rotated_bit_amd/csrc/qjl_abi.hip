@@ -4,11 +4,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
+
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -36,6 +39,63 @@ constexpr int32_t kAbiVersion = 3;
 
 thread_local std::string g_last_error;
 
+// ---- logging and trace ranges (environment, read once) ----
+// QJL_LOG=1: every failed call prints its error to stderr; QJL_LOG=2: every
+// entry into a compute entry point prints its name too.  QJL_TRACE=1: each
+// entry point is a roctx range (the ROCm tracer's marker API, loaded with
+// dlopen on first use; the ranges show in rocprofv3 --marker-trace).
+int log_level() {
+  static const int level = [] {
+    const char* v = std::getenv("QJL_LOG");
+    return v == nullptr ? 0 : std::atoi(v);
+  }();
+  return level;
+}
+
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx t;
+    const char* v = std::getenv("QJL_TRACE");
+    if (v == nullptr || std::atoi(v) == 0) return t;
+    for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"}) {
+      void* h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
+      if (h == nullptr) continue;
+      auto push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+      auto pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+      if (push != nullptr && pop != nullptr) {
+        t.push = push;
+        t.pop = pop;
+        return t;
+      }
+    }
+    if (log_level() > 0) std::fprintf(stderr, "[qjl] QJL_TRACE: no roctx library found\n");
+    return t;
+  }();
+  return r;
+}
+
+// Entry of a public call: clears the thread's last error, logs and traces.
+class CallScope {
+ public:
+  explicit CallScope(const char* name) : traced_(roctx().push != nullptr) {
+    g_last_error.clear();
+    if (log_level() >= 2) std::fprintf(stderr, "[qjl] %s\n", name);
+    if (traced_) roctx().push(name);
+  }
+  ~CallScope() {
+    if (traced_) roctx().pop();
+  }
+  CallScope(const CallScope&) = delete;
+  CallScope& operator=(const CallScope&) = delete;
+
+ private:
+  bool traced_;
+};
+
 qjl_status fail(qjl_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -43,6 +103,7 @@ qjl_status fail(qjl_status code, const char* fmt, ...) {
   std::vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_last_error = buf;
+  if (log_level() >= 1) std::fprintf(stderr, "[qjl] error %d: %s\n", static_cast<int>(code), buf);
   return code;
 }
 
@@ -296,7 +357,7 @@ qjl_status decode_common(const char* fn, const float* q, const uint32_t* signs, 
                          int32_t cap, int32_t d, int32_t m, uint64_t seed, float scale, float* out,
                          void* workspace, size_t workspace_bytes, void* stream, bool noalloc,
                          const qjl::AppendArgs* append = nullptr) {
-  g_last_error.clear();
+  const CallScope scope(fn);
   if (!supported_dm(d, m))
     return fail(QJL_EUNSUPPORTED, "%s: d=%d m=%d unsupported (d=128, m in {256,512})", fn, d, m);
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || cap <= 0 || N <= 0 || N > cap)
@@ -370,7 +431,7 @@ QJL_API int32_t qjl_abi_version(void) { return kAbiVersion; }
 QJL_API const char* qjl_last_error(void) { return g_last_error.c_str(); }
 
 QJL_API qjl_status qjl_sketch_host(uint64_t seed, int32_t d, int32_t m, uint16_t* out) {
-  g_last_error.clear();
+  const CallScope scope("qjl_sketch_host");
   if (out == nullptr) return fail(QJL_EINVAL, "qjl_sketch_host: out is NULL");
   if (d <= 0 || m <= 0) return fail(QJL_EINVAL, "qjl_sketch_host: d=%d m=%d must be positive", d, m);
   if (static_cast<int64_t>(d) * m > (int64_t{1} << 26))
@@ -380,7 +441,7 @@ QJL_API qjl_status qjl_sketch_host(uint64_t seed, int32_t d, int32_t m, uint16_t
 }
 
 QJL_API qjl_status qjl_rotation_host(uint64_t seed, int32_t d, float* out) {
-  g_last_error.clear();
+  const CallScope scope("qjl_rotation_host");
   if (out == nullptr) return fail(QJL_EINVAL, "qjl_rotation_host: out is NULL");
   if (d < 2 || d > 1024) return fail(QJL_EINVAL, "qjl_rotation_host: d=%d outside [2, 1024]", d);
   qjl::make_rotation_f32(seed, d, out);
@@ -388,7 +449,7 @@ QJL_API qjl_status qjl_rotation_host(uint64_t seed, int32_t d, float* out) {
 }
 
 QJL_API qjl_status qjl_tq_codebook_host(int32_t d, int32_t k, float* centroids) {
-  g_last_error.clear();
+  const CallScope scope("qjl_tq_codebook_host");
   if (centroids == nullptr) return fail(QJL_EINVAL, "qjl_tq_codebook_host: centroids is NULL");
   if (d < 4 || d > 65536 || k < 1 || k > 4)
     return fail(QJL_EINVAL, "qjl_tq_codebook_host: d=%d k=%d outside d in [4, 65536], k in [1, 4]", d, k);
@@ -397,7 +458,7 @@ QJL_API qjl_status qjl_tq_codebook_host(int32_t d, int32_t k, float* centroids) 
 }
 
 QJL_API qjl_status qjl_pq_codebook_host(int32_t level, int32_t bits, float* centroids, float* thresholds) {
-  g_last_error.clear();
+  const CallScope scope("qjl_pq_codebook_host");
   if (centroids == nullptr || thresholds == nullptr) return fail(QJL_EINVAL, "qjl_pq_codebook_host: NULL pointer");
   if (level < 1 || level > 10 || bits < 1 || bits > 5 || (level == 1 && bits < 2))
     return fail(QJL_EINVAL, "qjl_pq_codebook_host: level=%d bits=%d unsupported", level, bits);
@@ -408,7 +469,7 @@ QJL_API qjl_status qjl_pq_codebook_host(int32_t level, int32_t bits, float* cent
 QJL_API qjl_status qjl_encode_keys(const void* keys_bf16, int32_t B, int32_t H_kv, int32_t n,
                                    int32_t d, int32_t m, uint64_t seed, uint32_t* signs,
                                    float* norms, int32_t cap, int32_t pos, void* stream) {
-  g_last_error.clear();
+  const CallScope scope("qjl_encode_keys");
   if (!supported_dm(d, m))
     return fail(QJL_EUNSUPPORTED, "qjl_encode_keys: d=%d m=%d unsupported (d=128, m in {256,512})", d, m);
   if (B <= 0 || H_kv <= 0 || n < 0 || cap <= 0 || pos < 0)
@@ -499,7 +560,7 @@ QJL_API qjl_status qjl_baseline_decode_attention_bf16(const float* q, const void
                                                       float scale, float* out, void* workspace,
                                                       size_t workspace_bytes, void* stream) {
   const char* fn = "qjl_baseline_decode_attention_bf16";
-  g_last_error.clear();
+  const CallScope scope(fn);
   if (d != qjl::kHeadDim) return fail(QJL_EUNSUPPORTED, "%s: d=%d unsupported (d=128)", fn, d);
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || cap <= 0 || N <= 0 || N > cap)
     return fail(QJL_EINVAL, "%s: bad sizes B=%d H_q=%d H_kv=%d N=%d cap=%d", fn, B, H_q, H_kv, N, cap);
@@ -535,7 +596,7 @@ QJL_API qjl_status qjl_tq_encode_keys(const void* keys_bf16, int32_t B, int32_t 
                                       uint32_t* bits, float* norms, float* gammas, int32_t cap,
                                       int32_t pos, void* stream) {
   const char* fn = "qjl_tq_encode_keys";
-  g_last_error.clear();
+  const CallScope scope(fn);
   if (d != qjl::kHeadDim || k < 1 || k > 3)
     return fail(QJL_EUNSUPPORTED, "%s: d=%d k=%d unsupported (d=128, k in {1,2,3})", fn, d, k);
   qjl_status st = check_rows(fn, B, H_kv, n, cap, pos);
@@ -557,7 +618,7 @@ QJL_API qjl_status qjl_pq_encode_keys(const void* keys_bf16, int32_t B, int32_t 
                                       int32_t d, uint64_t seed, uint32_t* codes, float* radii,
                                       int32_t cap, int32_t pos, void* stream) {
   const char* fn = "qjl_pq_encode_keys";
-  g_last_error.clear();
+  const CallScope scope(fn);
   if (d != qjl::kHeadDim) return fail(QJL_EUNSUPPORTED, "%s: d=%d unsupported (d=128)", fn, d);
   qjl_status st = check_rows(fn, B, H_kv, n, cap, pos);
   if (st != QJL_OK || n == 0) return st;
@@ -584,7 +645,7 @@ QJL_API qjl_status qjl_tq_scores(const float* q, const uint32_t* codes, const ui
                                  uint64_t seed, float* scores, void* workspace, size_t workspace_bytes,
                                  void* stream) {
   const char* fn = "qjl_tq_scores";
-  g_last_error.clear();
+  const CallScope scope(fn);
   if (d != qjl::kHeadDim || k < 1 || k > 3)
     return fail(QJL_EUNSUPPORTED, "%s: d=%d k=%d unsupported (d=128, k in {1,2,3})", fn, d, k);
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || cap <= 0 || N <= 0 || N > cap)
@@ -622,7 +683,7 @@ QJL_API int32_t qjl_testing_set_rotq_margin(int32_t log2_factor) {
 }
 
 QJL_API qjl_status qjl_release_cache(void) {
-  g_last_error.clear();
+  const CallScope scope("qjl_release_cache");
   std::lock_guard<std::mutex> lock(g_cache_mu);
   int cur = 0;
   const bool have_dev = hipGetDevice(&cur) == hipSuccess;
