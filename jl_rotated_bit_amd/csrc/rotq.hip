@@ -198,6 +198,34 @@ __device__ __forceinline__ void mfma_tile(const Col& col, const double* x, int w
   }
 }
 
+// Wave-cooperative evaluation of a 128-term sum of exact fp64 products
+// (lane l holds the products of channels 2 l and 2 l + 1): an error-free
+// butterfly in which each level adds the two partial sums with TwoSum
+// (Knuth; the rounding error is recovered exactly) and accumulates the
+// errors, so every lane ends with the same sum s, error sum e and magnitude
+// sum a.  Level h adds at most (2 h + 1) 2^-106 a of error, 48 2^-106 a over
+// the six levels; returns V = fl(s + e) and B = 2^-90 a + 2^-50 |V| with
+// |exact - V| <= B, both wave-uniform.  Needs -ffp-contract=off (no fused
+// operations inside TwoSum).
+__device__ __forceinline__ void wave_exact_sum(double p0, double p1, double& V, double& B) {
+  double s = p0 + p1;
+  const double b0 = s - p0;
+  double e = (p0 - (s - b0)) + (p1 - b0);
+  double a = __builtin_fabs(p0) + __builtin_fabs(p1);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const double s2 = __shfl_xor(s, m), e2 = __shfl_xor(e, m), a2 = __shfl_xor(a, m);
+    const double sn = s + s2;
+    const double bn = sn - s;
+    const double t = (s - (sn - bn)) + (s2 - bn);
+    e = (e + e2) + t;
+    s = sn;
+    a = a + a2;
+  }
+  V = s + e;
+  B = a * 0x1.0p-90 + __builtin_fabs(V) * 0x1.0p-50;
+}
+
 // fp64 sum of squares of x[j][t] over j in order (the exact definition the
 // codes use), loads batched 16 at a time
 __device__ __forceinline__ double ordered_sumsq(const double* x, int t) {
@@ -277,22 +305,39 @@ __device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk, con
       L.y[t][i] = hi;
       if (lo != hi && t < nk) open |= 1u << (4 * c + r);
     }
-  // exact sums for the uncertified values (about one in 10^5): the lanes
-  // of a wave take turns with the wave's integer accumulator
+  // The uncertified values (about one in 10^4): the whole wave sums each
+  // one's 128 exact products (keys and rotation from LDS) with the
+  // error-free butterfly and rounds once the bound decides the fp32 value;
+  // otherwise (with the bound, about one in 10^8) one lane takes the exact
+  // integer accumulator.
   for (uint64_t any = __ballot(open != 0); any != 0; any = __ballot(open != 0)) {
     const int l = __builtin_ctzll(any);   // wave-uniform
-    if (lane == l) {
-      uint32_t* pos = L.scratch[wave];
-      uint32_t* neg = pos + ACC_WORDS;
-      for (uint32_t o = open; o; o &= o - 1) {
-        const int u = __builtin_ctz(o);
-        const int t = t_base + 4 * (u & 3), i = i_base + 16 * (u >> 2);
+    const uint32_t ol = __builtin_amdgcn_readlane(open, l);
+    const int u = __builtin_ctz(ol);
+    const int t = 16 * (wave & 1) + (l >> 4) + 4 * (u & 3);
+    const int i = 16 * CB * (wave >> 1) + (l & 15) + 16 * (u >> 2);
+    const double p0 = L.kt[(2 * lane) * TKP + t] * static_cast<double>(L.rotT[(2 * lane) * D + i]);
+    const double p1 = L.kt[(2 * lane + 1) * TKP + t] * static_cast<double>(L.rotT[(2 * lane + 1) * D + i]);
+    double V, B;
+    wave_exact_sum(p0, p1, V, B);
+    B *= wide;
+    const float lo = static_cast<float>(V - B);
+    float yv = static_cast<float>(V + B);
+    if (__float_as_uint(lo) != __float_as_uint(yv)) {   // wave-uniform
+      float ex = 0.f;
+      if (lane == 0) {
+        uint32_t* pos = L.scratch[wave];
+        uint32_t* neg = pos + ACC_WORDS;
         long_clear(pos);
         const uint16_t* krow = a.keys + static_cast<int64_t>(row0 + t) * D;
         for (int j = 0; j < D; ++j) add_product(pos, neg, krow[j], a.rot[i * D + j]);
-        L.y[t][i] = long_to_f32(pos, neg);
+        ex = long_to_f32(pos, neg);
       }
-      open = 0;
+      yv = __shfl(ex, 0);
+    }
+    if (lane == l) {
+      L.y[t][i] = yv;
+      open &= open - 1;   // value u done
     }
   }
   __syncthreads();
@@ -367,21 +412,43 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (!(__builtin_fabs(acc[c][r]) > Er[r]) && t_base + 4 * r < nk) open |= 1u << (4 * c + r);
-    // exact signs for the uncertified sums (rare): lanes take turns with the
-    // wave's integer accumulator
+    // exact signs for the uncertified sums (rare): the wave's error-free
+    // butterfly over the 128 exact products, then, if the bound cannot
+    // decide, one lane's integer accumulator
     for (uint64_t any = __ballot(open != 0); any != 0; any = __ballot(open != 0)) {
-      const int ln = __builtin_ctzll(any);
-      if (lane == ln) {
-        uint32_t* pos = L.scratch[wave];
-        uint32_t* neg = pos + ACC_WORDS;
-        for (uint32_t o = open; o; o &= o - 1) {
-          const int u = __builtin_ctz(o);
-          const int t = t_base + 4 * (u & 3), lc = l_base + 16 * (u >> 2);
+      const int ln = __builtin_ctzll(any);   // wave-uniform
+      const uint32_t ol = __builtin_amdgcn_readlane(open, ln);
+      const int u = __builtin_ctz(ol);
+      const int t = 16 * (wave & 1) + (ln >> 4) + 4 * (u & 3);
+      const int lc = 16 * CB * (wave >> 1) + (ln & 15) + 16 * (u >> 2);
+      const double p0 = static_cast<double>(L.y[t][2 * lane]) *
+                        static_cast<double>(__uint_as_float(static_cast<uint32_t>(L.s_il[(2 * lane) * D + lc]) << 16));
+      const double p1 = static_cast<double>(L.y[t][2 * lane + 1]) *
+                        static_cast<double>(__uint_as_float(static_cast<uint32_t>(L.s_il[(2 * lane + 1) * D + lc]) << 16));
+      double V, B;
+      wave_exact_sum(p0, p1, V, B);
+      B *= wide;
+      int positive;
+      if (V > B) {
+        positive = 1;
+      } else if (V < -B) {
+        positive = 0;
+      } else if (B == 0.0) {
+        positive = 1;   // every product is zero: the exact sum is 0, sign +1
+      } else {
+        int sg = 0;
+        if (lane == 0) {
+          uint32_t* pos = L.scratch[wave];
+          uint32_t* neg = pos + ACC_WORDS;
           long_clear(pos);
           for (int ii = 0; ii < D; ++ii) add_product(pos, neg, L.s_il[ii * D + lc], L.y[t][ii]);
-          acc[u >> 2][u & 3] = long_sign(pos, neg) ? 1.0 : -1.0;
+          sg = long_sign(pos, neg) ? 1 : 0;
         }
-        open = 0;
+        positive = __shfl(sg, 0);
+      }
+      if (lane == ln) {
+        acc[u >> 2][u & 3] = positive ? 1.0 : -1.0;
+        open &= open - 1;   // value u done
       }
     }
     // sign words: ballot bit l of register (c, r) is key 16 (wave & 1) +

@@ -101,14 +101,16 @@ def test_tq_encode_ragged(gpu_lib, B, H, n, cap, pos):
     check_tq(gpu_lib, keys, 2, cap=cap, pos=pos, label="ragged")
 
 
-@pytest.mark.parametrize("k", [1, 2])
-def test_tq_encode_exact_paths(gpu_lib, k):
-    """With the certificates widened by 2^40 every value takes the exact
-    integer paths (rounding of the rotation, residual signs); results are
-    unchanged."""
+@pytest.mark.parametrize("k,margin", [(1, 40), (2, 40), (2, 12), (3, 12)])
+def test_tq_encode_exact_paths(gpu_lib, k, margin):
+    """Certificates widened by 2^margin: at 2^12 about a third of the
+    rotated values (and every residual sign near zero) go to the wave's
+    error-free butterfly sums, which decide them; at 2^40 those sums cannot
+    decide either and every value takes the exact integer accumulator.
+    Results are unchanged."""
     rng = np.random.default_rng(30 + k)
     K = np.concatenate([wl.gaussian_keys(rng, 200), special_keys(rng)])
-    prev = gpu_lib.testing_set_rotq_margin(40)
+    prev = gpu_lib.testing_set_rotq_margin(margin)
     try:
         check_tq(gpu_lib, K.reshape(1, 1, -1, D), k, label="exact paths")
     finally:
@@ -198,10 +200,11 @@ def test_pq_encode_ragged(gpu_lib, B, H, n, cap, pos):
 def test_pq_encode_exact_paths_and_workload(gpu_lib):
     rng = np.random.default_rng(61)
     K = np.concatenate([wl.gaussian_keys(rng, 200), special_keys(rng)])
-    prev = gpu_lib.testing_set_rotq_margin(40)
-    try:
-        check_pq(gpu_lib, K.reshape(1, 1, -1, D), label="exact paths")
-    finally:
-        gpu_lib.testing_set_rotq_margin(prev)
+    for margin in (12, 40):   # butterfly sums decide / the integer accumulator decides
+        prev = gpu_lib.testing_set_rotq_margin(margin)
+        try:
+            check_pq(gpu_lib, K.reshape(1, 1, -1, D), label=f"exact paths, margin 2^{margin}")
+        finally:
+            gpu_lib.testing_set_rotq_margin(prev)
     w = wl.gqa32k()
     check_pq(gpu_lib, w.keys, label="gqa32k keys")
