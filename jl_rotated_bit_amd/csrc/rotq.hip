@@ -198,6 +198,15 @@ __device__ __forceinline__ void mfma_tile(const Col& col, const double* x, int w
   }
 }
 
+// A power of two at least sqrt(s) (s >= 0, finite), from the exponent field
+// alone: s < 2^(e + 1) with e = floor(log2 s), so sqrt(s) < 2^(e / 2 + 1).
+// Used for the certificate bounds, which need an upper bound of a norm, not
+// the norm (an fp64 square root is a long instruction sequence).
+__device__ __forceinline__ double sqrt_upper_pow2(double s) {
+  const int e = static_cast<int>((__double_as_longlong(s) >> 52) & 0x7FF) - 1023;   // s >= 0
+  return __builtin_ldexp(1.0, (e >> 1) + 1);
+}
+
 // Wave-cooperative evaluation of a 128-term sum of exact fp64 products
 // (lane l holds the products of channels 2 l and 2 l + 1): an error-free
 // butterfly in which each level adds the two partial sums with TwoSum
@@ -205,24 +214,36 @@ __device__ __forceinline__ void mfma_tile(const Col& col, const double* x, int w
 // errors, so every lane ends with the same sum s, error sum e and magnitude
 // sum a.  Level h adds at most (2 h + 1) 2^-106 a of error, 48 2^-106 a over
 // the six levels; returns V = fl(s + e) and B = 2^-90 a + 2^-50 |V| with
-// |exact - V| <= B, both wave-uniform.  Needs -ffp-contract=off (no fused
-// operations inside TwoSum).
-__device__ __forceinline__ void wave_exact_sum(double p0, double p1, double& V, double& B) {
+// |exact - V| <= B, both wave-uniform.  `exact` (wave-uniform) is set when no
+// addition of the errors, nor the final one, rounded (each checked with
+// TwoSum): V is then the exact sum.  That is the common case, and the one
+// that matters: after heavy cancellation the exact sum has few significant
+// bits and can sit exactly on an fp32 tie, which no error bound decides.
+// Needs -ffp-contract=off (no fused operations inside TwoSum).
+__device__ __forceinline__ double two_sum_err(double x, double y, double s) {
+  const double b = s - x;
+  return (x - (s - b)) + (y - b);
+}
+__device__ __forceinline__ void wave_exact_sum(double p0, double p1, double& V, double& B, bool& exact) {
   double s = p0 + p1;
-  const double b0 = s - p0;
-  double e = (p0 - (s - b0)) + (p1 - b0);
+  double e = two_sum_err(p0, p1, s);
   double a = __builtin_fabs(p0) + __builtin_fabs(p1);
+  bool inexact = false;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
     const double s2 = __shfl_xor(s, m), e2 = __shfl_xor(e, m), a2 = __shfl_xor(a, m);
     const double sn = s + s2;
-    const double bn = sn - s;
-    const double t = (s - (sn - bn)) + (s2 - bn);
-    e = (e + e2) + t;
+    const double t = two_sum_err(s, s2, sn);
+    const double es = e + e2;
+    const double en = es + t;
+    inexact = inexact || two_sum_err(e, e2, es) != 0.0 || two_sum_err(es, t, en) != 0.0;
+    e = en;
     s = sn;
     a = a + a2;
   }
   V = s + e;
+  inexact = inexact || two_sum_err(s, e, V) != 0.0;
+  exact = __ballot(inexact) == 0;
   B = a * 0x1.0p-90 + __builtin_fabs(V) * 0x1.0p-50;
 }
 
@@ -292,7 +313,7 @@ __device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk, con
   double Er[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    Er[r] = 2.0 * D * 0x1.0p-53 * (__builtin_sqrt(L.nsq[t_base + 4 * r]) * (1.0 + 0x1.0p-40)) *
+    Er[r] = 2.0 * D * 0x1.0p-53 * sqrt_upper_pow2(L.nsq[t_base + 4 * r]) *
                 static_cast<double>(a.rot_row_max) * wide + 0x1.0p-1060;
 #pragma unroll
   for (int c = 0; c < CB; ++c)
@@ -319,10 +340,14 @@ __device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk, con
     const double p0 = L.kt[(2 * lane) * TKP + t] * static_cast<double>(L.rotT[(2 * lane) * D + i]);
     const double p1 = L.kt[(2 * lane + 1) * TKP + t] * static_cast<double>(L.rotT[(2 * lane + 1) * D + i]);
     double V, B;
-    wave_exact_sum(p0, p1, V, B);
+    bool exact;
+    wave_exact_sum(p0, p1, V, B, exact);
     B *= wide;
-    const float lo = static_cast<float>(V - B);
-    float yv = static_cast<float>(V + B);
+    // an exact V rounds directly (ties to even); the test hook's widest
+    // margins skip that, so that the integer path below is exercised
+    const bool direct = exact && wide < 0x1.0p32;
+    const float lo = static_cast<float>(direct ? V : V - B);
+    float yv = static_cast<float>(direct ? V : V + B);
     if (__float_as_uint(lo) != __float_as_uint(yv)) {   // wave-uniform
       float ex = 0.f;
       if (lane == 0) {
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
     double Er[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      Er[r] = 2.0 * D * 0x1.0p-53 * (__builtin_sqrt(L.nsq[t_base + 4 * r]) * (1.0 + 0x1.0p-40)) *
+      Er[r] = 2.0 * D * 0x1.0p-53 * sqrt_upper_pow2(L.nsq[t_base + 4 * r]) *
                   static_cast<double>(a.s_col_max) * wide + 0x1.0p-1060;
 #pragma unroll
     for (int c = 0; c < CB; ++c)
@@ -426,15 +451,17 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
       const double p1 = static_cast<double>(L.y[t][2 * lane + 1]) *
                         static_cast<double>(__uint_as_float(static_cast<uint32_t>(L.s_il[(2 * lane + 1) * D + lc]) << 16));
       double V, B;
-      wave_exact_sum(p0, p1, V, B);
+      bool exact;
+      wave_exact_sum(p0, p1, V, B, exact);
       B *= wide;
+      if (exact && wide < 0x1.0p32) B = 0.0;   // V is the exact sum
       int positive;
       if (V > B) {
         positive = 1;
       } else if (V < -B) {
         positive = 0;
       } else if (B == 0.0) {
-        positive = 1;   // every product is zero: the exact sum is 0, sign +1
+        positive = V >= 0.0 ? 1 : 0;   // exact: sign(0) = +1
       } else {
         int sg = 0;
         if (lane == 0) {
