@@ -550,8 +550,8 @@ def bench_rotq(qjl, w, args, T):
     the 32K GQA workload's keys, and TurboQuant scores of its 32 query heads
     over them.  The encodes run their rotation (and TurboQuant's residual
     sketch) in fp64, so they are priced against the fp64 peak; the scores
-    kernel reads 56 bytes per (token, kv head) and is bound by its LDS
-    lookups (reported against HBM for reference)."""
+    kernels read 56 bytes per (token, kv head) and write 4 bytes per (token,
+    query head), priced against HBM."""
     import torch
     B, Hq, Hkv, N, d = w.B, w.H_q, w.H_kv, w.N, w.d
     k = 2
@@ -608,7 +608,7 @@ def bench_rotq(qjl, w, args, T):
             "pq_encode_us": round(pq_ms * 1e3, 3), "pq_encode_keys_per_s": round(R / (pq_ms / 1e3), 1),
             "pq_encode_roofline": fp64(pq_flops, pq_ms),
             "tq_scores_us": round(sc_ms * 1e3, 3),
-            "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, None, "tq_query_kernel + tq_scores_kernel", sc_bytes),
+            "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, None, "tq_query_kernel + tq_scores_mfma_kernel", sc_bytes),
             "ring_sets": n_sets}
 
 

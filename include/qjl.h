@@ -145,9 +145,10 @@ QJL_API qjl_status qjl_tq_encode_keys(const void *keys_bf16, int32_t B, int32_t 
                                       uint32_t *bits, float *norms, float *gammas, int32_t cap,
                                       int32_t pos, void *stream);
 
-/* Workspace bytes of qjl_tq_scores: the prepared queries (Pi q and
- * S^T Pi q, fp32) of the B * H_q heads.  0 for invalid sizes.  Pure host
- * code. */
+/* Workspace bytes of qjl_tq_scores: the prepared queries of the B * H_q
+ * heads, 4096 bytes each (k = 3: Pi q and S^T Pi q in fp32; k = 1, 2: their
+ * integer byte-limb operands and scale factors).  0 for invalid sizes.  Pure
+ * host code. */
 QJL_API size_t qjl_tq_scores_workspace_bytes(int32_t B, int32_t H_q, int32_t d);
 
 /* TurboQuant_prod scores: the estimate of <q, k_t> for every query head and
@@ -162,7 +163,9 @@ QJL_API size_t qjl_tq_scores_workspace_bytes(int32_t B, int32_t H_q, int32_t d);
  * qjl_tq_scores_workspace_bytes(B, H_q, d) bytes; its contents are
  * overwritten (no zero-fill needed, and a workspace shared with
  * qjl_decode_attention must be zero-filled again before that call).  fp32
- * arithmetic (relative error ~1e-6 of the score scale).  Returns QJL_OK,
+ * arithmetic for k = 3; for k = 1, 2 exact integer dot products of the
+ * codes' bit-planes with the query side quantized to 2^-28 of its largest
+ * value, combined in fp32 (relative error ~1e-6 of the score scale).  Returns QJL_OK,
  * QJL_EINVAL, QJL_EWORKSPACE, QJL_EUNSUPPORTED, QJL_ENOMEM or QJL_EHIP. */
 QJL_API qjl_status qjl_tq_scores(const float *q, const uint32_t *codes, const uint32_t *bits,
                                  const float *norms, const float *gammas, int32_t B, int32_t H_q,

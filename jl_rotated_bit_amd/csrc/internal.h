@@ -106,6 +106,7 @@ struct RotqTables {
   const uint16_t* s_il = nullptr; // QJL sketch of seed + 1 with m = d, bf16 [i][l]
   const float* tq_cents = nullptr;  // TurboQuant centroids, k = 1..3 at 8 * (k - 1)
   const float* pq_thr = nullptr;    // PolarQuant thresholds [7 levels][8]
+  const float* qtab = nullptr;     // [j][r]: rows r of [Pi; S^T Pi] (2d of them), fp32
   float rot_row_max = 0.f;        // max_i ||Pi_i|| rounded up
   float s_col_max = 0.f;          // max_l ||S[:, l]|| rounded up
 };
@@ -117,7 +118,7 @@ constexpr int kPqBits[7] = {4, 2, 2, 2, 2, 2, 2};   // PolarQuant bits per level
 int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys, int B, int H_kv, int n,
                        uint32_t* codes, uint32_t* bits, float* norms, float* gammas, int cap, int pos,
                        int margin_log2, void* stream);
-// the scores' workspace: the prepared queries (Pi q, S^T Pi q), fp32
+// the scores' workspace: the prepared queries, 4096 bytes a query head
 size_t tq_scores_workspace_bytes(int B, int H_q);
 int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t* codes,
                      const uint32_t* bits, const float* norms, const float* gammas, int B, int H_q,

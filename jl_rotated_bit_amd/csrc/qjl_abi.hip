@@ -252,11 +252,29 @@ qjl_status get_rotq(uint64_t seed, qjl::RotqTables* out) {
     }
     smax = std::max(smax, std::sqrt(ss));
   }
+  // query table of the scores: [j][r] = row r of [Pi; M] at input j, M =
+  // S^T Pi (so S^T Pi q = M q in one pass); M from fp64 sums of the stored
+  // bf16 and fp32 entries, rounded to fp32
+  std::vector<float> qtab(static_cast<size_t>(2 * d) * d);
+  std::vector<double> m64(static_cast<size_t>(d) * d, 0.0);
+  for (int i = 0; i < d; ++i)
+    for (int l = 0; l < d; ++l) {
+      uint32_t u = static_cast<uint32_t>(s_il[i * d + l]) << 16;
+      float sf;
+      std::memcpy(&sf, &u, sizeof(sf));
+      for (int j = 0; j < d; ++j) m64[l * d + j] += static_cast<double>(sf) * rot[i * d + j];
+    }
+  for (int r = 0; r < d; ++r)
+    for (int j = 0; j < d; ++j) {
+      qtab[j * 2 * d + r] = rot[r * d + j];
+      qtab[j * 2 * d + d + r] = static_cast<float>(m64[r * d + j]);
+    }
   std::vector<float> cents(24, 0.f), thr(7 * 8, 0.f), pc(32);
   for (int k = 1; k <= 3; ++k) qjl::make_tq_codebook(d, k, cents.data() + 8 * (k - 1));
   for (int lev = 1; lev <= 7; ++lev) qjl::make_pq_codebook(lev, qjl::kPqBits[lev - 1], pc.data(), thr.data() + 8 * (lev - 1));
-  const size_t b_rot = d * d * 4, b_s = d * d * 2, b_c = 24 * 4, b_t = 56 * 4;
-  const size_t o_rotT = b_rot, o_s = 2 * b_rot, o_c = o_s + b_s, o_t = o_c + 256, total = o_t + b_t;
+  const size_t b_rot = d * d * 4, b_s = d * d * 2, b_c = 24 * 4, b_t = 56 * 4, b_q = qtab.size() * 4;
+  const size_t o_rotT = b_rot, o_s = 2 * b_rot, o_c = o_s + b_s, o_t = o_c + 256, o_q = o_t + 256,
+               total = o_q + b_q;
   void* mem = nullptr;
   e = hipMalloc(&mem, total);
   if (e != hipSuccess) return fail(QJL_ENOMEM, "hipMalloc(%zu) for the rotation tables: %s", total, hipGetErrorString(e));
@@ -266,6 +284,7 @@ qjl_status get_rotq(uint64_t seed, qjl::RotqTables* out) {
   if (e == hipSuccess) e = hipMemcpy(base + o_s, s_il.data(), b_s, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_c, cents.data(), b_c, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_t, thr.data(), b_t, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_q, qtab.data(), b_q, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(mem);
     return fail(QJL_EHIP, "uploading the rotation tables: %s", hipGetErrorString(e));
@@ -279,6 +298,7 @@ qjl_status get_rotq(uint64_t seed, qjl::RotqTables* out) {
   ent.view.pq_thr = reinterpret_cast<const float*>(base + o_t);
   ent.view.rot_row_max = round_up_f32(rmax);
   ent.view.s_col_max = round_up_f32(smax);
+  ent.view.qtab = reinterpret_cast<const float*>(base + o_q);
   g_rotq.emplace(key, ent);
   *out = ent.view;
   return QJL_OK;

@@ -425,7 +425,6 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
     }, L.kt, wave, lane, acc);
     __syncthreads();   // nsq (residual) ready
     const int t_base = 16 * (wave & 1) + (lane >> 4);
-    const int l_base = 16 * CB * (wave >> 1) + (lane & 15);
     uint32_t open = 0;
     double Er[4];
 #pragma unroll
@@ -642,47 +641,75 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
 // TurboQuant_prod scores: est_t = n_t (<Pi q, c[idx_t]> + sqrt(pi/2)/m g_t
 // <S^T Pi q, 2 bit_t - 1>) for every token t < N and query head
 // ---------------------------------------------------------------------------
-// Two kernels.  tq_query_kernel prepares each query head once: Pi q and
-// S^T Pi q (fp32 FMAs, coalesced reads of the transposed rotation and of S)
-// into the workspace.  tq_scores_kernel takes a range of tokens of one
-// (batch, kv head); its prologue builds nibble tables in LDS from the
-// prepared queries of the kv head's G query heads, the G heads' values of one
-// table entry side by side (so one 16-byte LDS read serves four heads): for
-// the sign words, the sum of S^T Pi q over the set bits of every 4-bit group;
-// for the codes, <Pi q, c[idx]> over the coordinates of a 4-bit group (4
-// coordinates at k = 1, 2 at k = 2; at k = 3 one table row per coordinate).
-// A thread then scores its tokens with one table read per nibble (per four
-// heads): 32 sign nibbles and 32, 64 or 128 code lookups at k = 1, 2, 3.
+// Two kernels.  tq_query_kernel prepares each query head once into the
+// workspace: Pi q and S^T Pi q (fp32 FMAs over one table [Pi; M], M =
+// S^T Pi) and, for k = 1, 2, their integer operands below.
+//
+// Scores for k = 1, 2 (tq_scores_mfma_kernel) are dot products of 0/1
+// bit-planes on the int8 matrix cores.  With idx = b0 + 2 b1, c[idx] = c0 +
+// (c1 - c0) b0 + (c2 - c0) b1 + (c3 - c2 - c1 + c0) b0 b1 (k = 1: c0 +
+// (c1 - c0) b0), so
+//   <Pi q, c[idx]> = c0 sum_i (Pi q)_i + sum over planes P of sum_i v_P,i P_i,
+// v_P = alpha_P Pi q, and <S^T Pi q, 2 bit - 1> = 2 sum_l s_l bit_l - sum_l s_l.
+// The prep quantizes every v_P (one exponent per head, from the largest
+// |v_P,i|) and s (likewise) to integers Q = round(v / 2^E), |Q| <= 2^30
+// (error at most 2^-31 of the largest |v| per term), written as four signed
+// byte limbs: the A operand of
+// v_mfma_i32_16x16x64_i8, rows = head x limb for four heads, held in
+// registers for the whole kernel.  The tokens' bit-planes, spread to 0/1
+// bytes with one shift and one mask per register, are the B operand
+// (columns = 16 tokens); the int32 sums are exact, and a lane of the result
+// holds the four limb rows of one head for one token, combined in registers.
+// Scores for k = 3 (tq_scores_kernel; 3-bit codes do not fall on byte lanes):
+// a workgroup takes a range of tokens of one (batch, kv head); its prologue
+// builds nibble tables in LDS from the prepared queries of the kv head's G
+// query heads, the G heads' values of one table entry side by side (so one
+// 16-byte LDS read serves four heads): for the sign words, the sum of
+// S^T Pi q over the set bits of every 4-bit group; for the codes, <Pi q,
+// c[idx]> of every coordinate's 8 codes.  A thread scores its tokens with one
+// table read per sign nibble and per coordinate (per four heads).
 
-// prepared query of head hq: [hq][0][D] = Pi q, [hq][1][D] = S^T Pi q
-constexpr int kQPrepFloats = 2 * D;
+// prepared query of head hq, kQPrepBytes apart: floats Pi q at [0, 512) and
+// S^T Pi q at [512, 1024); limb operands at [1024, 3072): 16 bytes per
+// (plane p, k-step ks, limb j, k-group g), p = 0..2 code planes (b0, b1,
+// b0 b1; k = 1 uses b0 only), p = 3 the sign plane; scalars at 3072: 2^E of
+// the code planes, 2^E of the sign plane, c0 sum_i (Pi q)_i, sum_l s_l.
+// rows of the query table: [Pi; M]
+constexpr int kQRows = 2 * D;
+constexpr int kQPrepBytes = 4096;
+constexpr int kQPrepFloats = kQPrepBytes / 4;
+constexpr int kLimbOffset = 1024;
+constexpr int kScalarOffset = 3072;
 
-// 256 threads per query head: thread (jp, i4) sums the products of 16
-// channels j (part jp of 8) for coordinates 4 i4 .. 4 i4 + 3 (one 16-byte
-// read of a row of the transposed rotation, or 8 bytes of S, per channel);
-// the 8 partial sums of a coordinate are then added in part order.
+// Workgroup (query head, half s) computes rows 128 s .. 128 s + 127 of
+// [Pi; M] q: half 0 Pi q, half 1 S^T Pi q = M q, so neither waits for the
+// other.  Thread (jp, i4) sums the products of 16 inputs j (part jp of 8)
+// for rows 4 i4 .. 4 i4 + 3 (one 16-byte read of the transposed table per
+// input); the 8 partial sums of a row are added in part order.  For k = 1,
+// 2 each half then writes the byte limbs of its planes (half 0 the code
+// planes, half 1 the sign plane) with the exponent of its own largest value,
+// and its sum.
 constexpr int kQueryThreads = 256;
 __global__ __launch_bounds__(kQueryThreads) void tq_query_kernel(const float* __restrict__ q,
-                                                                 const float* __restrict__ rotT,
-                                                                 const uint16_t* __restrict__ s_il,
-                                                                 float* __restrict__ prep) {
-  constexpr int PARTS = kQueryThreads / (D / 4);   // 8
-  constexpr int JP = D / PARTS;                    // 16 channels per part
-  __shared__ float qs[D], qr[D];
+                                                                 const float* __restrict__ qtab,
+                                                                 const float* __restrict__ cents, int K,
+                                                                 uint8_t* __restrict__ prep_bytes) {
+  constexpr int PARTS = kQueryThreads / (D / 4);   // 8 parts of 16 inputs
+  constexpr int JP = D / PARTS;                    // 16
+  __shared__ float qs[D], vals[D];
   __shared__ __attribute__((aligned(16))) float part[PARTS][D];
-  const int tid = threadIdx.x;
+  __shared__ float red[2][2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int i4 = tid % (D / 4), jp = tid / (D / 4);
+  const int s = blockIdx.y;
   const int64_t hq = blockIdx.x;
-  // every global read is issued up front (the matrices do not depend on q)
+  // the table reads do not depend on q: issued first
   float4 r[JP];
-  uint2 w[JP];
 #pragma unroll
-  for (int u = 0; u < JP; ++u) r[u] = reinterpret_cast<const float4*>(rotT + (jp * JP + u) * D)[i4];
-#pragma unroll
-  for (int u = 0; u < JP; ++u) w[u] = reinterpret_cast<const uint2*>(s_il + (jp * JP + u) * D)[i4];
+  for (int u = 0; u < JP; ++u)
+    r[u] = *reinterpret_cast<const float4*>(qtab + (jp * JP + u) * kQRows + D * s + 4 * i4);
   if (tid < D) qs[tid] = q[hq * D + tid];
   __syncthreads();
-  // (Pi q)_i = sum_j Pi[i][j] q_j; the transposed table puts Pi[i][j] at [j][i]
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int u = 0; u < JP; ++u) {
@@ -694,31 +721,71 @@ __global__ __launch_bounds__(kQueryThreads) void tq_query_kernel(const float* __
   }
   reinterpret_cast<float4*>(part[jp])[i4] = acc;
   __syncthreads();
+  float* prep = reinterpret_cast<float*>(prep_bytes + hq * kQPrepBytes);
+  float v = 0.f;
   if (tid < D) {
-    float v = 0.f;
 #pragma unroll
     for (int p2 = 0; p2 < PARTS; ++p2) v += part[p2][tid];
-    qr[tid] = v;
-    prep[hq * kQPrepFloats + tid] = v;
+    vals[tid] = v;
+    prep[D * s + tid] = v;   // Pi q at [0, D), S^T Pi q at [D, 2 D)
   }
-  __syncthreads();
-  // (S^T Pi q)_l = sum_i S[i][l] (Pi q)_i, S stored [i][l]
-  acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int u = 0; u < JP; ++u) {
-    const float qi = qr[jp * JP + u];
-    acc.x = __builtin_fmaf(__uint_as_float(w[u].x << 16), qi, acc.x);
-    acc.y = __builtin_fmaf(__uint_as_float(w[u].x & 0xFFFF0000u), qi, acc.y);
-    acc.z = __builtin_fmaf(__uint_as_float(w[u].y << 16), qi, acc.z);
-    acc.w = __builtin_fmaf(__uint_as_float(w[u].y & 0xFFFF0000u), qi, acc.w);
-  }
-  reinterpret_cast<float4*>(part[jp])[i4] = acc;
-  __syncthreads();
+  if (K == 3) return;   // the table kernel reads Pi q and S^T Pi q only
+  // the half's largest |value| and its sum (waves 0 and 1 hold the D values)
   if (tid < D) {
-    float v = 0.f;
+    float mx = __builtin_fabsf(v), sm = v;
+    for (int m = 32; m >= 1; m >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, m));
+      sm += __shfl_xor(sm, m);
+    }
+    if (lane == 0) {
+      red[wv][0] = mx;
+      red[wv][1] = sm;
+    }
+  }
+  __syncthreads();
+  // plane coefficients (k = 1: b0; k = 2: b0, b1, b0 b1)
+  const float c0 = cents[0];
+  const float alpha[3] = {cents[1] - c0, K == 2 ? cents[2] - c0 : 0.f,
+                          K == 2 ? (cents[3] - cents[2]) - (cents[1] - c0) : 0.f};
+  const bool code = s == 0;
+  const float amax = fmaxf(__builtin_fabsf(alpha[0]), fmaxf(__builtin_fabsf(alpha[1]), __builtin_fabsf(alpha[2])));
+  // every |fl(alpha_P x)| <= fl(amax max|x|) (rounding is monotonic), so
+  // with that < 2^(E + 30), |Q| <= 2^30 and the top limb fits a byte
+  const float top = (code ? amax : 1.f) * fmaxf(red[0][0], red[1][0]);
+  const int e = top > 0.f ? __builtin_amdgcn_frexp_expf(top) - 30 : 0;
+  // limb dword (((p 2 + ks) 4 + j) 4 + g) 4 + qq holds bytes b = 0..3 (byte
+  // x = 4 qq + b of the operand) of limb j of coordinate coord(p, g, ks, x)
+  uint32_t* limbs = reinterpret_cast<uint32_t*>(prep_bytes + hq * kQPrepBytes + kLimbOffset);
+  const int nd = code ? (K == 2 ? 3 : 1) * 128 : 128;
+  for (int t = tid; t < nd; t += kQueryThreads) {
+    const int qq = t & 3, g = (t >> 2) & 3, j = (t >> 4) & 3, ks = (t >> 6) & 1;
+    const int pl = code ? t >> 7 : 3;
+    const float al = pl == 0 ? alpha[0] : pl == 1 ? alpha[1] : alpha[2];
+    uint32_t word = 0;
 #pragma unroll
-    for (int p2 = 0; p2 < PARTS; ++p2) v += part[p2][tid];
-    prep[hq * kQPrepFloats + D + tid] = v;
+    for (int bb = 0; bb < 4; ++bb) {
+      int coord;
+      if (code && K == 2) coord = 16 * (2 * g + ks) + 4 * bb + qq;   // code word 2 g + ks, 2 bits a coordinate
+      else coord = 32 * g + 8 * bb + 4 * ks + qq;                    // one bit a coordinate
+      const float x = code ? al * vals[coord] : vals[coord];
+      const int Q = static_cast<int>(__builtin_rintf(__builtin_ldexpf(x, -e)));
+      // balanced base-256 digits: Q = l0 + 256 l1 + 65536 l2 + 2^24 l3
+      int rest = Q, lj = 0;
+#pragma unroll
+      for (int k2 = 0; k2 <= 3; ++k2) {
+        const int l = ((rest + 128) & 255) - 128;
+        if (k2 == j) lj = l;
+        rest = (rest - l) >> 8;
+      }
+      word |= (static_cast<uint32_t>(lj) & 255u) << (8 * bb);
+    }
+    limbs[(((pl * 2 + ks) * 4 + j) * 4 + g) * 4 + qq] = word;
+  }
+  if (tid == 0) {
+    float* sc = reinterpret_cast<float*>(prep_bytes + hq * kQPrepBytes + kScalarOffset);
+    const float sum = red[0][1] + red[1][1];
+    sc[code ? 0 : 1] = __builtin_ldexpf(1.0f, e);
+    sc[code ? 2 : 3] = code ? c0 * sum : sum;
   }
 }
 
@@ -740,18 +807,17 @@ __device__ __forceinline__ void add_entry(const float* e, float (&acc)[GH]) {
   }
 }
 
-// one token's cache row: code words, sign words, norm and gamma
-template <int K>
+// one token's cache row at k = 3: code words, sign words, norm and gamma
+constexpr int kTq3Words = D * 3 / 32;   // 12: whole 16-byte chunks
 struct TqRow {
-  uint32_t cw[D * K / 32];
+  uint32_t cw[kTq3Words];
   uint32_t bw[4];
   float n, g;
 };
-template <int K>
-__device__ __forceinline__ void load_tq_row(TqRow<K>& r, const uint32_t* __restrict__ codes,
+__device__ __forceinline__ void load_tq_row(TqRow& r, const uint32_t* __restrict__ codes,
                                             const uint32_t* __restrict__ bits, const float* __restrict__ norms,
                                             const float* __restrict__ gammas, int64_t row) {
-  constexpr int CW = D * K / 32;   // 4, 8 or 12: whole 16-byte chunks
+  constexpr int CW = kTq3Words;
 #pragma unroll
   for (int w4 = 0; w4 < CW / 4; ++w4) {
     const uint4 v = reinterpret_cast<const uint4*>(codes + row * CW)[w4];
@@ -769,14 +835,14 @@ __device__ __forceinline__ void load_tq_row(TqRow<K>& r, const uint32_t* __restr
   r.g = gammas[row];
 }
 
-template <int G, int K>
+template <int G>
 __global__ __launch_bounds__(256) void tq_scores_kernel(
     const float* __restrict__ prep, const uint32_t* __restrict__ codes, const uint32_t* __restrict__ bits,
     const float* __restrict__ norms, const float* __restrict__ gammas, const float* __restrict__ cents, int H_kv,
     int N, int cap, int tpw, float coef, float* __restrict__ out) {
-  constexpr int CW = D * K / 32;                       // code words per token
-  constexpr int CROWS = K == 3 ? D : D * K / 4;        // code-table rows
-  constexpr int CCOLS = K == 3 ? 8 : 16;
+  constexpr int CW = kTq3Words;                        // code words per token
+  constexpr int CROWS = D;                             // code-table rows (coordinates)
+  constexpr int CCOLS = 8;                             // codes
   __shared__ float qr[G][D];                           // Pi q
   __shared__ float qs[G][D];                           // S^T Pi q
   __shared__ __attribute__((aligned(16))) float lb[D / 4][16][G];   // sign-word nibbles
@@ -788,11 +854,11 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
   const int t_end = min(N, (static_cast<int>(blockIdx.x) + 1) * tpw);
   // the first token's row is in flight while the tables are built
   int t = blockIdx.x * tpw + tid;
-  TqRow<K> cur;
-  if (t < t_end) load_tq_row<K>(cur, codes, bits, norms, gammas, bh * cap + t);
-  float c[1 << K];
+  TqRow cur;
+  if (t < t_end) load_tq_row(cur, codes, bits, norms, gammas, bh * cap + t);
+  float c[8];
 #pragma unroll
-  for (int v = 0; v < (1 << K); ++v) c[v] = cents[v];
+  for (int v = 0; v < 8; ++v) c[v] = cents[v];
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, i = e % D;
     const float* p = prep + (bh * G + h) * kQPrepFloats;
@@ -809,17 +875,7 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
   }
   for (int e = tid; e < CROWS * CCOLS * G; e += 256) {
     const int h = e % G, col = (e / G) % CCOLS, row = e / (G * CCOLS);
-    float v;
-    if constexpr (K == 1) {
-      v = 0.f;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) v += qr[h][4 * row + bb] * c[(col >> bb) & 1];
-    } else if constexpr (K == 2) {
-      v = qr[h][2 * row] * c[col & 3] + qr[h][2 * row + 1] * c[col >> 2];
-    } else {
-      v = qr[h][row] * c[col];
-    }
-    lc[row][col][h] = v;
+    lc[row][col][h] = qr[h][row] * c[col];
   }
   if (tid < G) {
     float s2 = 0.f;
@@ -830,8 +886,8 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
 #pragma unroll 1
   for (; t < t_end; t += 256) {
     // the next token's row loads while this one is scored
-    TqRow<K> nxt = cur;
-    if (t + 256 < t_end) load_tq_row<K>(nxt, codes, bits, norms, gammas, bh * cap + t + 256);
+    TqRow nxt = cur;
+    if (t + 256 < t_end) load_tq_row(nxt, codes, bits, norms, gammas, bh * cap + t + 256);
     const uint32_t* cwd = cur.cw;
     const uint32_t* bw = cur.bw;
     const float n = cur.n, g = cur.g;
@@ -859,17 +915,12 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
         mse[h] = 0.f;
         pos[h] = 0.f;
       }
-      if constexpr (K == 3) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-          const int bpos = 3 * i;
-          uint32_t idx = cw2[bpos >> 5] >> (bpos & 31);
-          if ((bpos & 31) > 29) idx |= cw2[(bpos >> 5) + 1] << (32 - (bpos & 31));
-          add_entry<GH>(&lc[i][idx & 7][h0], mse);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < CROWS; ++r) add_entry<GH>(&lc[r][(cw2[r >> 3] >> (4 * (r & 7))) & 15][h0], mse);
+      for (int i = 0; i < D; ++i) {
+        const int bpos = 3 * i;
+        uint32_t idx = cw2[bpos >> 5] >> (bpos & 31);
+        if ((bpos & 31) > 29) idx |= cw2[(bpos >> 5) + 1] << (32 - (bpos & 31));
+        add_entry<GH>(&lc[i][idx & 7][h0], mse);
       }
 #pragma unroll
       for (int r = 0; r < D / 4; ++r) add_entry<GH>(&lb[r][(bw2[r >> 3] >> (4 * (r & 7))) & 15][h0], pos);
@@ -882,6 +933,144 @@ __global__ __launch_bounds__(256) void tq_scores_kernel(
   }
 }
 
+
+typedef int i32x4_t __attribute__((__vector_size__(4 * sizeof(int))));
+
+// 0/1 bytes of one token's bit-plane for one k-step: register q, byte b =
+// bit 8 b + sh + step q of word w (the limb operand was laid out to match)
+template <int STEP>
+__device__ __forceinline__ i32x4_t plane_bytes(uint32_t w, int sh) {
+  i32x4_t v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = static_cast<int>((w >> (sh + STEP * q)) & 0x01010101u);
+  return v;
+}
+
+// the tokens' rows of one 64-token chunk of a wave: lane (row, grp) holds
+// token t0 + 16 u + row's code words (k = 2: words 2 grp, 2 grp + 1; k = 1:
+// word grp), its sign word grp, norm and gamma
+template <int K>
+struct TqChunk {
+  uint32_t c0[4], c1[4], sw[4];
+  float n[4], g[4];
+};
+template <int K>
+__device__ __forceinline__ void load_tq_chunk(TqChunk<K>& c, const uint32_t* __restrict__ codes,
+                                              const uint32_t* __restrict__ bits, const float* __restrict__ norms,
+                                              const float* __restrict__ gammas, int64_t base, int t0, int row,
+                                              int grp, int last) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t r = base + min(t0 + 16 * u + row, last);
+    if constexpr (K == 2) {
+      const uint2 v = reinterpret_cast<const uint2*>(codes + r * 8)[grp];
+      c.c0[u] = v.x;
+      c.c1[u] = v.y;
+    } else {
+      c.c0[u] = codes[r * 4 + grp];
+      c.c1[u] = 0;
+    }
+    c.sw[u] = bits[r * 4 + grp];
+    c.n[u] = norms[r];
+    c.g[u] = gammas[r];
+  }
+}
+
+// k = 1, 2: a workgroup of four waves takes 256-token chunks of one (batch,
+// kv head); a wave scores 64 tokens a pass as four 16-token tiles.  The
+// limb operands of the kv head's G query heads stay in registers (rows 4 h'
+// + j of row block rb: head 4 rb + h', limb j; zero rows past G); the result
+// lane (row, grp) of row block rb holds head 4 rb + grp's four limb sums for
+// token row of the tile.
+template <int G, int K>
+__global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
+    const uint8_t* __restrict__ prep, const uint32_t* __restrict__ codes, const uint32_t* __restrict__ bits,
+    const float* __restrict__ norms, const float* __restrict__ gammas, int H_kv, int N, int cap, int tpw,
+    float coef, float* __restrict__ out) {
+  constexpr int NRB = (G + 3) / 4;
+  constexpr int NP = K == 2 ? 3 : 1;   // code planes
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = static_cast<int64_t>(b) * H_kv + kvh;
+  const int64_t base = bh * cap;
+  const int t_end = min(N, (static_cast<int>(blockIdx.x) + 1) * tpw);
+  int t0 = blockIdx.x * tpw + 64 * wave;
+  // the first chunk's rows are in flight while the operands load
+  TqChunk<K> cur;
+  if (t0 < t_end) load_tq_chunk<K>(cur, codes, bits, norms, gammas, base, t0, row, grp, N - 1);
+  i32x4_t ac[NRB][NP][2], as[NRB][2];
+  float4 sc[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int h = 4 * rb + (row >> 2), j = row & 3;
+    const uint8_t* lp = prep + (bh * G + h) * kQPrepBytes + kLimbOffset + (j * 4 + grp) * 16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        ac[rb][p][ks] = h < G ? *reinterpret_cast<const i32x4_t*>(lp + (p * 2 + ks) * 256) : i32x4_t{0, 0, 0, 0};
+      as[rb][ks] = h < G ? *reinterpret_cast<const i32x4_t*>(lp + (3 * 2 + ks) * 256) : i32x4_t{0, 0, 0, 0};
+    }
+    const int ho = 4 * rb + grp;
+    sc[rb] = ho < G ? *reinterpret_cast<const float4*>(prep + (bh * G + ho) * kQPrepBytes + kScalarOffset)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll 1
+  for (; t0 < t_end; t0 += 256) {
+    // the next pass's rows load while this one is scored
+    TqChunk<K> nxt = cur;
+    if (t0 + 256 < t_end) load_tq_chunk<K>(nxt, codes, bits, norms, gammas, base, t0 + 256, row, grp, N - 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      i32x4_t bc[NP][2], bs[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (K == 2) {
+          // word 2 grp + ks: coordinate 16 (2 grp + ks) + 4 b + q at bits
+          // 8 b + 2 q (b0) and 8 b + 2 q + 1 (b1)
+          const uint32_t w = ks ? cur.c1[u] : cur.c0[u];
+          bc[0][ks] = plane_bytes<2>(w, 0);
+          bc[1][ks] = plane_bytes<2>(w, 1);
+          bc[2][ks] = plane_bytes<2>(w & (w >> 1), 0);
+        } else {
+          // word grp: coordinate 32 grp + 8 b + 4 ks + q at bit 8 b + 4 ks + q
+          bc[0][ks] = plane_bytes<1>(cur.c0[u], 4 * ks);
+        }
+        bs[ks] = plane_bytes<1>(cur.sw[u], 4 * ks);
+      }
+      const int t = t0 + 16 * u + row;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        i32x4_t accc = {0, 0, 0, 0}, accs = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int p = 0; p < NP; ++p)
+            accc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ac[rb][p][ks], bc[p][ks], accc, 0, 0, 0);
+          accs = __builtin_amdgcn_mfma_i32_16x16x64_i8(as[rb][ks], bs[ks], accs, 0, 0, 0);
+        }
+        // sum_j 256^j acc[j], highest limb first (the partial sums below
+        // 2^24 are exact in fp32)
+        const float vc = __builtin_fmaf(
+            __builtin_fmaf(__builtin_fmaf(static_cast<float>(accc[3]), 256.f, static_cast<float>(accc[2])), 256.f,
+                           static_cast<float>(accc[1])),
+            256.f, static_cast<float>(accc[0]));
+        const float vs = __builtin_fmaf(
+            __builtin_fmaf(__builtin_fmaf(static_cast<float>(accs[3]), 256.f, static_cast<float>(accs[2])), 256.f,
+                           static_cast<float>(accs[1])),
+            256.f, static_cast<float>(accs[0]));
+        const float mse = __builtin_fmaf(sc[rb].x, vc, sc[rb].z);
+        const float pos = sc[rb].y * vs;
+        const int ho = 4 * rb + grp;
+        if (ho < G && t < t_end)
+          out[(bh * G + ho) * static_cast<int64_t>(N) + t] =
+              cur.n[u] * (mse + coef * cur.g[u] * (2.f * pos - sc[rb].w));
+      }
+    }
+    cur = nxt;
+  }
+}
 }  // namespace
 
 int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys, int B, int H_kv, int n,
@@ -925,7 +1114,7 @@ int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys
 }
 
 size_t tq_scores_workspace_bytes(int B, int H_q) {
-  return static_cast<size_t>(B) * H_q * kQPrepFloats * sizeof(float);
+  return static_cast<size_t>(B) * H_q * kQPrepBytes;
 }
 
 int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t* codes,
@@ -935,35 +1124,50 @@ int launch_tq_scores(const RotqTables& tb, int k, const float* q, const uint32_t
   // sqrt(pi/2) / m with m = d
   const float coef = static_cast<float>(1.2533141373155002512 / D);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* prep = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(tq_query_kernel, dim3(B * H_q), dim3(kQueryThreads), 0, st, q, tb.rotT, tb.s_il, prep);
-  // about two workgroups per compute unit, each a multiple of 256 tokens
+  uint8_t* prep_bytes = static_cast<uint8_t*>(workspace);
+  const float* prep = static_cast<const float*>(workspace);
+  const float* cents = tb.tq_cents + 8 * (k - 1);
+  hipLaunchKernelGGL(tq_query_kernel, dim3(B * H_q, 2), dim3(kQueryThreads), 0, st, q, tb.qtab, cents, k,
+                     prep_bytes);
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t heads = static_cast<int64_t>(B) * H_kv;
+  if (k != 3) {
+    // up to eight workgroups per compute unit, each a multiple of 256 tokens
+    const int64_t chunks = (N + 255) / 256;
+    const int64_t want8 = 8 * static_cast<int64_t>(cus) / heads, want = want8 > 1 ? want8 : 1;
+    const int tpw = static_cast<int>((chunks + want - 1) / want * 256);
+    dim3 grid((N + tpw - 1) / tpw, H_kv, B);
+#define QJL_TQ_MFMA(GG)                                                                                       \
+  if (k == 1) hipLaunchKernelGGL((tq_scores_mfma_kernel<GG, 1>), grid, dim3(256), 0, st, prep_bytes, codes, bits, \
+                                 norms, gammas, H_kv, N, cap, tpw, coef, out);                                  \
+  else hipLaunchKernelGGL((tq_scores_mfma_kernel<GG, 2>), grid, dim3(256), 0, st, prep_bytes, codes, bits, norms, \
+                          gammas, H_kv, N, cap, tpw, coef, out)
+    switch (G) {
+      case 1: QJL_TQ_MFMA(1); break;
+      case 2: QJL_TQ_MFMA(2); break;
+      case 4: QJL_TQ_MFMA(4); break;
+      case 8: QJL_TQ_MFMA(8); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef QJL_TQ_MFMA
+    return hipGetLastError();
+  }
+  // k = 3: about two workgroups per compute unit, each a multiple of 256 tokens
   const int64_t want = (2 * static_cast<int64_t>(cus) + heads - 1) / heads;
   const int64_t per = (N + want - 1) / want;
   const int tpw = static_cast<int>((per + 255) / 256 * 256);
   dim3 grid((N + tpw - 1) / tpw, H_kv, B);
-  const float* cents = tb.tq_cents + 8 * (k - 1);
-#define QJL_TQ_SCORES(GG, KK)                                                                          \
-  hipLaunchKernelGGL((tq_scores_kernel<GG, KK>), grid, dim3(256), 0, st, prep, codes, bits, norms, gammas, \
-                     cents, H_kv, N, cap, tpw, coef, out)
-#define QJL_TQ_SCORES_K(GG)            \
-  switch (k) {                         \
-    case 1: QJL_TQ_SCORES(GG, 1); break; \
-    case 2: QJL_TQ_SCORES(GG, 2); break; \
-    case 3: QJL_TQ_SCORES(GG, 3); break; \
-    default: return hipErrorInvalidValue; \
-  }
+#define QJL_TQ_SCORES(GG)                                                                              \
+  hipLaunchKernelGGL((tq_scores_kernel<GG>), grid, dim3(256), 0, st, prep, codes, bits, norms, gammas, cents, \
+                     H_kv, N, cap, tpw, coef, out)
   switch (G) {
-    case 1: QJL_TQ_SCORES_K(1); break;
-    case 2: QJL_TQ_SCORES_K(2); break;
-    case 4: QJL_TQ_SCORES_K(4); break;
-    case 8: QJL_TQ_SCORES_K(8); break;
+    case 1: QJL_TQ_SCORES(1); break;
+    case 2: QJL_TQ_SCORES(2); break;
+    case 4: QJL_TQ_SCORES(4); break;
+    case 8: QJL_TQ_SCORES(8); break;
     default: return hipErrorInvalidValue;
   }
-#undef QJL_TQ_SCORES_K
 #undef QJL_TQ_SCORES
   return hipGetLastError();
 }

@@ -96,7 +96,7 @@ void sizes() {
   CHECK(qjl_decode_num_splits(1, 32, 8, 32768, 128, 256) > 1);
   CHECK(qjl_decode_workspace_bytes(1, 32, 8, 32768, 128, 384) == 0);
   CHECK(qjl_decode_num_splits(0, 32, 8, 32768, 128, 256) <= 0);
-  CHECK(qjl_tq_scores_workspace_bytes(2, 8, 128) == 2 * 8 * 2 * 128 * 4);
+  CHECK(qjl_tq_scores_workspace_bytes(2, 8, 128) == 2 * 8 * 4096);
   CHECK(qjl_tq_scores_workspace_bytes(0, 8, 128) == 0);
   CHECK(qjl_tq_scores_workspace_bytes(2, 8, 64) == 0);
 }

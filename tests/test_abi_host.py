@@ -338,9 +338,9 @@ def test_rotq_entry_point_validation(lib):
     assert "misaligned" in qjl.last_error()
     assert tqs(lib, codes=A16 + 4) == EINVAL and tqs(lib, bits=A16 + 8) == EINVAL   # 16 B
     assert tqs(lib, B=70000, Hq=70000, Hkv=70000, N=1, cap=1) == EINVAL
-    # the workspace holds Pi q and S^T Pi q of every query head
+    # the workspace holds 4096 bytes of prepared query per query head
     need = lib.qjl_tq_scores_workspace_bytes(2, 8, 128)
-    assert need == 2 * 8 * 2 * 128 * 4
+    assert need == 2 * 8 * 4096
     assert lib.qjl_tq_scores_workspace_bytes(0, 8, 128) == 0
     assert lib.qjl_tq_scores_workspace_bytes(2, 8, 64) == 0
     assert tqs(lib, B=2, Hq=8, Hkv=2, ws=None) == EWS

@@ -16,7 +16,7 @@ from oracle import polarquant as opq
 from oracle import turboquant as otq
 from jl_rotated_bit_amd import workloads as wl
 
-from .gpu_util import SENTINEL, dev_f32, dev_u16, host_u32, say
+from .gpu_util import SENTINEL, dev_f32, dev_u16, dev_u32, host_u32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -136,6 +136,28 @@ def test_tq_scores(gpu_lib, G, k):
     got = gpu_lib.tq_scores(dev_f32(q), codes, bits, norms, gammas, N, SEED, k)
     torch.cuda.synchronize()
     ref = otq.scores(q, host_u32(codes), host_u32(bits), norms.cpu().numpy(), gammas.cpu().numpy(), N, k, SEED)
+    got = got.cpu().numpy().astype(np.float64)
+    scale = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+    assert np.max(np.abs(got - ref) / scale) <= 1e-5
+
+
+@pytest.mark.parametrize("G,k", [(4, 2), (8, 1), (8, 2), (1, 1)])
+def test_tq_scores_many_passes(gpu_lib, G, k):
+    """Caches long enough that every wave of the matrix-core scores kernel
+    takes several passes over several workgroups, from random bit patterns
+    (every pattern is a valid cache), with a ragged end."""
+    import torch
+    rng = np.random.default_rng(60 + 10 * G + k)
+    B, Hkv, N, cap = 1, 2, 300_001, 300_016
+    codes = rng.integers(0, 2 ** 32, (B, Hkv, cap, D * k // 32), dtype=np.uint64).astype(np.uint32)
+    bits = rng.integers(0, 2 ** 32, (B, Hkv, cap, D // 32), dtype=np.uint64).astype(np.uint32)
+    norms = rng.uniform(0.5, 4.0, (B, Hkv, cap)).astype(np.float32)
+    gammas = rng.uniform(0.0, 1.0, (B, Hkv, cap)).astype(np.float32)
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float32)
+    say("tq scores many passes", "G", G, "k", k, "N", N)
+    got = gpu_lib.tq_scores(dev_f32(q), dev_u32(codes), dev_u32(bits), dev_f32(norms), dev_f32(gammas), N, SEED, k)
+    torch.cuda.synchronize()
+    ref = otq.scores(q, codes, bits, norms, gammas, N, k, SEED)
     got = got.cpu().numpy().astype(np.float64)
     scale = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
     assert np.max(np.abs(got - ref) / scale) <= 1e-5
