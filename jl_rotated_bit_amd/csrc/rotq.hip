@@ -371,6 +371,7 @@ __device__ void rotate_tile(RotqLds& L, const RotqArgs& a, int row0, int nk, con
 // ---------------------------------------------------------------------------
 // TurboQuant_prod encode
 // ---------------------------------------------------------------------------
+template <int K>
 __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
   __shared__ __attribute__((aligned(16))) RotqLds L;
   const int tid = threadIdx.x;
@@ -379,11 +380,12 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
     reinterpret_cast<float4*>(L.rotT)[e] = reinterpret_cast<const float4*>(a.rotT)[e];
   for (int e = tid; e < D * D / 8; e += NT)
     reinterpret_cast<uint4*>(L.s_il)[e] = reinterpret_cast<const uint4*>(a.s_il)[e];
-  const int K = a.k;
-  const int L2 = 1 << K;
-  float cents[8], bnds[7];
-  for (int v = 0; v < 8; ++v) cents[v] = v < L2 ? a.cents[v] : 0.f;
-  for (int v = 0; v < 7; ++v) bnds[v] = v < L2 - 1 ? 0.5f * (cents[v] + cents[v + 1]) : INFINITY;
+  constexpr int L2 = 1 << K;
+  float cents[L2], bnds[L2 - 1];
+#pragma unroll
+  for (int v = 0; v < L2; ++v) cents[v] = a.cents[v];
+#pragma unroll
+  for (int v = 0; v < L2 - 1; ++v) bnds[v] = 0.5f * (cents[v] + cents[v + 1]);
   const double wide = __builtin_ldexp(1.0, a.margin_log2);
   __syncthreads();
 
@@ -396,25 +398,32 @@ __global__ __launch_bounds__(NT) void tq_encode_kernel(RotqArgs a, int tiles) {
     // the next tile's keys load while this one is encoded
     const int next = tile + gridDim.x;
     if (next < tiles) load_key_regs(kr, a, next * TK, min(TK, a.R - next * TK));
-    // u, codes, residual (thread per (coordinate, key half))
-    const int i = tid & (D - 1), h = tid >> 7;   // h < NT / D
-    for (int u8 = 0; u8 < TK * D / NT; ++u8) {
-      const int t = (TK * D / NT) * h + u8;
-      const float n = L.nrm[t];
-      const float u = n > 0.f ? L.y[t][i] / n : 0.f;
-      int idx = 0;
-      for (int v = 0; v < L2 - 1; ++v) idx += u >= bnds[v] ? 1 : 0;
-      float c = cents[0];
-      for (int v = 1; v < L2; ++v) c = idx == v ? cents[v] : c;
-      const float r = u - c;
-      L.cell[t][i] = static_cast<uint8_t>(idx);
-      L.y[t][i] = r;   // the residual replaces y
-    }
-    __syncthreads();
-    // residuals -> fp64 [i][t]; g in coordinate order
-    for (int e = tid; e < TK * D; e += NT) {
-      const int t = e / D, ii = e % D;
-      L.kt[ii * TKP + t] = static_cast<double>(L.y[t][ii]);
+    // u, codes, residual (thread per (coordinate, quarter of the keys); the
+    // reads are issued together)
+    {
+      constexpr int PT = TK * D / NT;   // keys per thread
+      const int i = tid & (D - 1), h = tid >> 7;
+      float yv[PT], nv[PT];
+#pragma unroll
+      for (int u8 = 0; u8 < PT; ++u8) {
+        nv[u8] = L.nrm[PT * h + u8];
+        yv[u8] = L.y[PT * h + u8][i];
+      }
+#pragma unroll
+      for (int u8 = 0; u8 < PT; ++u8) {
+        const int t = PT * h + u8;
+        const float u = nv[u8] > 0.f ? yv[u8] / nv[u8] : 0.f;
+        int idx = 0;
+#pragma unroll
+        for (int v = 0; v < L2 - 1; ++v) idx += u >= bnds[v] ? 1 : 0;
+        float c = cents[0];
+#pragma unroll
+        for (int v = 1; v < L2; ++v) c = idx == v ? cents[v] : c;
+        const float r = u - c;
+        L.cell[t][i] = static_cast<uint8_t>(idx);
+        L.y[t][i] = r;                                   // the residual replaces y
+        L.kt[i * TKP + t] = static_cast<double>(r);     // and the keys, as fp64 [i][t]
+      }
     }
     __syncthreads();
     if (tid < TK) L.nsq[tid] = ordered_sumsq(L.kt, tid);
@@ -549,9 +558,15 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
     rotate_tile(L, a, row0, nk, kr);
     const int next = tile + gridDim.x;
     if (next < tiles) load_key_regs(kr, a, next * TK, min(TK, a.R - next * TK));
+    // Each wave takes the levels of its own KPW keys, so the levels need no
+    // workgroup barrier (a wave's LDS accesses complete in order; the fences
+    // keep the compiler from moving them).  A key keeps the same D / 2 slots
+    // of each sum buffer at every level, so no wave touches another's keys.
     // level 1: pair cells and the pairs' sums of squares
-    for (int e = tid; e < TK * (D / 2); e += NT) {
-      const int t = e / (D / 2), j = e % (D / 2);
+    constexpr int KPW = TK / (NT / 64);
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int r = 0; r < KPW; ++r) {
+      const int t = KPW * wave + r, j = lane;
       const double av = static_cast<double>(L.y[t][2 * j]);
       const double bv = static_cast<double>(L.y[t][2 * j + 1]);
       int q;
@@ -574,7 +589,7 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
       L.cell[t][j] = static_cast<uint8_t>(q * ((1 << kBits[0]) / 4) + within);
       sq[t * (D / 2) + j] = av * av + bv * bv;   // [t][pair]
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     // levels 2 .. 7: cells from the slice sums, then the pairwise sums
     // (ping-pong between two halves of the key tile's LDS)
     double* cur = sq;
@@ -584,24 +599,26 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
     for (int lev = 2; lev <= PQ_LEVELS; ++lev) {
       const int half = width / 2;
       const int nthr = (1 << kBits[lev - 1]) - 1;
-      for (int e = tid; e < TK * half; e += NT) {
-        const int t = e / half, j = e % half;
-        const double sa = cur[t * width + 2 * j], sb = cur[t * width + 2 * j + 1];
+      for (int e = lane; e < KPW * half; e += 64) {
+        const int t = KPW * wave + e / half, j = e % half;
+        const double sa = cur[t * (D / 2) + 2 * j], sb = cur[t * (D / 2) + 2 * j + 1];
         int c = 0;
         for (int u = 0; u < nthr; ++u) {
           const double T = static_cast<double>(L.thr[(lev - 1) * PQ_MAXT + u]);
           c += sb >= (T * T) * sa ? 1 : 0;
         }
         L.cell[t][cell_off + j] = static_cast<uint8_t>(c);
-        nxt[t * half + j] = sa + sb;
+        nxt[t * (D / 2) + j] = sa + sb;
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       double* tmp = cur;
       cur = nxt;
       nxt = tmp;
       cell_off += half;
       width = half;
     }
+    if (lane < KPW) L.nsq[KPW * wave + lane] = cur[(KPW * wave + lane) * (D / 2)];   // the top-level sums
+    __syncthreads();   // every key's cells and sums
     // stream: level 1 cells (4 bits each), then 2-bit cells of levels 2..7
     for (int e = tid; e < TK * PQ_WORDS; e += NT) {
       const int t = e / PQ_WORDS, w = e % PQ_WORDS;
@@ -631,7 +648,7 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
     }
     if (tid < nk) {
       const int64_t row = dest_row(a.r0 + row0 + tid, static_cast<uint32_t>(a.n), a.cap, a.pos);
-      a.radii[row] = static_cast<float>(__builtin_sqrt(cur[tid]));
+      a.radii[row] = static_cast<float>(__builtin_sqrt(L.nsq[tid]));
     }
     __syncthreads();
   }
@@ -1108,7 +1125,14 @@ int launch_rotq_encode(const RotqTables& tb, int method, int k, const void* keys
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int grid = tiles < cus ? tiles : cus;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (method == 0) hipLaunchKernelGGL(tq_encode_kernel, dim3(grid), dim3(NT), 0, st, a, tiles);
+  if (method == 0) {
+    switch (k) {
+      case 1: hipLaunchKernelGGL(tq_encode_kernel<1>, dim3(grid), dim3(NT), 0, st, a, tiles); break;
+      case 2: hipLaunchKernelGGL(tq_encode_kernel<2>, dim3(grid), dim3(NT), 0, st, a, tiles); break;
+      case 3: hipLaunchKernelGGL(tq_encode_kernel<3>, dim3(grid), dim3(NT), 0, st, a, tiles); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   else hipLaunchKernelGGL(pq_encode_kernel, dim3(grid), dim3(NT), 0, st, a, tiles);
   return hipGetLastError();
 }
