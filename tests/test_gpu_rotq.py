@@ -163,6 +163,35 @@ def test_tq_scores_many_passes(gpu_lib, G, k):
     assert np.max(np.abs(got - ref) / scale) <= 1e-5
 
 
+@pytest.mark.parametrize("k", [1, 2, 3])
+@pytest.mark.parametrize("N", [1, 17])
+def test_tq_scores_edge_queries(gpu_lib, k, N):
+    """Very short caches, and query heads that are zero, or scaled by 2^70
+    or 2^-70 (the limbs' exponent follows each head's own largest value)."""
+    import torch
+    rng = np.random.default_rng(70 + 10 * k + N)
+    G, B, Hkv, cap = 4, 1, 2, N + 3
+    keys = wl.gaussian_keys(rng, B * Hkv * cap, scale=2.0).reshape(B, Hkv, cap, D)
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float32)
+    q[0, 0] = 0.0
+    q[0, 1] *= np.float32(2.0 ** 70)
+    q[0, 2] *= np.float32(2.0 ** -70)
+    q[0, 5] = 0.0
+    codes, bits, norms, gammas = gpu_tq(gpu_lib, keys, k)
+    say("tq scores edge queries", "k", k, "N", N)
+    got = gpu_lib.tq_scores(dev_f32(q), codes, bits, norms, gammas, N, SEED, k)
+    torch.cuda.synchronize()
+    ref = otq.scores(q, host_u32(codes), host_u32(bits), norms.cpu().numpy(), gammas.cpu().numpy(), N, k, SEED)
+    got = got.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    for h in range(Hkv * G):
+        if not np.any(q[0, h]):
+            assert np.all(got[0, h] == 0.0), h
+            continue
+        scale = np.sqrt(np.mean(ref[0, h] ** 2))
+        assert np.max(np.abs(got[0, h] - ref[0, h])) <= 1e-5 * scale, h
+
+
 def test_tq_scores_track_exact_inner_products(gpu_lib):
     """Quality reading (not parity): over many keys the scores are unbiased
     estimates of <q, k> with the relative spread the oracle predicts."""
