@@ -551,7 +551,8 @@ def bench_rotq(qjl, w, args, T):
     over them.  The encodes run their rotation (and TurboQuant's residual
     sketch) in fp64, so they are priced against the fp64 peak; the scores
     kernels read 56 bytes per (token, kv head) and write 4 bytes per (token,
-    query head), priced against HBM."""
+    query head), priced against HBM, at batch 1 and (random cache contents)
+    at batch 8."""
     import torch
     B, Hq, Hkv, N, d = w.B, w.H_q, w.H_kv, w.N, w.d
     k = 2
@@ -593,6 +594,35 @@ def bench_rotq(qjl, w, args, T):
         f"{pq_ms * 1e3:.1f} us, TurboQuant scores {sc_ms * 1e3:.1f} us")
     del sets
     torch.cuda.empty_cache()
+    # The scores at batch 8 of the same shape, where the launch and latency
+    # costs are spread over 8x the bytes.  Cache contents are seeded random
+    # bit patterns (every pattern is a valid cache), norms in [0.5, 4),
+    # residual norms in [0, 1).
+    B8 = 8
+    b8_bytes = B8 * Hkv * N * (d * k // 8 + d // 8 + 8) + B8 * Hq * N * 4
+    n8 = ring_sets(b8_bytes)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    sets8 = []
+    for _ in range(n8):
+        sets8.append(dict(
+            codes=torch.randint(-2 ** 31, 2 ** 31, (B8, Hkv, N, d * k // 32), dtype=torch.int32, device="cuda",
+                                generator=g),
+            bits=torch.randint(-2 ** 31, 2 ** 31, (B8, Hkv, N, d // 32), dtype=torch.int32, device="cuda", generator=g),
+            norms=torch.rand((B8, Hkv, N), device="cuda", generator=g) * 3.5 + 0.5,
+            gammas=torch.rand((B8, Hkv, N), device="cuda", generator=g),
+            q=torch.randn((B8, Hq, d), device="cuda", generator=g),
+            scores=torch.empty((B8, Hq, N), dtype=torch.float32, device="cuda")))
+
+    def sc8(i):
+        s = sets8[i % n8]
+        qjl.tq_scores(s["q"], s["codes"], s["bits"], s["norms"], s["gammas"], N, SEED, k, out=s["scores"])
+    for i in range(n8):
+        sc8(i)
+    sc8_ms = T.b2b(sc8, reps)
+    log(f"[bench] rotq: TurboQuant scores at batch 8 {sc8_ms * 1e3:.1f} us")
+    del sets8
+    torch.cuda.empty_cache()
     tq_flops = R * 2.0 * (2 * d * d)            # rotation + residual sketch (m = d)
     pq_flops = R * 2.0 * d * d                  # rotation
     sc_bytes = R * (d * k // 8 + d // 8 + 8) + B * Hq * N * 4
@@ -609,6 +639,9 @@ def bench_rotq(qjl, w, args, T):
             "pq_encode_roofline": fp64(pq_flops, pq_ms),
             "tq_scores_us": round(sc_ms * 1e3, 3),
             "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, None, "tq_query_kernel + tq_scores_mfma_kernel", sc_bytes),
+            "tq_scores_batch8_us": round(sc8_ms * 1e3, 3),
+            "tq_scores_batch8_roofline": roofline(b8_bytes / (sc8_ms / 1e3) / 1e9, None,
+                                                  "tq_query_kernel + tq_scores_mfma_kernel", b8_bytes),
             "ring_sets": n_sets}
 
 
