@@ -270,7 +270,13 @@ qjl_status get_rotq(uint64_t seed, qjl::RotqTables* out) {
       qtab[j * 2 * d + d + r] = static_cast<float>(m64[r * d + j]);
     }
   std::vector<float> cents(24, 0.f), thr(7 * 8, 0.f), pc(32);
-  for (int k = 1; k <= 3; ++k) qjl::make_tq_codebook(d, k, cents.data() + 8 * (k - 1));
+  for (int k = 1; k <= 3; ++k) {
+    float* c = cents.data() + 8 * (k - 1);
+    qjl::make_tq_codebook(d, k, c);
+    // the scores kernel for k = 1, 2 relies on c[v] = -c[2^k - 1 - v]
+    for (int v = 0; v < (1 << k); ++v)
+      if (c[v] != -c[(1 << k) - 1 - v]) return fail(QJL_EHIP, "TurboQuant codebook (k=%d) is not symmetric", k);
+  }
   for (int lev = 1; lev <= 7; ++lev) qjl::make_pq_codebook(lev, qjl::kPqBits[lev - 1], pc.data(), thr.data() + 8 * (lev - 1));
   const size_t b_rot = d * d * 4, b_s = d * d * 2, b_c = 24 * 4, b_t = 56 * 4, b_q = qtab.size() * 4;
   const size_t o_rotT = b_rot, o_s = 2 * b_rot, o_c = o_s + b_s, o_t = o_c + 256, o_q = o_t + 256,

@@ -665,7 +665,8 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
 // Scores for k = 1, 2 (tq_scores_mfma_kernel) are dot products of 0/1
 // bit-planes on the int8 matrix cores.  With idx = b0 + 2 b1, c[idx] = c0 +
 // (c1 - c0) b0 + (c2 - c0) b1 + (c3 - c2 - c1 + c0) b0 b1 (k = 1: c0 +
-// (c1 - c0) b0), so
+// (c1 - c0) b0), where the last coefficient is 0 for the symmetric
+// codebooks used here, so
 //   <Pi q, c[idx]> = c0 sum_i (Pi q)_i + sum over planes P of sum_i v_P,i P_i,
 // v_P = alpha_P Pi q, and <S^T Pi q, 2 bit - 1> = 2 sum_l s_l bit_l - sum_l s_l.
 // The prep quantizes every v_P (one exponent per head, from the largest
@@ -686,13 +687,14 @@ __global__ __launch_bounds__(NT) void pq_encode_kernel(RotqArgs a, int tiles) {
 // c[idx]> of every coordinate's 8 codes.  A thread scores its tokens with one
 // table read per sign nibble and per coordinate (per four heads).
 
-// prepared query of head hq, kQPrepBytes apart: floats Pi q at [0, 512) and
-// S^T Pi q at [512, 1024); limb operands at [1024, 3072): 16 bytes per
-// (plane p, k-step ks, limb j, k-group g), p = 0..2 code planes (b0, b1,
-// b0 b1; k = 1 uses b0 only), p = 3 the sign plane; scalars at 3072: 2^E of
-// the code planes, 2^E of the sign plane, c0 sum_i (Pi q)_i, sum_l s_l.
 // rows of the query table: [Pi; M]
 constexpr int kQRows = 2 * D;
+// prepared query of head hq, kQPrepBytes apart: floats Pi q at [0, 512) and
+// S^T Pi q at [512, 1024); limb operands at [1024, 3072): 16 bytes per
+// (plane p, k-step ks, limb j, k-group g), p = 0, 1 code planes (b0, b1;
+// k = 1 uses b0 only; slot 2 is unused), p = 3 the sign plane; scalars at
+// 3072: 2^E of the code planes, 2^E of the sign plane, c0 sum_i (Pi q)_i,
+// sum_l s_l.
 constexpr int kQPrepBytes = 4096;
 constexpr int kQPrepFloats = kQPrepBytes / 4;
 constexpr int kLimbOffset = 1024;
@@ -760,12 +762,14 @@ __global__ __launch_bounds__(kQueryThreads) void tq_query_kernel(const float* __
     }
   }
   __syncthreads();
-  // plane coefficients (k = 1: b0; k = 2: b0, b1, b0 b1)
+  // plane coefficients (k = 1: b0; k = 2: b0, b1).  The codebooks are
+  // symmetric (c[v] = -c[2^k - 1 - v], checked when the tables are built), so
+  // the b0 b1 coefficient c3 - c2 - c1 + c0 is exactly 0 in fp32 (c3 - c2 and
+  // c1 - c0 are the same fp32 difference) and that plane is left out.
   const float c0 = cents[0];
-  const float alpha[3] = {cents[1] - c0, K == 2 ? cents[2] - c0 : 0.f,
-                          K == 2 ? (cents[3] - cents[2]) - (cents[1] - c0) : 0.f};
+  const float alpha[2] = {cents[1] - c0, K == 2 ? cents[2] - c0 : 0.f};
   const bool code = s == 0;
-  const float amax = fmaxf(__builtin_fabsf(alpha[0]), fmaxf(__builtin_fabsf(alpha[1]), __builtin_fabsf(alpha[2])));
+  const float amax = fmaxf(__builtin_fabsf(alpha[0]), __builtin_fabsf(alpha[1]));
   // every |fl(alpha_P x)| <= fl(amax max|x|) (rounding is monotonic), so
   // with that < 2^(E + 30), |Q| <= 2^30 and the top limb fits a byte
   const float top = (code ? amax : 1.f) * fmaxf(red[0][0], red[1][0]);
@@ -773,11 +777,11 @@ __global__ __launch_bounds__(kQueryThreads) void tq_query_kernel(const float* __
   // limb dword (((p 2 + ks) 4 + j) 4 + g) 4 + qq holds bytes b = 0..3 (byte
   // x = 4 qq + b of the operand) of limb j of coordinate coord(p, g, ks, x)
   uint32_t* limbs = reinterpret_cast<uint32_t*>(prep_bytes + hq * kQPrepBytes + kLimbOffset);
-  const int nd = code ? (K == 2 ? 3 : 1) * 128 : 128;
+  const int nd = code ? (K == 2 ? 2 : 1) * 128 : 128;
   for (int t = tid; t < nd; t += kQueryThreads) {
     const int qq = t & 3, g = (t >> 2) & 3, j = (t >> 4) & 3, ks = (t >> 6) & 1;
     const int pl = code ? t >> 7 : 3;
-    const float al = pl == 0 ? alpha[0] : pl == 1 ? alpha[1] : alpha[2];
+    const float al = pl == 0 ? alpha[0] : alpha[1];
     uint32_t word = 0;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
@@ -1005,7 +1009,7 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
     const float* __restrict__ norms, const float* __restrict__ gammas, int H_kv, int N, int cap, int tpw,
     float coef, float* __restrict__ out) {
   constexpr int NRB = (G + 3) / 4;
-  constexpr int NP = K == 2 ? 3 : 1;   // code planes
+  constexpr int NP = K == 2 ? 2 : 1;   // code planes (b0, b1)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -1049,7 +1053,6 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
           const uint32_t w = ks ? cur.c1[u] : cur.c0[u];
           bc[0][ks] = plane_bytes<2>(w, 0);
           bc[1][ks] = plane_bytes<2>(w, 1);
-          bc[2][ks] = plane_bytes<2>(w & (w >> 1), 0);
         } else {
           // word grp: coordinate 32 grp + 8 b + 4 ks + q at bit 8 b + 4 ks + q
           bc[0][ks] = plane_bytes<1>(cur.c0[u], 4 * ks);
