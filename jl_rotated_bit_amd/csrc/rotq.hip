@@ -1070,22 +1070,18 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
             accc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ac[rb][p][ks], bc[p][ks], accc, 0, 0, 0);
           accs = __builtin_amdgcn_mfma_i32_16x16x64_i8(as[rb][ks], bs[ks], accs, 0, 0, 0);
         }
-        // sum_j 256^j acc[j], highest limb first (the partial sums below
-        // 2^24 are exact in fp32)
-        const float vc = __builtin_fmaf(
-            __builtin_fmaf(__builtin_fmaf(static_cast<float>(accc[3]), 256.f, static_cast<float>(accc[2])), 256.f,
-                           static_cast<float>(accc[1])),
-            256.f, static_cast<float>(accc[0]));
-        const float vs = __builtin_fmaf(
-            __builtin_fmaf(__builtin_fmaf(static_cast<float>(accs[3]), 256.f, static_cast<float>(accs[2])), 256.f,
-                           static_cast<float>(accs[1])),
-            256.f, static_cast<float>(accs[0]));
+        // sum_j 256^j acc[j] = hi 2^16 + lo with lo = acc0 + 256 acc1 and hi =
+        // acc2 + 256 acc3 (|acc_j| <= 2 128 128, the top limb <= 64 in
+        // magnitude: both below 2^24, exact in int32 and fp32), one rounding
+        const int loc = accc[0] + 256 * accc[1], hic = accc[2] + 256 * accc[3];
+        const int los = accs[0] + 256 * accs[1], his = accs[2] + 256 * accs[3];
+        const float vc = __builtin_fmaf(static_cast<float>(hic), 65536.f, static_cast<float>(loc));
+        const float vs = __builtin_fmaf(static_cast<float>(his), 65536.f, static_cast<float>(los));
         const float mse = __builtin_fmaf(sc[rb].x, vc, sc[rb].z);
-        const float pos = sc[rb].y * vs;
+        const float qjl = __builtin_fmaf(2.f * sc[rb].y, vs, -sc[rb].w);   // <s, 2 bit - 1>
         const int ho = 4 * rb + grp;
         if (ho < G && t < t_end)
-          out[(bh * G + ho) * static_cast<int64_t>(N) + t] =
-              cur.n[u] * (mse + coef * cur.g[u] * (2.f * pos - sc[rb].w));
+          out[(bh * G + ho) * static_cast<int64_t>(N) + t] = cur.n[u] * __builtin_fmaf(coef * cur.g[u], qjl, mse);
       }
     }
     cur = nxt;
