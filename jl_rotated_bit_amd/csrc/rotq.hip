@@ -967,9 +967,19 @@ __device__ __forceinline__ i32x4_t plane_bytes(uint32_t w, int sh) {
   return v;
 }
 
+// Buffer descriptor over [base, base + bytes): loads past the end return
+// zero (base and bytes wave-uniform).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t rows_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 // the tokens' rows of one 64-token chunk of a wave: lane (row, grp) holds
 // token t0 + 16 u + row's code words (k = 2: words 2 grp, 2 grp + 1; k = 1:
-// word grp), its sign word grp, norm and gamma
+// word grp), its sign word grp, norm and gamma.  Loaded through descriptors
+// over the chunk's nrows valid rows (row0 = the first one's cache row), so
+// the lane offsets are the same every pass and rows past N read as zero.
 template <int K>
 struct TqChunk {
   uint32_t c0[4], c1[4], sw[4];
@@ -978,22 +988,27 @@ struct TqChunk {
 template <int K>
 __device__ __forceinline__ void load_tq_chunk(TqChunk<K>& c, const uint32_t* __restrict__ codes,
                                               const uint32_t* __restrict__ bits, const float* __restrict__ norms,
-                                              const float* __restrict__ gammas, int64_t base, int t0, int row,
-                                              int grp, int last) {
+                                              const float* __restrict__ gammas, int64_t row0, int nrows, int row,
+                                              int grp) {
+  constexpr int CW = D * K / 32;   // code words per token
+  const rsrc_t rc = rows_rsrc(codes + row0 * CW, nrows * CW * 4);
+  const rsrc_t rs = rows_rsrc(bits + row0 * 4, nrows * 16);
+  const rsrc_t rn = rows_rsrc(norms + row0, nrows * 4);
+  const rsrc_t rg = rows_rsrc(gammas + row0, nrows * 4);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int64_t r = base + min(t0 + 16 * u + row, last);
+    const int r = 16 * u + row;
     if constexpr (K == 2) {
-      const uint2 v = reinterpret_cast<const uint2*>(codes + r * 8)[grp];
-      c.c0[u] = v.x;
-      c.c1[u] = v.y;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, (r * CW + 2 * grp) * 4, 0, 0);
+      c.c0[u] = v[0];
+      c.c1[u] = v[1];
     } else {
-      c.c0[u] = codes[r * 4 + grp];
+      c.c0[u] = __builtin_amdgcn_raw_buffer_load_b32(rc, (r * CW + grp) * 4, 0, 0);
       c.c1[u] = 0;
     }
-    c.sw[u] = bits[r * 4 + grp];
-    c.n[u] = norms[r];
-    c.g[u] = gammas[r];
+    c.sw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (r * 4 + grp) * 4, 0, 0);
+    c.n[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, r * 4, 0, 0));
+    c.g[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, r * 4, 0, 0));
   }
 }
 
@@ -1010,16 +1025,18 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
     float coef, float* __restrict__ out) {
   constexpr int NRB = (G + 3) / 4;
   constexpr int NP = K == 2 ? 2 : 1;   // code planes (b0, b1)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform passes
   const int row = lane & 15, grp = lane >> 4;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int64_t bh = static_cast<int64_t>(b) * H_kv + kvh;
   const int64_t base = bh * cap;
   const int t_end = min(N, (static_cast<int>(blockIdx.x) + 1) * tpw);
   int t0 = blockIdx.x * tpw + 64 * wave;
+  auto valid_rows = [&](int t) { return max(0, min(64, N - t)); };
   // the first chunk's rows are in flight while the operands load
   TqChunk<K> cur;
-  if (t0 < t_end) load_tq_chunk<K>(cur, codes, bits, norms, gammas, base, t0, row, grp, N - 1);
+  if (t0 < t_end) load_tq_chunk<K>(cur, codes, bits, norms, gammas, base + t0, valid_rows(t0), row, grp);
   i32x4_t ac[NRB][NP][2], as[NRB][2];
   float4 sc[NRB];
 #pragma unroll
@@ -1041,7 +1058,8 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
   for (; t0 < t_end; t0 += 256) {
     // the next pass's rows load while this one is scored
     TqChunk<K> nxt = cur;
-    if (t0 + 256 < t_end) load_tq_chunk<K>(nxt, codes, bits, norms, gammas, base, t0 + 256, row, grp, N - 1);
+    if (t0 + 256 < t_end)
+      load_tq_chunk<K>(nxt, codes, bits, norms, gammas, base + t0 + 256, valid_rows(t0 + 256), row, grp);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       i32x4_t bc[NP][2], bs[2];
