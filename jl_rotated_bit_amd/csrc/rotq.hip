@@ -181,21 +181,30 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 // Each product of two values exact in fp64 (a bf16 key or an fp32 residual
 // times an fp32 rotation entry or a bf16 sketch entry) is exact; the sums
 // carry at most d roundings, whatever order the unit adds in.
+// Even and odd k-steps accumulate into separate registers (four independent
+// product chains per wave) that are added at the end: d products still take
+// d - 1 additions, so the bound above holds.
 template <class Col>
 __device__ __forceinline__ void mfma_tile(const Col& col, const double* x, int wave, int lane,
                                           f64x4_t (&acc)[CB]) {
   const int kb = wave & 1, cg = wave >> 1;
   const int lr = lane & 15, lk = lane >> 4;
+  f64x4_t acc2[CB];
 #pragma unroll
-  for (int c = 0; c < CB; ++c) acc[c] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  for (int c = 0; c < CB; ++c) acc[c] = acc2[c] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
-  for (int s = 0; s < D / 4; ++s) {
-    const int kk = 4 * s + lk;
+  for (int s = 0; s < D / 4; s += 2) {
+    const int kk = 4 * s + lk, kk2 = 4 * (s + 1) + lk;
     const double av = x[kk * TKP + 16 * kb + lr];
+    const double av2 = x[kk2 * TKP + 16 * kb + lr];
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
+    for (int c = 0; c < CB; ++c) {
       acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, col(kk, 16 * (CB * cg + c) + lr), acc[c], 0, 0, 0);
+      acc2[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av2, col(kk2, 16 * (CB * cg + c) + lr), acc2[c], 0, 0, 0);
+    }
   }
+#pragma unroll
+  for (int c = 0; c < CB; ++c) acc[c] += acc2[c];
 }
 
 // A power of two at least sqrt(s) (s >= 0, finite), from the exponent field
