@@ -97,6 +97,8 @@ DESCRIPTIONS = {
     "gqa32k": "gqa32k: Llama-3.1-8B-shaped GQA decode, 32 q / 8 kv heads, d=128, m=256, batch 1, "
               "32768 cached tokens; encode of those 262144 keys + one decode step",
     "small": "small: 1 kv / 8 q heads, d=128, m=256, 4096 tokens",
+    "tp8": "tp8: one GPU's share of gqa32k under 8-way tensor parallelism: 1 kv / 4 q heads, d=128, "
+           "m=256, batch 1, 32768 tokens",
     "prefill": "prefill: encode of 16 x 8192 tokens x 8 kv heads (1048576 keys), d=128, m=256",
     "long64k": "long64k: 8 kv / 32 q heads, d=128, m=512, 65536 cached tokens, then 64 decode steps "
                "that each append one token",
@@ -352,7 +354,7 @@ def bench_gqa32k(qjl, w, args, T):
 # other workloads
 # ----------------------------------------------------------------------------
 
-def bench_small(qjl, w, args, T):
+def bench_small(qjl, w, args, T, name="small", note="latency-bound (1.2 MB per decode call)"):
     import torch
     B, Hq, Hkv, N, d, m = w.B, w.H_q, w.H_kv, w.N, w.d, w.m
     dbytes = decode_bytes(B, Hq, Hkv, N, d, m)
@@ -379,15 +381,20 @@ def bench_small(qjl, w, args, T):
         dec(i)
     enc_ms = T.b2b(enc, reps)
     dec_ms = T.b2b(dec, reps)
-    log(f"[bench] small: encode {enc_ms * 1e3:.2f} us, decode {dec_ms * 1e3:.2f} us")
+    log(f"[bench] {name}: encode {enc_ms * 1e3:.2f} us, decode {dec_ms * 1e3:.2f} us")
     del sets
     torch.cuda.empty_cache()
     gbs = dbytes / (dec_ms / 1e3) / 1e9
-    return {"workload": DESCRIPTIONS["small"], "encode_us": round(enc_ms * 1e3, 3),
+    return {"workload": DESCRIPTIONS[name], "encode_us": round(enc_ms * 1e3, 3),
             "encode_keys_per_s": round(B * Hkv * N / (enc_ms / 1e3), 1),
             "decode_us": round(dec_ms * 1e3, 3), "decode_gbs": round(gbs, 2),
             "roofline": roofline(gbs, None, "decode_kernel", dbytes), "ring_sets": n_sets,
-            "note": "latency-bound (1.2 MB per decode call)"}
+            "note": note}
+
+
+def bench_tp8(qjl, w, args, T):
+    return bench_small(qjl, w, args, T, name="tp8",
+                       note="one GPU's share at 8-way tensor parallelism (9.6 MB per decode call)")
 
 
 def bench_prefill(qjl, w, args, T):
@@ -725,12 +732,12 @@ def main():
     qjl.load()
     T = Timer()
 
-    runners = {"small": bench_small, "prefill": bench_prefill, "long64k": bench_long64k,
+    runners = {"small": bench_small, "tp8": bench_tp8, "prefill": bench_prefill, "long64k": bench_long64k,
                "mha16k": bench_mha16k, "rotq": bench_rotq}
     if args.workload not in ("all", "gqa32k"):
         name = args.workload
         log(f"[bench] generating workload {name}")
-        res = runners[name](qjl, wl.WORKLOADS["gqa32k" if name == "rotq" else name](), args, T)
+        res = runners[name](qjl, wl.WORKLOADS[{"rotq": "gqa32k"}.get(name, name)](), args, T)
         if args.copy_calibration:
             a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
             b = torch.empty_like(a)
@@ -745,7 +752,7 @@ def main():
     head = bench_gqa32k(qjl, w, args, T)
     configs = {}
     if args.workload == "all":
-        for name in ("small", "prefill", "long64k", "mha16k"):
+        for name in ("small", "tp8", "prefill", "long64k", "mha16k"):
             log(f"[bench] generating workload {name}")
             t0 = time.perf_counter()
             wk = wl.WORKLOADS[name]()

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the QJL encode/decode workloads.
 
 This module only draws inputs (keys, values, queries) with the shapes and
-value distributions of the five workloads below and rounds them to bf16 the
+value distributions of the workloads below and rounds them to bf16 the
 way a model's fp32 activations would be stored.  It holds none of the method's
 arithmetic: no sketch, no projection, no estimator.  The tests and the bench
 feed the same arrays to the HIP library and to the CPU oracle.
@@ -15,6 +15,9 @@ Workloads (all d = 128):
                     m = 256, batch 1, 32768 tokens; K, V = z * exp(g) with
                     g ~ N(0, 1) per (kv head, channel) drawn separately for K
                     and V, plus 1% of the (kv head, channel) pairs scaled x20.
+* ``tp8``         - one GPU's share of ``gqa32k`` under 8-way tensor
+                    parallelism: 1 kv head and its 4 query heads, 32768
+                    tokens, the same distributions.
 * ``prefill``     - encode throughput: batch 16 x 8192 tokens x 8 kv heads,
                     m = 256, keys drawn like ``gqa32k`` (scales per (kv head,
                     channel), shared by the batch).
@@ -172,8 +175,17 @@ def gaussian_keys(rng: np.random.Generator, rows: int, d: int = HEAD_DIM,
     return round_to_bf16_bits(rng.standard_normal((rows, d), dtype=np.float32) * np.float32(scale))
 
 
+def tp8(data_seed: int = 1006) -> Workload:
+    """One GPU's share of ``gqa32k`` under 8-way tensor parallelism: 1 kv
+    head and its 4 query heads, 32768 tokens, the same distributions."""
+    w = gqa32k(H_q=4, H_kv=1, data_seed=data_seed)
+    w.name = "tp8"
+    return w
+
+
 WORKLOADS = {
     "small": small,
+    "tp8": tp8,
     "gqa32k": gqa32k,
     "prefill": prefill,
     "long64k": long64k,

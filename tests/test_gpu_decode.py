@@ -74,6 +74,26 @@ def test_gqa32k_full(gpu_lib):
     check_decode(gpu_lib, w.q, words, norms, w.values, w.N, w.m, label="gqa32k")
 
 
+def test_gqa32k_tp8_share_end_to_end(gpu_lib):
+    """One GPU's share of the 32K GQA workload under 8-way tensor parallelism
+    (1 kv head, its 4 query heads, 32768 tokens): GPU encode (every word
+    equal to the oracle's, norms within 1e-5), then GPU decode on those
+    caches against the oracle decode on its own."""
+    import torch
+    w = wl.tp8()
+    signs, norms = gpu_encode(gpu_lib, w.keys, w.m, SEED)
+    ref_w, ref_n = oracle_cache(w.keys, w.m)
+    assert np.array_equal(host_u32(signs), ref_w)
+    gn = norms.cpu().numpy()
+    assert np.max(np.abs(gn - ref_n) / ref_n) <= 1e-5
+    say("decode gqa32k TP=8 share", "splits", gpu_lib.decode_num_splits(1, 4, 1, w.N, 128, w.m))
+    out = gpu_lib.decode_attention(dev_f32(w.q), signs, norms, dev_u16(w.values), w.N, SEED, w.m)
+    torch.cuda.synchronize()
+    ref = oracle.decode(w.q, ref_w, ref_n, w.values, w.N, oracle.sketch(SEED, 128, w.m))
+    err = row_rel_l2(out.cpu().numpy(), ref)
+    assert err <= TIGHT_TOL, err
+
+
 def test_mha16k_full(gpu_lib):
     """The whole 40-head, batch-8, 16K workload: the GPU encode of all
     5 242 880 keys equals the oracle's cache (every word, every norm within
