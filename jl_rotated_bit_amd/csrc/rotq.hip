@@ -1063,12 +1063,9 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
     sc[rb] = ho < G ? *reinterpret_cast<const float4*>(prep + (bh * G + ho) * kQPrepBytes + kScalarOffset)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-#pragma unroll 1
-  for (; t0 < t_end; t0 += 256) {
-    // the next pass's rows load while this one is scored
-    TqChunk<K> nxt = cur;
-    if (t0 + 256 < t_end)
-      load_tq_chunk<K>(nxt, codes, bits, norms, gammas, base + t0 + 256, valid_rows(t0 + 256), row, grp);
+  // two row buffers used in turn (a pass scores one while the next pass's
+  // rows load into the other), so no registers are copied between passes
+  auto score = [&](const TqChunk<K>& c, int tp) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       i32x4_t bc[NP][2], bs[2];
@@ -1077,16 +1074,16 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
         if constexpr (K == 2) {
           // word 2 grp + ks: coordinate 16 (2 grp + ks) + 4 b + q at bits
           // 8 b + 2 q (b0) and 8 b + 2 q + 1 (b1)
-          const uint32_t w = ks ? cur.c1[u] : cur.c0[u];
+          const uint32_t w = ks ? c.c1[u] : c.c0[u];
           bc[0][ks] = plane_bytes<2>(w, 0);
           bc[1][ks] = plane_bytes<2>(w, 1);
         } else {
           // word grp: coordinate 32 grp + 8 b + 4 ks + q at bit 8 b + 4 ks + q
-          bc[0][ks] = plane_bytes<1>(cur.c0[u], 4 * ks);
+          bc[0][ks] = plane_bytes<1>(c.c0[u], 4 * ks);
         }
-        bs[ks] = plane_bytes<1>(cur.sw[u], 4 * ks);
+        bs[ks] = plane_bytes<1>(c.sw[u], 4 * ks);
       }
-      const int t = t0 + 16 * u + row;
+      const int t = tp + 16 * u + row;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         i32x4_t accc = {0, 0, 0, 0}, accs = {0, 0, 0, 0};
@@ -1108,10 +1105,22 @@ __global__ __launch_bounds__(256) void tq_scores_mfma_kernel(
         const float qjl = __builtin_fmaf(2.f * sc[rb].y, vs, -sc[rb].w);   // <s, 2 bit - 1>
         const int ho = 4 * rb + grp;
         if (ho < G && t < t_end)
-          out[(bh * G + ho) * static_cast<int64_t>(N) + t] = cur.n[u] * __builtin_fmaf(coef * cur.g[u], qjl, mse);
+          out[(bh * G + ho) * static_cast<int64_t>(N) + t] = c.n[u] * __builtin_fmaf(coef * c.g[u], qjl, mse);
       }
     }
-    cur = nxt;
+  };
+  TqChunk<K> alt;
+#pragma unroll 1
+  while (t0 < t_end) {
+    if (t0 + 256 < t_end)
+      load_tq_chunk<K>(alt, codes, bits, norms, gammas, base + t0 + 256, valid_rows(t0 + 256), row, grp);
+    score(cur, t0);
+    t0 += 256;
+    if (t0 >= t_end) break;
+    if (t0 + 256 < t_end)
+      load_tq_chunk<K>(cur, codes, bits, norms, gammas, base + t0 + 256, valid_rows(t0 + 256), row, grp);
+    score(alt, t0);
+    t0 += 256;
   }
 }
 }  // namespace
