@@ -163,6 +163,38 @@ def test_tq_scores_many_passes(gpu_lib, G, k):
     assert np.max(np.abs(got - ref) / scale) <= 1e-5
 
 
+@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("N", [24_000, 40_000])
+def test_tq_scores_odd_passes(gpu_lib, k, N):
+    """64 kv heads, so that each workgroup of the matrix-core scores kernel
+    takes 768 or 1280 tokens and each wave an odd number of passes (3 or 5
+    with 256 compute units): the pass loop alternates two row buffers, and
+    these counts end it after a pass of the first one, once after going
+    round (3) and once after going round twice (5); ragged last workgroup."""
+    import torch
+    rng = np.random.default_rng(80 + k + N % 97)
+    B, Hkv, G = 1, 64, 1
+    cap = N + 5
+    codes = rng.integers(0, 2 ** 32, (B, Hkv, cap, D * k // 32), dtype=np.uint64).astype(np.uint32)
+    bits = rng.integers(0, 2 ** 32, (B, Hkv, cap, D // 32), dtype=np.uint64).astype(np.uint32)
+    norms = rng.uniform(0.5, 4.0, (B, Hkv, cap)).astype(np.float32)
+    gammas = rng.uniform(0.0, 1.0, (B, Hkv, cap)).astype(np.float32)
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float32)
+    say("tq scores odd passes", "k", k, "N", N, "Hkv", Hkv)
+    got = gpu_lib.tq_scores(dev_f32(q), dev_u32(codes), dev_u32(bits), dev_f32(norms), dev_f32(gammas), N, SEED, k)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    # the oracle on three windows of 1536 tokens (each spans every pass of
+    # the waves of the workgroups it touches): the start, the middle and the
+    # ragged end
+    L = 1536
+    for t0 in (0, (N // 2) // 256 * 256, N - L):
+        sl = slice(t0, t0 + L)
+        ref = otq.scores(q, codes[:, :, sl], bits[:, :, sl], norms[:, :, sl], gammas[:, :, sl], L, k, SEED)
+        scale = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+        assert np.max(np.abs(got[:, :, sl] - ref) / scale) <= 1e-5, t0
+
+
 @pytest.mark.parametrize("k", [1, 2, 3])
 @pytest.mark.parametrize("N", [1, 17])
 def test_tq_scores_edge_queries(gpu_lib, k, N):
