@@ -633,21 +633,22 @@ def bench_rotq(qjl, w, args, T):
     tq_flops = R * 2.0 * (2 * d * d)            # rotation + residual sketch (m = d)
     pq_flops = R * 2.0 * d * d                  # rotation
     sc_bytes = R * (d * k // 8 + d // 8 + 8) + B * Hq * N * 4
-    fp64 = lambda fl, ms: {"bound": "mfma", "dtype": "f64", "achieved": round(fl / (ms / 1e3) / 1e12, 2),
-                           "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(fl / (ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS, 4),
-                           "flops_per_launch": int(fl)}
+    fp64 = lambda fl, ms, tr: {"bound": "mfma", "dtype": "f64", "achieved": round(fl / (ms / 1e3) / 1e12, 2),
+                               "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(fl / (ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS, 4),
+                               "traffic": tr, "flops_per_launch": int(fl)}
     return {"workload": "the 262144 keys and 32 query heads of the 32K GQA workload; TurboQuant_prod at "
                         "3 bits per coordinate (2-bit codes + 1-bit QJL of the residual), PolarQuant "
                         "4/2-bit levels",
             "tq_encode_us": round(tq_ms * 1e3, 3), "tq_encode_keys_per_s": round(R / (tq_ms / 1e3), 1),
-            "tq_encode_roofline": fp64(tq_flops, tq_ms),
+            "tq_encode_roofline": fp64(tq_flops, tq_ms, measured_traffic("rotq", "tq_encode")),
             "pq_encode_us": round(pq_ms * 1e3, 3), "pq_encode_keys_per_s": round(R / (pq_ms / 1e3), 1),
-            "pq_encode_roofline": fp64(pq_flops, pq_ms),
+            "pq_encode_roofline": fp64(pq_flops, pq_ms, measured_traffic("rotq", "pq_encode")),
             "tq_scores_us": round(sc_ms * 1e3, 3),
-            "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, None, "tq_query_kernel + tq_scores_mfma_kernel", sc_bytes),
+            "tq_scores_roofline": roofline(sc_bytes / (sc_ms / 1e3) / 1e9, measured_traffic("rotq", "tq_scores_b1"),
+                                           "tq_query_kernel + tq_scores_mfma_kernel", sc_bytes),
             "tq_scores_batch8_us": round(sc8_ms * 1e3, 3),
-            "tq_scores_batch8_roofline": roofline(b8_bytes / (sc8_ms / 1e3) / 1e9, None,
+            "tq_scores_batch8_roofline": roofline(b8_bytes / (sc8_ms / 1e3) / 1e9, measured_traffic("rotq", "tq_scores_b8"),
                                                   "tq_query_kernel + tq_scores_mfma_kernel", b8_bytes),
             "ring_sets": n_sets}
 
