@@ -388,7 +388,7 @@ def bench_small(qjl, w, args, T, name="small", note="latency-bound (1.2 MB per d
     return {"workload": DESCRIPTIONS[name], "encode_us": round(enc_ms * 1e3, 3),
             "encode_keys_per_s": round(B * Hkv * N / (enc_ms / 1e3), 1),
             "decode_us": round(dec_ms * 1e3, 3), "decode_gbs": round(gbs, 2),
-            "roofline": roofline(gbs, None, "decode_kernel", dbytes), "ring_sets": n_sets,
+            "roofline": roofline(gbs, measured_traffic("decode", name), "decode_kernel", dbytes), "ring_sets": n_sets,
             "note": note}
 
 
