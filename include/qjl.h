@@ -38,8 +38,8 @@
  *   until qjl_release_cache() or process exit.
  * - Validation runs before any HIP call: on an error return nothing has been
  *   launched and no output has been written.
- * - All entry points are thread-safe.  Inputs with Inf or NaN give undefined
- *   (but memory-safe) results.
+ * - All entry points except qjl_release_cache are thread-safe.  Inputs with
+ *   Inf or NaN give undefined (but memory-safe) results.
  * - The library is silent unless the environment (read once per process)
  *   says otherwise: QJL_LOG=1 prints every error to stderr ("[qjl] error
  *   <status>: <message>"), QJL_LOG=2 also names every call; QJL_TRACE=1 wraps
@@ -341,8 +341,10 @@ QJL_API qjl_status qjl_decode_attention_noalloc(const float *q, const uint32_t *
                                                 int32_t cap, int32_t d, int32_t m, uint64_t seed,
                                                 float scale, float *out, void *stream);
 
-/* Frees the library's device copies of S on every device (waits for the
- * device first).  Later calls re-create them on demand. */
+/* Frees the library's device copies of S and of the rotate-then-quantize
+ * tables on every device (waiting for each device first).  Later calls
+ * re-create them on demand.  Call it only while no other thread is inside a
+ * qjl_* call: a call in progress may already hold the tables' addresses. */
 QJL_API qjl_status qjl_release_cache(void);
 
 #ifdef __cplusplus

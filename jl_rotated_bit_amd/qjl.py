@@ -406,4 +406,6 @@ def testing_set_encode_small_max(keys: int) -> int:
 
 
 def release_cache():
+    """qjl_release_cache: frees the device tables of every seed; call it only
+    while no other thread is inside the library."""
     _check(load().qjl_release_cache())
