@@ -244,8 +244,9 @@ QJL_API size_t qjl_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, 
  *   workspace    device, 256-byte aligned, at least
  *                qjl_decode_workspace_bytes(...) bytes, zero-filled before
  *                its first use.  Its first 4096 bytes hold arrival counters
- *                (one uint32 per (batch, kv head)) that every call returns
- *                to zero; the rest is scratch that each call overwrites.  A
+ *                (one uint32 per (batch, kv head), up to 256 bytes apart
+ *                when there are few of them) that every call returns to
+ *                zero; the rest is scratch that each call overwrites.  A
  *                workspace can therefore be reused by later calls of any
  *                size on the same stream; calls that may overlap (other
  *                streams) must not share one.

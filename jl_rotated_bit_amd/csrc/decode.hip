@@ -319,7 +319,7 @@ template <int M, int G, int NW, bool APPEND, bool BF16K = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     const float* __restrict__ q, const uint32_t* signs, const float* norms, const uint16_t* values,
     const uint16_t* __restrict__ s_frag, float cnmax, int H_kv, int N, int cap, int n_split,
-    int tps, float coef, float* __restrict__ out, uint32_t* __restrict__ counters,
+    int tps, float coef, float* __restrict__ out, uint32_t* __restrict__ counters, int cstride,
     float* __restrict__ part_acc, float* __restrict__ part_ml, AppendArgs app,
     const uint16_t* kbf) {
   static_assert(!(APPEND && BF16K), "the baseline kernel has no append");
@@ -1010,7 +1010,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev =
-        __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&counters[bh * cstride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == static_cast<uint32_t>(n_split - 1));
   }
   __syncthreads();
@@ -1117,7 +1117,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       reinterpret_cast<float4*>(out)[(bh * G + g) * (D / 4) + cc] = o;
     }
   }
-  if (tid == 0) __hip_atomic_store(&counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&counters[bh * cstride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int G, int NW>
@@ -1131,7 +1131,7 @@ int launch_decode_bf16_gw(const DecodePlan& plan, const float* q, const void* ke
   dim3 grid(plan.n_split, H_kv, B);
   hipLaunchKernelGGL((decode_kernel<256, G, NW, false, true>), grid, dim3(64 * NW), 0, stream, q,
                      nullptr, nullptr, static_cast<const uint16_t*>(values), nullptr, 0.f, H_kv, N, cap,
-                     plan.n_split, plan.tokens_per_split, coef, out, counters, part_acc, part_ml,
+                     plan.n_split, plan.tokens_per_split, coef, out, counters, plan.counter_stride, part_acc, part_ml,
                      AppendArgs{}, static_cast<const uint16_t*>(keys));
   return hipGetLastError();
 }
@@ -1159,11 +1159,11 @@ int launch_decode_mgw(const DeviceSketch& s, const DecodePlan& plan, const float
   if (app != nullptr) {
     hipLaunchKernelGGL((decode_kernel<M, G, NW, true>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
                        v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
-                       coef, out, counters, part_acc, part_ml, *app, nullptr);
+                       coef, out, counters, plan.counter_stride, part_acc, part_ml, *app, nullptr);
   } else {
     hipLaunchKernelGGL((decode_kernel<M, G, NW, false>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
                        v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
-                       coef, out, counters, part_acc, part_ml, AppendArgs{}, nullptr);
+                       coef, out, counters, plan.counter_stride, part_acc, part_ml, AppendArgs{}, nullptr);
   }
   return hipGetLastError();
 }
@@ -1247,6 +1247,9 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
   // partials of any other plan, so one zero-filled workspace serves calls of
   // all sizes.
   plan->counter_bytes = kCounterRegionBytes;
+  int cs = kCounterStrideMax;
+  while (cs > 1 && streams * cs > kMaxCounters) cs >>= 1;
+  plan->counter_stride = cs;
   const size_t parts = static_cast<size_t>(B) * H_q * n_split;
   plan->partial_bytes = parts * (D + 2) * sizeof(float);
   plan->total_bytes = plan->counter_bytes + plan->partial_bytes;

@@ -80,7 +80,8 @@ def run_step_case(qjl, rng, B, Hkv, G, pos, cap, m, new_rows=None, label=""):
     got_v = vals.cpu().numpy().view(np.uint16)
     assert np.array_equal(got_w[:, :, :pos + 1], ref_w[:, :, :pos + 1]), "sign words differ"
     assert np.all(got_w[:, :, pos + 1:] == np.uint32(SENTINEL)), "rows past pos were written"
-    rel = np.abs(got_n[:, :, pos].astype(np.float64) - ref_n[:, :, pos]) / np.maximum(ref_n[:, :, pos], 1e-300)
+    ref_np = ref_n[:, :, pos].astype(np.float64)
+    rel = np.abs(got_n[:, :, pos].astype(np.float64) - ref_np) / np.maximum(ref_np, 1e-300)
     zero = ref_n[:, :, pos] == 0
     assert np.all(got_n[:, :, pos][zero] == 0)
     assert rel[~zero].max(initial=0.0) <= NORM_RTOL
