@@ -60,6 +60,17 @@ constexpr int NDB = D / 16;      // 16-column blocks of the output (8)
 constexpr int VROW = D * 2 + 32; // bytes per value row in LDS (256 + 32 padding)
 constexpr int VBUF = HALF * VROW;            // wave-private value tile (9 KB)
 constexpr int MAX_SPLITS = 256;
+
+// Words between the arrival counters of consecutive (batch, kv head) streams
+// in the fixed counter region: 64 (a 256-byte line each) when at most 16
+// streams split, so that the arrivals of different kv heads do not queue at
+// one line's atomic unit; otherwise as far apart as the region allows.
+int counter_stride(int B, int H_kv) {
+  const int64_t streams = static_cast<int64_t>(B) * H_kv;
+  int cs = 64;
+  while (cs > 1 && streams * cs > kMaxCounters) cs >>= 1;
+  return cs;
+}
 constexpr int QBITS = 21;        // |Q_i| <= 2^21
 constexpr int PROW = 32;         // bytes per token of probability rows (16 bf16: head x part)
 
@@ -1131,7 +1142,7 @@ int launch_decode_bf16_gw(const DecodePlan& plan, const float* q, const void* ke
   dim3 grid(plan.n_split, H_kv, B);
   hipLaunchKernelGGL((decode_kernel<256, G, NW, false, true>), grid, dim3(64 * NW), 0, stream, q,
                      nullptr, nullptr, static_cast<const uint16_t*>(values), nullptr, 0.f, H_kv, N, cap,
-                     plan.n_split, plan.tokens_per_split, coef, out, counters, plan.counter_stride, part_acc, part_ml,
+                     plan.n_split, plan.tokens_per_split, coef, out, counters, counter_stride(B, H_kv), part_acc, part_ml,
                      AppendArgs{}, static_cast<const uint16_t*>(keys));
   return hipGetLastError();
 }
@@ -1159,11 +1170,11 @@ int launch_decode_mgw(const DeviceSketch& s, const DecodePlan& plan, const float
   if (app != nullptr) {
     hipLaunchKernelGGL((decode_kernel<M, G, NW, true>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
                        v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
-                       coef, out, counters, plan.counter_stride, part_acc, part_ml, *app, nullptr);
+                       coef, out, counters, counter_stride(B, H_kv), part_acc, part_ml, *app, nullptr);
   } else {
     hipLaunchKernelGGL((decode_kernel<M, G, NW, false>), grid, dim3(64 * NW), 0, stream, q, signs, norms,
                        v, s.s_frag, s.col_norm_all, H_kv, N, cap, plan.n_split, plan.tokens_per_split,
-                       coef, out, counters, plan.counter_stride, part_acc, part_ml, AppendArgs{}, nullptr);
+                       coef, out, counters, counter_stride(B, H_kv), part_acc, part_ml, AppendArgs{}, nullptr);
   }
   return hipGetLastError();
 }
@@ -1247,9 +1258,6 @@ bool make_decode_plan(int B, int H_q, int H_kv, int N, int d, int m, DecodePlan*
   // partials of any other plan, so one zero-filled workspace serves calls of
   // all sizes.
   plan->counter_bytes = kCounterRegionBytes;
-  int cs = kCounterStrideMax;
-  while (cs > 1 && streams * cs > kMaxCounters) cs >>= 1;
-  plan->counter_stride = cs;
   const size_t parts = static_cast<size_t>(B) * H_q * n_split;
   plan->partial_bytes = parts * (D + 2) * sizeof(float);
   plan->total_bytes = plan->counter_bytes + plan->partial_bytes;

@@ -49,19 +49,14 @@ struct DeviceSketch {
 
 // The decode workspace starts with a fixed region of arrival counters (one
 // uint32 per (batch, kv head)); calls with more streams than that never split.
-// With few streams the counters sit kCounterStrideMax words apart (each in a
-// 256-byte line of its own), so that the arrivals of different kv heads do
-// not queue at one line's atomic unit.
 constexpr size_t kCounterRegionBytes = 4096;
 constexpr int64_t kMaxCounters = kCounterRegionBytes / 4;
-constexpr int kCounterStrideMax = 64;
 
 // Decode split geometry, shared by the workspace query and the launch.
 struct DecodePlan {
   int waves = 4;            // waves per workgroup (4 or 8)
   int n_split = 0;          // context splits per (batch, kv head)
   int tokens_per_split = 0; // multiple of the token tile
-  int counter_stride = 1;   // uint32 words between the counters of consecutive streams
   size_t counter_bytes = 0; // kCounterRegionBytes
   size_t partial_bytes = 0; // B*H_q*n_split*(d + 2) floats
   size_t total_bytes = 0;
