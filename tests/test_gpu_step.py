@@ -48,6 +48,24 @@ def split_rule(B, Hkv, N, m):
     return ns, tps, 8
 
 
+def step_rule(ns, tps, nw, N):
+    """Splits of the fused step (the library's host arithmetic): where a
+    split gives each wave at least two tiles, fewer splits (at most an eighth
+    fewer) until the last split, which appends the new token, is at least one
+    tile per wave shorter than the others."""
+    shorter = nw * 64
+    if ns < 2 or tps < 2 * shorter:
+        return ns, tps
+    want = ns
+    while want >= 2 and want >= ns - ns // 8:
+        t = -(-(-(-N // want)) // 64) * 64
+        n = -(-N // t)
+        if n > 1 and N - (n - 1) * t <= t - shorter:
+            return n, t
+        want -= 1
+    return ns, tps
+
+
 def run_step_case(qjl, rng, B, Hkv, G, pos, cap, m, new_rows=None, label=""):
     import torch
     d = 128
@@ -70,7 +88,8 @@ def run_step_case(qjl, rng, B, Hkv, G, pos, cap, m, new_rows=None, label=""):
     signs, norms, vals = dev_u32(w0), dev_f32(n0), dev_u16(v0)
     ns, tps, nw = split_rule(B, Hkv, pos + 1, m)
     assert qjl.decode_num_splits(B, Hkv * G, Hkv, pos + 1, d, m) == ns
-    first_tile_of_wave = (pos - (ns - 1) * tps) < 64      # the new token opens a wave's first tile
+    ns, tps = step_rule(ns, tps, nw, pos + 1)
+    first_tile_of_wave = (pos - (ns - 1) * tps) < nw * 64   # the new token is in a wave's first tile
     say("decode step", label, "B", B, "Hkv", Hkv, "G", G, "pos", pos, "cap", cap, "m", m,
         "splits", ns, "waves", nw, "deferred first tile", first_tile_of_wave)
     out = qjl.decode_step(dev_f32(q), dev_u16(keys[:, :, pos].copy()), dev_u16(values[:, :, pos].copy()),
@@ -121,6 +140,18 @@ def test_step_eight_wave_splits(gpu_lib, m):
                                 label=f"last split of one token, N={N}")
             break
     assert hit
+
+
+@pytest.mark.parametrize("m,N", [(256, 32768), (512, 61440)])
+def test_step_shortened_last_split(gpu_lib, m, N):
+    """Contexts whose plain plan ends with a full split (32K tokens of 8 kv
+    heads at m = 256, 30 x 2048 tokens at m = 512): the step takes fewer,
+    longer splits so that the appending workgroup's split is short."""
+    ns, tps, nw = split_rule(1, 8, N, m)
+    assert nw == 8 and N - (ns - 1) * tps == tps
+    sns, stps = step_rule(ns, tps, nw, N)
+    assert sns < ns and N - (sns - 1) * stps <= stps - nw * 64
+    run_step_case(gpu_lib, np.random.default_rng(N + m), 1, 8, 4, N - 1, N, m, label=f"short last split, N={N}")
 
 
 @pytest.mark.parametrize("m", [256, 512])
