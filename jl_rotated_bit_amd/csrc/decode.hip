@@ -1280,12 +1280,12 @@ DecodePlan append_plan(const DecodePlan& plan, int N) {
   DecodePlan p = plan;
   const int shorter = plan.waves * TILE;
   if (plan.n_split < 2 || plan.tokens_per_split < 2 * shorter) return p;
-  for (int want = plan.n_split; want >= 2 && want >= plan.n_split - plan.n_split / 8; --want) {
-    const int t = ((N + want - 1) / want + TILE - 1) / TILE * TILE;
-    const int n = (N + t - 1) / t;
+  for (int64_t want = plan.n_split; want >= 2 && want >= plan.n_split - plan.n_split / 8; --want) {
+    const int64_t t = ((N + want - 1) / want + TILE - 1) / TILE * TILE;
+    const int64_t n = (N + t - 1) / t;
     if (n > 1 && N - (n - 1) * t <= t - shorter) {
-      p.n_split = n;
-      p.tokens_per_split = t;
+      p.n_split = static_cast<int>(n);
+      p.tokens_per_split = static_cast<int>(t);
       break;
     }
   }
