@@ -242,12 +242,13 @@ def test_special_inputs(gpu_lib):
 
 def test_workspace_reuse_across_calls(gpu_lib):
     """Arrival counters return to zero: back-to-back calls sharing one workspace
-    (different sizes, different split counts) all stay correct."""
+    (different sizes, different split counts, and counters 256 bytes apart
+    for up to 16 kv heads, 128 bytes apart for 32) all stay correct."""
     import torch
     rng = np.random.default_rng(11)
     ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
     cases = []
-    for N, Hkv, G in [(20000, 8, 4), (777, 2, 2), (20000, 8, 4), (300, 1, 8), (9000, 4, 1)]:
+    for N, Hkv, G in [(20000, 8, 4), (777, 2, 2), (20000, 8, 4), (300, 1, 8), (9000, 4, 1), (3000, 32, 1)]:
         keys = wl.gaussian_keys(rng, Hkv * N).reshape(1, Hkv, N, 128)
         values = wl.gaussian_keys(rng, Hkv * N).reshape(1, Hkv, N, 128)
         q = rng.standard_normal((1, Hkv * G, 128)).astype(np.float32)
